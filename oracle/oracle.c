@@ -1,0 +1,235 @@
+/*
+ * oracle.c -- the CPU reference for the fused row kernels.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark do.  It shares no code, header, table or helper with the HIP
+ * library.
+ *
+ * Every routine is the plain definition of what the fused kernels compute,
+ * written out in double precision with simple loops, in the order the pages
+ * state the steps.  No blocking, no fusion, no reordering of a sum beyond the
+ * natural ascending index.  Rows are independent, so an OpenMP loop over rows
+ * changes nothing in the arithmetic of any one row.
+ *
+ * Pages cited (titles abbreviated):
+ *   [P1] "CUDA算子融合优化：提升GPU推理性能的核心机制"
+ *   [P2] "4. 算子融合与Kernel合并：Element-wise算子融合、Reduce与Scan的融合策略…"
+ *   [P3] "算子融合的收益量化：显存带宽瓶颈下的 Kernel 拼接实测"
+ *   [P4] "融合计算范式对比：从分离 Kernel 到算子内融合的 GPU 应用优化实践"
+ *
+ * Inputs are the exact stored values of the device tensors (fp16 / bf16 /
+ * fp32), widened to double by the caller.  Outputs are unrounded doubles.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+/*
+ * Residual add followed by LayerNorm.
+ *
+ * [P3] §1 (物理流量量化): the fused sub-graph is A = X + R followed by a
+ * LayerNorm of A; only the normalised Y is produced.
+ * [P2] §4.2 (the fused_layernorm sketch): mean = (sum of the row) / N; var =
+ * (sum of squared deviations from that mean) / N, i.e. the population
+ * variance, taken in a second sweep over the row; std = sqrt(var + eps);
+ * out = gamma * (v - mean) / std + beta, with gamma and beta indexed by the
+ * position in the row.
+ *
+ * residual may be NULL, which gives the plain LayerNorm of x.
+ * y may not alias x or residual.
+ */
+void oracle_add_layernorm(const double *x, const double *residual,
+                          const double *gamma, const double *beta, double *y,
+                          int64_t rows, int64_t hidden, double eps)
+{
+    int64_t row;
+#pragma omp parallel for schedule(static)
+    for (row = 0; row < rows; row++) {
+        const double *xr = x + row * hidden;
+        const double *rr = residual ? residual + row * hidden : NULL;
+        double *v = y + row * hidden; /* holds x + r until overwritten */
+        double sum = 0.0, var = 0.0, mean, std;
+        int64_t i;
+
+        for (i = 0; i < hidden; i++)
+            v[i] = rr ? xr[i] + rr[i] : xr[i];
+
+        for (i = 0; i < hidden; i++)
+            sum += v[i];
+        mean = sum / (double)hidden;
+
+        for (i = 0; i < hidden; i++)
+            var += (v[i] - mean) * (v[i] - mean);
+        std = sqrt(var / (double)hidden + eps);
+
+        for (i = 0; i < hidden; i++)
+            v[i] = gamma[i] * (v[i] - mean) / std + beta[i];
+    }
+}
+
+/*
+ * Gaussian error linear unit, exact (erf) form: GELU(t) = t * Phi(t) with
+ * Phi the standard normal CDF, Phi(t) = (1 + erf(t / sqrt 2)) / 2.
+ * The pages name GELU without defining it; the erf form is the one the
+ * workload specifies.
+ */
+static double gelu_erf(double t)
+{
+    return 0.5 * t * (1.0 + erf(t / sqrt(2.0)));
+}
+
+/*
+ * BiasAdd -> GELU -> ResidualAdd, the three-kernel chain of [P3]'s traffic
+ * figure (intro diagram and §1): t = x + bias[col]; g = GELU(t); y = g + r.
+ * The bias broadcasts over rows.
+ */
+void oracle_bias_gelu_residual(const double *x, const double *bias,
+                               const double *residual, double *y,
+                               int64_t rows, int64_t hidden)
+{
+    int64_t row;
+#pragma omp parallel for schedule(static)
+    for (row = 0; row < rows; row++) {
+        int64_t i;
+        for (i = 0; i < hidden; i++) {
+            double t = x[row * hidden + i] + bias[i];
+            double g = gelu_erf(t);
+            y[row * hidden + i] = g + residual[row * hidden + i];
+        }
+    }
+}
+
+/*
+ * Row softmax of scaled scores.
+ *
+ * [P1] §二.1 lists "Softmax + Scale" as one vertical fusion: z = scale * x.
+ * [P2] §4.3 (the fused_softmax sketch): m = max over the row; each term is
+ * exp(z - m); s = their sum; out = exp(z - m) / s.
+ */
+void oracle_softmax_rows(const double *x, double *y, int64_t rows,
+                         int64_t cols, double scale)
+{
+    int64_t row;
+#pragma omp parallel for schedule(static)
+    for (row = 0; row < rows; row++) {
+        const double *xr = x + row * cols;
+        double *yr = y + row * cols;
+        double m = -INFINITY, s = 0.0;
+        int64_t j;
+
+        for (j = 0; j < cols; j++) {
+            double z = scale * xr[j];
+            if (z > m)
+                m = z;
+        }
+        for (j = 0; j < cols; j++)
+            s += exp(scale * xr[j] - m);
+        for (j = 0; j < cols; j++)
+            yr[j] = exp(scale * xr[j] - m) / s;
+    }
+}
+
+/* SiLU(c) = c * sigmoid(c) = c / (1 + e^-c). */
+static double silu(double c)
+{
+    return c / (1.0 + exp(-c));
+}
+
+/*
+ * Plain matrix product c[M,N] = a[M,K] . b[K,N], all row-major, each entry
+ * summed over k in ascending order.  The loop nest walks k outside j so that
+ * b is read along its rows; the order of the terms of every c[i][j] is
+ * unchanged by that.
+ */
+void oracle_matmul(const double *a, const double *b, double *c, int64_t M,
+                   int64_t N, int64_t K)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < M; i++) {
+        double *ci = c + i * N;
+        int64_t j, k;
+        for (j = 0; j < N; j++)
+            ci[j] = 0.0;
+        for (k = 0; k < K; k++) {
+            double aik = a[i * K + k];
+            const double *bk = b + k * N;
+            for (j = 0; j < N; j++)
+                ci[j] += aik * bk[j];
+        }
+    }
+}
+
+/*
+ * SwiGLU of the MLP's first layer, [P4] 对比对象定义:
+ * out = SiLU(matmul(a, b1)) * matmul(a, b2), element-wise product.
+ * Computed as scheme A of the same page: both products first (c1, c2 are
+ * caller-provided M x N scratch), then the activation and the product.
+ */
+void oracle_swiglu(const double *a, const double *b1, const double *b2,
+                   double *out, double *c1, double *c2, int64_t M, int64_t N,
+                   int64_t K)
+{
+    int64_t e;
+    oracle_matmul(a, b1, c1, M, N, K);
+    oracle_matmul(a, b2, c2, M, N, K);
+    for (e = 0; e < M * N; e++)
+        out[e] = silu(c1[e]) * c2[e];
+}
+
+/*
+ * Round-to-nearest-even of a double to the binary16 / bfloat16 grid, the
+ * value returned as a double.  Used where an unfused chain stores an
+ * intermediate in the I/O type ([P3] §1 accounts each intermediate at the
+ * I/O width).  IEEE 754 binary16: 10 fraction bits, exponent range
+ * [-14, 15], subnormal quantum 2^-24.  bfloat16: 7 fraction bits, exponent
+ * range [-126, 127], subnormal quantum 2^-133.  The round is done by scaling
+ * to the quantum of the value's binade (exact for powers of two) and calling
+ * nearbyint in the default round-to-nearest-even mode.
+ */
+static double round_to_grid(double v, int frac_bits, int emin, int emax)
+{
+    double a = fabs(v), q, r, maxfin;
+    int e;
+
+    if (isnan(v) || isinf(v) || v == 0.0)
+        return v;
+    /* largest finite value: (2 - 2^-frac) * 2^emax */
+    maxfin = ldexp(2.0 - ldexp(1.0, -frac_bits), emax);
+    frexp(a, &e); /* a = f * 2^e with f in [0.5, 1) => binade exponent e-1 */
+    e -= 1;
+    if (e < emin)
+        e = emin; /* subnormal range shares the quantum of the lowest binade */
+    q = ldexp(1.0, e - frac_bits);
+    r = nearbyint(a / q) * q;
+    /* values at or beyond max + half a quantum overflow to infinity */
+    if (r > maxfin)
+        r = INFINITY;
+    return v < 0 ? -r : r;
+}
+
+/* kind 1 = binary16, kind 2 = bfloat16; any other kind copies unchanged. */
+void oracle_round(const double *in, double *out, int64_t n, int kind)
+{
+    int64_t i;
+    for (i = 0; i < n; i++) {
+        if (kind == 1)
+            out[i] = round_to_grid(in[i], 10, -14, 15);
+        else if (kind == 2)
+            out[i] = round_to_grid(in[i], 7, -126, 127);
+        else
+            out[i] = in[i];
+    }
+}
+
+/* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,103 @@
+"""Host-side logic without a GPU: seeded inputs, comparison rules, roofline arithmetic."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import read_golden
+from memory_bound_amd import roofline, synth
+from oracle import tolerance
+
+
+# ---- seeded inputs -----------------------------------------------------------------------------
+
+def test_inputs_are_deterministic_and_seed_dependent():
+    a = synth.add_layernorm_inputs(8, 96, "f16", 1003)
+    b = synth.add_layernorm_inputs(8, 96, "f16", 1003)
+    c = synth.add_layernorm_inputs(8, 96, "f16", 1004)
+    for k in ("x", "residual", "gamma", "beta"):
+        assert torch.equal(a[k], b[k])
+        assert a[k].dtype == torch.float16
+    assert not torch.equal(a["x"], c["x"])
+
+
+def test_inputs_distributions():
+    d = synth.add_layernorm_inputs(256, 4096, "f32", 1)
+    x = d["x"].double()
+    assert abs(x.mean().item()) < 0.01 and abs(x.std().item() - 1) < 0.01
+    assert d["gamma"].min() >= 0.5 and d["gamma"].max() <= 1.5
+    assert abs(d["beta"].double().std().item() - 0.1) < 0.01
+    s = synth.softmax_inputs(64, 2048, "f16", 2)
+    assert abs(s["x"].double().std().item() - math.sqrt(128)) < 0.2
+    assert s["scale"] == 1 / math.sqrt(128)
+    w = synth.swiglu_inputs(64, 512, 1536, "bf16", 3)
+    assert w["a"].dtype == torch.bfloat16 and w["b1"].shape == (1536, 512)
+    assert abs(w["b1"].double().std().item() - 1 / math.sqrt(1536)) < 1e-3
+    g = synth.bias_gelu_residual_inputs(64, 4096, "f16", 4)
+    assert abs(g["bias"].double().std().item() - 0.02) < 0.003
+
+
+def test_workload_table():
+    w = synth.WORKLOADS
+    assert w["addln_f16_2048x4096"].shape == (2048, 4096)
+    assert w["addln_f16_16384x4096"].shape == (8 * 2048, 4096)
+    assert w["softmax_f16_65536x2048"].shape == (32 * 2048, 2048)
+    assert w["swiglu_bf16_2048x8960x1536"].shape == (2048, 8960, 1536)
+    assert len({x.seed for x in w.values()}) == len(w)
+
+
+# ---- comparison rules --------------------------------------------------------------------------
+
+def test_ulp16():
+    v = np.array([1.0, 1.5, 8.0, 9.0, 2.0 ** -14, 2.0 ** -20, 0.0, -4.0])
+    np.testing.assert_array_equal(tolerance.ulp16(v), [2.0 ** -10, 2.0 ** -10, 2.0 ** -7, 2.0 ** -7,
+                                                       2.0 ** -24, 2.0 ** -24, 2.0 ** -24, 2.0 ** -8])
+
+
+def test_compare_rules():
+    ref = np.array([0.5, 10.0, -3.0])
+    assert tolerance.compare(ref + [1.9e-3, 7e-3, -1.9e-3], ref, "f16")["ok"]
+    assert not tolerance.compare(ref + [2.1e-3, 0, 0], ref, "f16")["ok"]
+    assert not tolerance.compare(ref + [0, 8e-3, 0], ref, "f16")["ok"]
+    # bf16: relative with a 1e-2 floor
+    assert tolerance.compare([1.009, 0.0, 5e-3 + 9e-5], [1.0, 0.0, 5e-3], "bf16")["ok"]
+    assert not tolerance.compare([1.011], [1.0], "bf16")["ok"]
+    assert not tolerance.compare([2e-4], [0.0], "bf16")["ok"]
+    assert tolerance.compare([1.0 + 9e-6], [1.0], "f32")["ok"]
+    assert not tolerance.compare([1.0 + 2e-5], [1.0], "f32")["ok"]
+    # NaN must match NaN
+    assert not tolerance.compare([np.nan], [1.0], "f32")["ok"]
+    assert not tolerance.compare([1.0], [np.nan], "f32")["ok"]
+    assert tolerance.compare([np.nan], [np.nan], "f32")["ok"]
+
+
+def test_perfect_fp16_rounding_meets_the_rule():
+    rng = np.random.default_rng(0)
+    ref = rng.standard_normal(100000) * 4
+    y = ref.astype(np.float16).astype(np.float64)
+    assert tolerance.compare(y, ref, "f16")["ok"]
+
+
+# ---- roofline arithmetic against the page's own traffic figures ----------------------------------
+
+def test_traffic_matches_page_three_section_one():
+    mib = {k: int(v) for k, v in read_golden("traffic_page3.txt")}
+    rows, hidden = 1 * 2048, 4096
+    tensor = rows * hidden * 2
+    assert tensor == mib["tensor_mib"] << 20
+    fused = roofline.add_layernorm_bytes(rows, hidden, "f16", fused=True)
+    unfused = roofline.add_layernorm_bytes(rows, hidden, "f16", fused=False)
+    assert fused["tensor_bytes"] == mib["fused_total_mib"] << 20
+    assert unfused["tensor_bytes"] == mib["unfused_total_mib"] << 20
+    assert (mib["unfused_add_mib"] + mib["unfused_layernorm_mib"]) == mib["unfused_total_mib"]
+    # with gamma and beta: 3 * 16 MiB + 2 * 8 KiB
+    assert fused["bytes"] == 50_348_032
+
+
+def test_other_algorithmic_work():
+    assert roofline.bias_gelu_residual_bytes(2048, 4096, "f16")["bytes"] == 50_339_840
+    assert roofline.softmax_rows_bytes(65536, 2048, "f16")["bytes"] == 536_870_912
+    assert roofline.swiglu_flops(2048, 8960, 1536) == 112_742_891_520
+    assert roofline.add_layernorm_bytes(64, 768, "f32")["bytes"] == 595_968
+    assert roofline.add_layernorm_bytes(16384, 4096, "f16")["bytes"] == 402_669_568
