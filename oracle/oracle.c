@@ -73,10 +73,15 @@ void oracle_add_layernorm(const double *x, const double *residual,
  * Phi the standard normal CDF, Phi(t) = (1 + erf(t / sqrt 2)) / 2.
  * The pages name GELU without defining it; the erf form is the one the
  * workload specifies.
+ *
+ * Phi is evaluated as erfc(-t / sqrt 2) / 2, the same function: written as
+ * 1 + erf(.) it cancels to exactly zero in double precision for t below
+ * about -8.3, where Phi(t) is still ~1e-16, while C's erfc keeps full
+ * relative accuracy in that tail.
  */
 static double gelu_erf(double t)
 {
-    return 0.5 * t * (1.0 + erf(t / sqrt(2.0)));
+    return t * (0.5 * erfc(-t / sqrt(2.0)));
 }
 
 /*

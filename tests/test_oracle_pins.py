@@ -140,6 +140,18 @@ def test_gelu_odd_part_identity_and_tails():
     assert big[0] == 12.0 and abs(big[1]) < 1e-30
 
 
+@pytest.mark.parametrize("t", [-5.0, -8.0, -8.5, -10.0, -12.0, -20.0, -30.0])
+def test_gelu_negative_tail_within_mills_bounds(t):
+    # For u > 0 the normal tail Q(u) = Phi(-u) satisfies the textbook Mills-ratio bounds
+    # phi(u)/u * (1 - 1/u^2) < Q(u) < phi(u)/u, phi(u) = exp(-u^2/2)/sqrt(2 pi).  GELU(t)/t = Phi(t)
+    # must stay inside them: an evaluation through 1 + erf(t/sqrt 2) collapses to 0 here.
+    u = -t
+    phi = math.exp(-u * u / 2) / math.sqrt(2 * math.pi)
+    lo, hi = phi / u * (1 - 1 / (u * u)), phi / u
+    q = _gelu_only([t])[0, 0] / t
+    assert lo < q < hi, (t, q, lo, hi)
+
+
 def test_gelu_bias_by_column_and_residual_after():
     rng = np.random.default_rng(5)
     rows, n = 3, 40
