@@ -1,0 +1,369 @@
+"""Benchmark of the fused row kernels on one MI355X.
+
+Headline: fused ResidualAdd+LayerNorm, [B,S,H] = [1,2048,4096] fp16 (2048 rows x 4096), achieved
+HBM GB/s.  One step = one launch over one [2048,4096] batch.  The K timed steps (and the W warmup
+steps) are captured into one HIP graph each and replayed, so the host's per-call cost does not
+leave the GPU idle between 7-microsecond kernels.  Every step uses a different buffer set; the
+sets span more than 1 GiB so that no step finds its inputs in the 256 MB Infinity Cache left
+there by an earlier step: the bytes come from HBM.
+
+value = algorithmic bytes of K steps / wall time of the timed region (host clock, synchronized
+on both sides).  roofline.achieved = algorithmic bytes of one launch / average launch duration,
+from HIP events recorded on the launch stream around the timed replay.  The other rows of the
+hot path (BiasAdd+GELU+Residual, row softmax, SwiGLU), their unfused baselines and a plain copy
+are timed the same way and reported under "rows".  cpu_baseline times the CPU oracle on the
+same workload.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-rows] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HEADLINE = "addln_f16_2048x4096"
+ROTATE_BYTES = 1 << 30
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "add_layernorm_f16_2048x4096_counters.txt")
+HEADLINE_SOURCES = ["fuse_common.hpp", "row_kernels.hpp", "row_launch.hpp"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "memory_bound_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_counters():
+    """HBM bytes per dispatch from the committed counter summary, or None when the kernel
+    source changed since the counters were taken."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    kv = {}
+    for line in open(PROFILE_COUNTERS):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != source_hash(HEADLINE_SOURCES):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timed:
+    """Captures `count` calls of launch(i) into a HIP graph on a private stream."""
+
+    def __init__(self, torch, stream, launch, count):
+        self.torch = torch
+        self.stream = stream
+        self.count = count
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph, stream=stream):
+            for i in range(count):
+                launch(i)
+
+    def run(self):
+        """Replay once; returns (host seconds, event milliseconds)."""
+        torch = self.torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(self.stream)
+        self.graph.replay()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return t1 - t0, e0.elapsed_time(e1)
+
+
+def rotation_sets(torch, tensors: dict, outputs: dict, min_bytes: int):
+    """Copies of the input tensors (and fresh outputs) until the sets together span min_bytes."""
+    per = sum(t.numel() * t.element_size() for t in tensors.values())
+    per += sum(t.numel() * t.element_size() for t in outputs.values())
+    n = max(2, math.ceil(min_bytes / per))
+    sets = []
+    for _ in range(n):
+        s = {k: v.to("cuda").clone() for k, v in tensors.items()}
+        s.update({k: torch.empty_like(v, device="cuda") for k, v in outputs.items()})
+        sets.append(s)
+    return sets
+
+
+def time_launches(torch, stream, launch, n, warm=3):
+    for i in range(warm):
+        launch(i)
+    torch.cuda.synchronize()
+    t = Timed(torch, stream, launch, n)
+    t.run()  # first replay warms the graph
+    host_s, ev_ms = t.run()
+    return host_s, ev_ms
+
+
+def headline(torch, api, synth, roofline, steps, warmup):
+    w = synth.WORKLOADS[HEADLINE]
+    rows, hidden = w.shape
+    d = w.inputs()
+    gamma, beta = d["gamma"].cuda(), d["beta"].cuda()
+    sets = rotation_sets(torch, {"x": d["x"], "r": d["residual"]}, {"y": d["x"]}, ROTATE_BYTES)
+    log(f"headline {HEADLINE}: {len(sets)} buffer sets")
+    stream = torch.cuda.Stream()
+    work = roofline.workload_work(w.op, w.shape, w.dtype)
+
+    def launch(i):
+        s = sets[i % len(sets)]
+        api.fuse_add_layernorm(s["x"], s["r"], gamma, beta, d["eps"], y=s["y"])
+
+    with torch.cuda.stream(stream):
+        for i in range(3):
+            launch(i)
+        torch.cuda.synchronize()
+        warm_graph = Timed(torch, stream, launch, max(1, warmup))
+        timed_graph = Timed(torch, stream, lambda i: launch(i + warmup), steps)
+        warm_graph.run()
+        host_s, ev_ms = timed_graph.run()
+    avg_us = ev_ms * 1e3 / steps
+    return {
+        "workload": w,
+        "bytes": work["bytes"],
+        "host_s": host_s,
+        "avg_launch_us": avg_us,
+        "value_gbps": work["bytes"] * steps / host_s / 1e9,
+        "achieved_gbps": work["bytes"] / (avg_us * 1e-6) / 1e9,
+        "sets": len(sets),
+    }
+
+
+def other_rows(torch, api, synth, roofline, n_launch=40):
+    """Each remaining row of the hot path, its unfused baseline, and the copy ceiling."""
+    out = {}
+    stream = torch.cuda.Stream()
+    peak_bw = roofline.HBM_PEAK_GBPS
+
+    def record(name, op, shape, dtype, fused, ev_ms, n, extra=None):
+        work = roofline.workload_work(op, shape, dtype, fused)
+        us = ev_ms * 1e3 / n
+        r = {"avg_launch_us": round(us, 3), "algorithmic_bytes": work["bytes"]}
+        if op == "swiglu":
+            tf = work["flops"] / (us * 1e-6) / 1e12
+            r.update({"achieved_tflops": round(tf, 1), "peak_tflops": roofline.MFMA_PEAK_TFLOPS["bf16"],
+                      "frac": round(tf / roofline.MFMA_PEAK_TFLOPS["bf16"], 4), "bound": "mfma"})
+        else:
+            gb = work["bytes"] / (us * 1e-6) / 1e9
+            r.update({"achieved_gbps": round(gb, 1), "frac": round(gb / peak_bw, 4), "bound": "hbm"})
+        if extra:
+            r.update(extra)
+        out[name] = r
+        log(f"{name}: {us:.2f} us")
+
+    with torch.cuda.stream(stream):
+        # headline shape, unfused
+        w = synth.WORKLOADS[HEADLINE]
+        d = w.inputs()
+        gamma, beta = d["gamma"].cuda(), d["beta"].cuda()
+        sets = rotation_sets(torch, {"x": d["x"], "r": d["residual"]}, {"y": d["x"]}, ROTATE_BYTES)
+        ws = api._workspace(api.FUSE_OP_ADD_LAYERNORM, *w.shape, 0, api.FUSE_F16, "cuda")
+
+        def unf(i):
+            s = sets[i % len(sets)]
+            api.fuse_unfused_add_layernorm(s["x"], s["r"], gamma, beta, d["eps"], y=s["y"], workspace=ws)
+        _, ev = time_launches(torch, stream, unf, n_launch)
+        record("add_layernorm_unfused_f16_2048x4096", w.op, w.shape, w.dtype, False, ev, n_launch,
+               {"note": "add kernel + LayerNorm kernel; bytes = the unfused chain's 5 tensor passes"})
+
+        w = synth.WORKLOADS["addln_f16_16384x4096"]
+        d = w.inputs()
+        gamma, beta = d["gamma"].cuda(), d["beta"].cuda()
+        sets = rotation_sets(torch, {"x": d["x"], "r": d["residual"]}, {"y": d["x"]}, ROTATE_BYTES)
+        del d
+
+        def ln8(i):
+            s = sets[i % len(sets)]
+            api.fuse_add_layernorm(s["x"], s["r"], gamma, beta, 1e-5, y=s["y"])
+        _, ev = time_launches(torch, stream, ln8, n_launch)
+        record("add_layernorm_f16_16384x4096", w.op, w.shape, w.dtype, True, ev, n_launch)
+        del sets
+
+        w = synth.WORKLOADS["addln_f32_64x768"]
+        d = w.inputs()
+        g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in d.items()}
+        y = torch.empty_like(g["x"])
+
+        def ln_small(i):
+            api.fuse_add_layernorm(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"], y=y)
+        _, ev = time_launches(torch, stream, ln_small, n_launch)
+        record("add_layernorm_f32_64x768", w.op, w.shape, w.dtype, True, ev, n_launch,
+               {"note": "596 KB, cache resident and launch-latency bound; GB/s not an HBM figure"})
+
+        w = synth.WORKLOADS["gelu_f16_2048x4096"]
+        d = w.inputs()
+        bias = d["bias"].cuda()
+        sets = rotation_sets(torch, {"x": d["x"], "r": d["residual"]}, {"y": d["x"]}, ROTATE_BYTES)
+        ws = api._workspace(api.FUSE_OP_BIAS_GELU_RESIDUAL, *w.shape, 0, api.FUSE_F16, "cuda")
+
+        def gelu(i):
+            s = sets[i % len(sets)]
+            api.fuse_bias_gelu_residual(s["x"], bias, s["r"], y=s["y"])
+
+        def gelu_unf(i):
+            s = sets[i % len(sets)]
+            api.fuse_unfused_bias_gelu_residual(s["x"], bias, s["r"], y=s["y"], workspace=ws)
+        _, ev = time_launches(torch, stream, gelu, n_launch)
+        record("bias_gelu_residual_f16_2048x4096", w.op, w.shape, w.dtype, True, ev, n_launch)
+        _, ev = time_launches(torch, stream, gelu_unf, n_launch)
+        record("bias_gelu_residual_unfused_f16_2048x4096", w.op, w.shape, w.dtype, False, ev, n_launch)
+        del sets, ws
+
+        w = synth.WORKLOADS["softmax_f16_65536x2048"]
+        d = w.inputs()
+        sets = rotation_sets(torch, {"x": d["x"]}, {"y": d["x"]}, ROTATE_BYTES)
+        ws = api._workspace(api.FUSE_OP_SOFTMAX_ROWS, *w.shape, 0, api.FUSE_F16, "cuda")
+        del d
+
+        def sm(i):
+            s = sets[i % len(sets)]
+            api.fuse_softmax_rows(s["x"], 1 / math.sqrt(128), y=s["y"])
+
+        def sm_unf(i):
+            s = sets[i % len(sets)]
+            api.fuse_unfused_softmax_rows(s["x"], 1 / math.sqrt(128), y=s["y"], workspace=ws)
+        _, ev = time_launches(torch, stream, sm, n_launch // 2)
+        record("softmax_f16_65536x2048", w.op, w.shape, w.dtype, True, ev, n_launch // 2)
+        _, ev = time_launches(torch, stream, sm_unf, n_launch // 2)
+        record("softmax_unfused_f16_65536x2048", w.op, w.shape, w.dtype, False, ev, n_launch // 2)
+        del sets, ws
+
+        w = synth.WORKLOADS["swiglu_bf16_2048x8960x1536"]
+        d = w.inputs()
+        a, b1, b2 = d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda()
+        o = torch.empty(w.shape[0], w.shape[1], dtype=torch.bfloat16, device="cuda")
+        ws = api._workspace(api.FUSE_OP_SWIGLU, *w.shape, api.FUSE_BF16, "cuda")
+
+        def sw(i):
+            api.fuse_swiglu_dualgemm(a, b1, b2, out=o)
+
+        def sw_unf(i):
+            api.fuse_unfused_swiglu(a, b1, b2, out=o, workspace=ws)
+        _, ev = time_launches(torch, stream, sw, n_launch // 2)
+        record("swiglu_bf16_2048x8960x1536", w.op, w.shape, w.dtype, True, ev, n_launch // 2)
+        _, ev = time_launches(torch, stream, sw_unf, n_launch // 2)
+        record("swiglu_unfused_bf16_2048x8960x1536", w.op, w.shape, w.dtype, False, ev, n_launch // 2)
+        del ws
+
+        # copy of the headline's byte count (read 32 MiB + write 16 MiB would not be a copy;
+        # copy 24 MiB -> 24 MiB moves the same 48 MiB)
+        nbytes = 24 << 20
+        n = max(2, math.ceil(ROTATE_BYTES / (2 * nbytes)))
+        bufs = [(torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1),
+                 torch.empty(nbytes, dtype=torch.uint8, device="cuda")) for _ in range(n)]
+
+        def cp(i):
+            s, t = bufs[i % len(bufs)]
+            api.fuse_copy(s, t)
+        _, ev = time_launches(torch, stream, cp, n_launch)
+        us = ev * 1e3 / n_launch
+        gb = 2 * nbytes / (us * 1e-6) / 1e9
+        out["copy_48MiB"] = {"avg_launch_us": round(us, 3), "achieved_gbps": round(gb, 1),
+                             "frac": round(gb / peak_bw, 4), "bound": "hbm",
+                             "note": "plain copy of 24 MiB (48 MiB moved): the achievable streaming ceiling"}
+        log(f"copy: {us:.2f} us {gb:.0f} GB/s")
+    return out
+
+
+def cpu_baseline(synth, roofline, budget_s=10.0):
+    import numpy as np
+
+    import oracle
+
+    w = synth.WORKLOADS[HEADLINE]
+    d = w.inputs()
+    x, r, g, b = (oracle.f64(d[k]) for k in ("x", "residual", "gamma", "beta"))
+    eps = float(np.float32(d["eps"]))
+    oracle.add_layernorm(x, r, g, b, eps)  # warm (page faults, library load)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.add_layernorm(x, r, g, b, eps)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 2000:
+            break
+    per = el / reps
+    work = roofline.workload_work(w.op, w.shape, w.dtype)
+    return {"value": round(work["bytes"] / per / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"full {w.shape[0]}x{w.shape[1]} workload, {reps} oracle calls in {el:.1f} s "
+                      f"({per * 1e3:.2f} ms per call, fp64, inputs pre-widened)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-rows", action="store_true", help="skip the other rows of the hot path")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): the fused row kernels are "
+              "single-GPU; rows shard across GPUs with no exchange, so N GPUs would run the same "
+              "kernel on rows/N each.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from memory_bound_amd import api, roofline, synth
+
+    api.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    h = headline(torch, api, synth, roofline, a.steps, a.warmup)
+    log(f"headline: {h['avg_launch_us']:.2f} us/launch, value {h['value_gbps']:.0f} GB/s")
+    rows = {} if a.no_rows else other_rows(torch, api, synth, roofline)
+    cpu = None if a.no_cpu else cpu_baseline(synth, roofline)
+
+    traffic = read_counters()
+    w = h["workload"]
+    line = {
+        "metric": "achieved HBM GB/s (% of peak) fused Add+LayerNorm [2048,4096] fp16",
+        "value": round(h["value_gbps"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(h["host_s"] * 1e3 / a.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "fused ResidualAdd+LayerNorm, [B,S,H]=[1,2048,4096] fp16, eps=1e-5",
+                   "rows": w.shape[0], "hidden": w.shape[1], "seed": w.seed,
+                   "buffer_sets": h["sets"], "launch": "HIP graph of the timed steps"},
+        "pct_of_peak": round(100 * h["value_gbps"] / roofline.HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(h["achieved_gbps"], 1),
+                     "peak": roofline.HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(h["achieved_gbps"] / roofline.HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": h["bytes"],
+                     "avg_launch_us": round(h["avg_launch_us"], 3)},
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+/*
+ * libfuse.h -- C ABI of libfuse: single-pass fused row kernels for AMD MI355X (gfx950).
+ *
+ * Pages cited (titles abbreviated):
+ *   [P1] "CUDA算子融合优化：提升GPU推理性能的核心机制"
+ *   [P2] "4. 算子融合与Kernel合并：Element-wise算子融合、Reduce与Scan的融合策略…"
+ *   [P3] "算子融合的收益量化：显存带宽瓶颈下的 Kernel 拼接实测"
+ *   [P4] "融合计算范式对比：从分离 Kernel 到算子内融合的 GPU 应用优化实践"
+ *
+ * Conventions shared by every entry point:
+ *
+ *  - Memory.  Every tensor pointer is a device pointer (memory of the device that is current
+ *    on the calling thread).  The caller owns all buffers; the library never allocates or
+ *    frees device memory.  Fused operations need no workspace.
+ *  - Layout.  Dense, row-major, no padding: an activation [B, S, H] is passed as rows = B*S
+ *    rows of `hidden` elements; per-column parameters (gamma, beta, bias) are [hidden] vectors
+ *    in the activation type.  SwiGLU takes a [M,K], b1 and b2 [K,N], out [M,N].
+ *  - Types.  FUSE_F32, FUSE_F16 (IEEE binary16) or FUSE_BF16 storage; arithmetic is fp32 in
+ *    every kernel; every fp32 -> fp16/bf16 conversion rounds to nearest even.
+ *  - Streams.  `stream` is a hipStream_t (NULL = the null stream).  Every call only enqueues
+ *    work on it and returns without synchronising ([P1] §三.3 asynchronous execution).
+ *  - Errors.  Every argument is checked before anything is launched; on an error nothing is
+ *    enqueued and the outputs are untouched ([P1] §三.3 atomic execution of a fused kernel).
+ *    A failed launch returns FUSE_ERR_HIP; fuse_last_hip_error() then gives the hipError_t.
+ *    No entry point aborts or throws.
+ *  - Alignment.  Any element-aligned pointer is accepted.  When every pointer is 16-byte
+ *    aligned and a row is a whole number of 16-byte words the kernels use 128-bit accesses,
+ *    otherwise a per-element path with the same results.
+ *  - Aliasing.  An output may be exactly the same buffer as a same-shaped input (in-place use:
+ *    each element is read before it is written by the same lane).  Any other overlap between
+ *    an output and an input returns FUSE_ERR_ALIAS.
+ *  - Sizes.  rows == 0 (or M == 0) is a valid no-op.  Negative sizes are FUSE_ERR_BAD_SHAPE.
+ *  - Thread safety.  The library keeps no state besides a per-thread last-error code.
+ */
+#ifndef LIBFUSE_H
+#define LIBFUSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FUSE_OK = 0,
+    FUSE_ERR_NULL_PTR = 1,    /* a required pointer is NULL */
+    FUSE_ERR_BAD_SHAPE = 2,   /* a size is negative, zero where it must be positive, or too big */
+    FUSE_ERR_BAD_DTYPE = 3,   /* the storage type is not one this operation supports */
+    FUSE_ERR_BAD_VALUE = 4,   /* eps or scale is not finite, or eps is negative */
+    FUSE_ERR_ALIAS = 5,       /* an output overlaps an input other than by exact in-place use */
+    FUSE_ERR_UNSUPPORTED = 6, /* a row is longer than the in-register maximum */
+    FUSE_ERR_WORKSPACE = 7,   /* an unfused baseline was given too small a workspace */
+    FUSE_ERR_MISALIGNED = 8,  /* a pointer is not aligned to its element size */
+    FUSE_ERR_HIP = 9          /* the HIP runtime reported an error at launch */
+} fuse_status_t;
+
+typedef enum { FUSE_F32 = 0, FUSE_F16 = 1, FUSE_BF16 = 2 } fuse_dtype_t;
+
+/* Longest row the register-resident row kernels accept (elements). */
+#define FUSE_MAX_HIDDEN 16384
+#define FUSE_MAX_SOFTMAX_COLS 16384
+
+/*
+ * Fused ResidualAdd + LayerNorm, one pass over HBM.
+ *   v = x + residual;  mean = sum(v)/H;  var = sum((v - mean)^2)/H;
+ *   y = gamma * (v - mean) / sqrt(var + eps) + beta.
+ * [P3] §1 (物理流量量化): X and R are read once into registers, the sum and the LayerNorm
+ * reduction happen in place, and only Y is written (48 MB instead of 80 MB at
+ * [1,2048,4096] fp16).  [P2] §4.2 fixes the statistics: population variance (divide by H)
+ * and eps added to the variance inside the square root.
+ *
+ *   x, residual : [rows, hidden] inputs.  residual may be NULL (plain LayerNorm of x).
+ *   gamma, beta : [hidden] scale and shift.
+ *   y           : [rows, hidden] output; may equal x or residual.
+ *   eps         : finite, >= 0.
+ *   dtype       : FUSE_F32, FUSE_F16 or FUSE_BF16 (all tensors share it).
+ * hidden must be in [1, FUSE_MAX_HIDDEN].
+ */
+fuse_status_t fuse_add_layernorm(const void *x, const void *residual, const void *gamma,
+                                 const void *beta, void *y, int64_t rows, int64_t hidden,
+                                 float eps, fuse_dtype_t dtype, void *stream);
+
+/*
+ * Fused BiasAdd + GELU + ResidualAdd, one pass over HBM.
+ *   t = x + bias[col];  g = t * Phi(t) = t/2 * (1 + erf(t / sqrt 2));  y = g + residual.
+ * [P3] intro diagram and §1: the three kernels BiasAdd, GELU and Residual become one kernel
+ * that reads its inputs once and writes its output once.  The GELU is the exact (erf) form.
+ *
+ *   x, residual : [rows, hidden];  bias : [hidden];  y : [rows, hidden], may equal x or residual.
+ *   dtype       : FUSE_F32, FUSE_F16 or FUSE_BF16.
+ * hidden >= 1; rows*hidden must be below 2^34 elements.
+ */
+fuse_status_t fuse_bias_gelu_residual(const void *x, const void *bias, const void *residual,
+                                      void *y, int64_t rows, int64_t hidden,
+                                      fuse_dtype_t dtype, void *stream);
+
+/*
+ * Fused row softmax of scaled scores, one pass over HBM.
+ *   z = scale * x;  m = max_j z_j;  y_j = exp(z_j - m) / sum_k exp(z_k - m).
+ * [P2] §4.3: max-reduce, exp-and-sum reduce, and the element-wise divide fused into one
+ * kernel.  [P1] §二.1 lists "Softmax + Scale" as one vertical fusion: the scale is applied
+ * inside the same kernel.
+ *
+ *   x : [rows, cols];  y : [rows, cols], may equal x.
+ *   scale : finite, any sign.
+ *   dtype : FUSE_F32, FUSE_F16 or FUSE_BF16.
+ * cols must be in [1, FUSE_MAX_SOFTMAX_COLS].
+ */
+fuse_status_t fuse_softmax_rows(const void *x, void *y, int64_t rows, int64_t cols, float scale,
+                                fuse_dtype_t dtype, void *stream);
+
+/*
+ * Fused SwiGLU dual GEMM (scheme B of [P4] 对比对象定义):
+ *   out = SiLU(a . b1) * (a . b2),  SiLU(c) = c / (1 + e^-c).
+ * Each workgroup loads its tile of a once and multiplies it with the matching tiles of b1 and
+ * b2 ([P4] 核心差异分析 §1); both fp32 accumulators stay in registers and the activation and
+ * product are applied before the single store of out.
+ *
+ *   a : [M, K];  b1, b2 : [K, N];  out : [M, N], must not overlap a, b1 or b2.
+ *   dtype : FUSE_BF16 (bf16 inputs and output, fp32 accumulation).
+ * M >= 0, N >= 1, K >= 1, each below 2^31.
+ */
+fuse_status_t fuse_swiglu_dualgemm(const void *a, const void *b1, const void *b2, void *out,
+                                   int64_t M, int64_t N, int64_t K, fuse_dtype_t dtype,
+                                   void *stream);
+
+/*
+ * Unfused baselines (measurement companions).  Each runs the same computation as separate
+ * kernels that store every intermediate in HBM in the I/O type, as the pages' "before
+ * fusion" pictures do ([P3] §1: Add kernel writes A, LayerNorm kernel reads it; [P3] intro
+ * diagram: BiasAdd, GELU, Residual; [P2] §4.3: row max, exp and sum, divide; [P4] scheme A:
+ * one kernel for both products, one for SiLU and the product).  They exist so that the
+ * traffic and time fusion saves can be measured, and they are the semantic reference the
+ * pages recommend keeping ([P4] 迁移与使用注意事项 §3).
+ *
+ * The workspace is caller-owned device memory of at least fuse_unfused_workspace_bytes()
+ * bytes (256-byte aligned), not overlapping any argument.  `op` selects the operation:
+ */
+typedef enum {
+    FUSE_OP_ADD_LAYERNORM = 0,
+    FUSE_OP_BIAS_GELU_RESIDUAL = 1,
+    FUSE_OP_SOFTMAX_ROWS = 2,
+    FUSE_OP_SWIGLU = 3
+} fuse_op_t;
+
+/* Workspace bytes for an unfused baseline: (rows, hidden, -) for the row operations,
+ * (M, N, K) for SwiGLU.  Returns 0 for invalid arguments. */
+size_t fuse_unfused_workspace_bytes(fuse_op_t op, int64_t d0, int64_t d1, int64_t d2,
+                                    fuse_dtype_t dtype);
+
+fuse_status_t fuse_unfused_add_layernorm(const void *x, const void *residual, const void *gamma,
+                                         const void *beta, void *y, int64_t rows,
+                                         int64_t hidden, float eps, fuse_dtype_t dtype,
+                                         void *workspace, size_t workspace_bytes, void *stream);
+
+fuse_status_t fuse_unfused_bias_gelu_residual(const void *x, const void *bias,
+                                              const void *residual, void *y, int64_t rows,
+                                              int64_t hidden, fuse_dtype_t dtype,
+                                              void *workspace, size_t workspace_bytes,
+                                              void *stream);
+
+fuse_status_t fuse_unfused_softmax_rows(const void *x, void *y, int64_t rows, int64_t cols,
+                                        float scale, fuse_dtype_t dtype, void *workspace,
+                                        size_t workspace_bytes, void *stream);
+
+fuse_status_t fuse_unfused_swiglu(const void *a, const void *b1, const void *b2, void *out,
+                                  int64_t M, int64_t N, int64_t K, fuse_dtype_t dtype,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Plain device-to-device copy of `bytes` bytes, the calibration kernel of the roofline: its
+ * achieved bandwidth is the practical ceiling a streaming kernel can reach, and its hardware
+ * byte counters give the scale between counter readings and bytes moved.  src and dst must
+ * not overlap; bytes at most 2^40.
+ */
+fuse_status_t fuse_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *fuse_status_string(fuse_status_t status);
+
+/* hipError_t of the last FUSE_ERR_HIP returned on this thread (0 if none). */
+int fuse_last_hip_error(void);
+
+/* Library version string (static storage). */
+const char *fuse_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFUSE_H */

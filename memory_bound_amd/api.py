@@ -1,0 +1,267 @@
+"""Python binding of the libfuse C ABI (include/libfuse.h): argument marshalling only.
+
+Every function has the name of the C entry point it calls and takes torch tensors that already
+live on the GPU; it passes their data pointers, sizes and the current torch stream, and raises
+``FuseError`` on a non-OK status.  All computation happens in the HIP kernels of libfuse.so; if
+the library is not built this module raises instead of computing anything another way.
+
+torch is imported before libfuse.so is loaded so that both share torch's HIP runtime.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfuse.so")
+
+FUSE_F32, FUSE_F16, FUSE_BF16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: FUSE_F32, torch.float16: FUSE_F16, torch.bfloat16: FUSE_BF16}
+
+FUSE_OP_ADD_LAYERNORM, FUSE_OP_BIAS_GELU_RESIDUAL, FUSE_OP_SOFTMAX_ROWS, FUSE_OP_SWIGLU = 0, 1, 2, 3
+
+STATUS = {0: "FUSE_OK", 1: "FUSE_ERR_NULL_PTR", 2: "FUSE_ERR_BAD_SHAPE", 3: "FUSE_ERR_BAD_DTYPE",
+          4: "FUSE_ERR_BAD_VALUE", 5: "FUSE_ERR_ALIAS", 6: "FUSE_ERR_UNSUPPORTED",
+          7: "FUSE_ERR_WORKSPACE", 8: "FUSE_ERR_MISALIGNED", 9: "FUSE_ERR_HIP"}
+
+# Every symbol include/libfuse.h declares.
+EXPORTS = [
+    "fuse_add_layernorm", "fuse_bias_gelu_residual", "fuse_softmax_rows", "fuse_swiglu_dualgemm",
+    "fuse_unfused_workspace_bytes", "fuse_unfused_add_layernorm", "fuse_unfused_bias_gelu_residual",
+    "fuse_unfused_softmax_rows", "fuse_unfused_swiglu", "fuse_copy", "fuse_status_string",
+    "fuse_last_hip_error", "fuse_version",
+]
+
+
+class FuseError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        lib = _lib
+        msg = lib.fuse_status_string(status).decode() if lib else STATUS.get(status, str(status))
+        if status == 9 and lib:
+            msg += f" (hipError_t {lib.fuse_last_hip_error()})"
+        super().__init__(f"{what}: {msg}")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libfuse.so (built by memory_bound_amd.build); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m memory_bound_amd.build` "
+                           "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, f32, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "fuse_add_layernorm": [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp],
+        "fuse_bias_gelu_residual": [vp, vp, vp, vp, i64, i64, i32, vp],
+        "fuse_softmax_rows": [vp, vp, i64, i64, f32, i32, vp],
+        "fuse_swiglu_dualgemm": [vp, vp, vp, vp, i64, i64, i64, i32, vp],
+        "fuse_unfused_add_layernorm": [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp, sz, vp],
+        "fuse_unfused_bias_gelu_residual": [vp, vp, vp, vp, i64, i64, i32, vp, sz, vp],
+        "fuse_unfused_softmax_rows": [vp, vp, i64, i64, f32, i32, vp, sz, vp],
+        "fuse_unfused_swiglu": [vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp],
+        "fuse_copy": [vp, vp, sz, vp],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.fuse_unfused_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
+    lib.fuse_unfused_workspace_bytes.restype = sz
+    lib.fuse_status_string.argtypes = [i32]
+    lib.fuse_status_string.restype = ctypes.c_char_p
+    lib.fuse_last_hip_error.argtypes = []
+    lib.fuse_last_hip_error.restype = ctypes.c_int
+    lib.fuse_version.argtypes = []
+    lib.fuse_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------------------------------------------
+# marshalling helpers
+# ------------------------------------------------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dt(t) -> int:
+    if t.dtype not in _DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DTYPE_CODE[t.dtype]
+
+
+def _check(t, name, dtype=None, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _rows_cols(x):
+    h = x.shape[-1] if x.dim() else 1
+    return (x.numel() // h if h else 0), h
+
+
+def _ok(status: int, what: str):
+    if status != 0:
+        raise FuseError(status, what)
+
+
+def _workspace(op, d0, d1, d2, dtype_code, device):
+    n = load().fuse_unfused_workspace_bytes(op, d0, d1, d2, dtype_code)
+    # one extra 256 bytes so that the base can be rounded up to a 256-byte boundary
+    buf = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf, ctypes.c_void_p(buf.data_ptr() + off), n
+
+
+# ------------------------------------------------------------------------------------------------
+# fused entry points
+# ------------------------------------------------------------------------------------------------
+
+def fuse_add_layernorm(x, residual, gamma, beta, eps=1e-5, y=None, stream=None):
+    """y = LayerNorm(x + residual) * gamma + beta over the last dim (residual may be None)."""
+    rows, hidden = _rows_cols(x)
+    _check(x, "x")
+    _check(residual, "residual", x.dtype, x.shape)
+    _check(gamma, "gamma", x.dtype, (hidden,))
+    _check(beta, "beta", x.dtype, (hidden,))
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", x.dtype, x.shape)
+    _ok(load().fuse_add_layernorm(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y), rows, hidden,
+                                  float(eps), _dt(x), _stream(stream)), "fuse_add_layernorm")
+    return y
+
+
+def fuse_bias_gelu_residual(x, bias, residual, y=None, stream=None):
+    """y = GELU_erf(x + bias) + residual over the last dim."""
+    rows, hidden = _rows_cols(x)
+    _check(x, "x")
+    _check(bias, "bias", x.dtype, (hidden,))
+    _check(residual, "residual", x.dtype, x.shape)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", x.dtype, x.shape)
+    _ok(load().fuse_bias_gelu_residual(_ptr(x), _ptr(bias), _ptr(residual), _ptr(y), rows, hidden, _dt(x),
+                                       _stream(stream)), "fuse_bias_gelu_residual")
+    return y
+
+
+def fuse_softmax_rows(x, scale=1.0, y=None, stream=None):
+    """y = softmax(scale * x) over the last dim."""
+    rows, cols = _rows_cols(x)
+    _check(x, "x")
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", x.dtype, x.shape)
+    _ok(load().fuse_softmax_rows(_ptr(x), _ptr(y), rows, cols, float(scale), _dt(x), _stream(stream)),
+        "fuse_softmax_rows")
+    return y
+
+
+def fuse_swiglu_dualgemm(a, b1, b2, out=None, stream=None):
+    """out = SiLU(a @ b1) * (a @ b2); a [M,K], b1 and b2 [K,N], bf16."""
+    M, K = a.shape
+    N = b1.shape[1]
+    _check(a, "a")
+    _check(b1, "b1", a.dtype, (K, N))
+    _check(b2, "b2", a.dtype, (K, N))
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    _check(out, "out", a.dtype, (M, N))
+    _ok(load().fuse_swiglu_dualgemm(_ptr(a), _ptr(b1), _ptr(b2), _ptr(out), M, N, K, _dt(a), _stream(stream)),
+        "fuse_swiglu_dualgemm")
+    return out
+
+
+# ------------------------------------------------------------------------------------------------
+# unfused baselines (the workspace is allocated here unless given as (tensor, ptr, bytes))
+# ------------------------------------------------------------------------------------------------
+
+def fuse_unfused_add_layernorm(x, residual, gamma, beta, eps=1e-5, y=None, workspace=None, stream=None):
+    rows, hidden = _rows_cols(x)
+    _check(x, "x")
+    _check(residual, "residual", x.dtype, x.shape)
+    if y is None:
+        y = torch.empty_like(x)
+    ws = workspace or _workspace(FUSE_OP_ADD_LAYERNORM, rows, hidden, 0, _dt(x), x.device)
+    _ok(load().fuse_unfused_add_layernorm(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y), rows,
+                                          hidden, float(eps), _dt(x), ws[1], ws[2], _stream(stream)),
+        "fuse_unfused_add_layernorm")
+    return y
+
+
+def fuse_unfused_bias_gelu_residual(x, bias, residual, y=None, workspace=None, stream=None):
+    rows, hidden = _rows_cols(x)
+    _check(x, "x")
+    if y is None:
+        y = torch.empty_like(x)
+    ws = workspace or _workspace(FUSE_OP_BIAS_GELU_RESIDUAL, rows, hidden, 0, _dt(x), x.device)
+    _ok(load().fuse_unfused_bias_gelu_residual(_ptr(x), _ptr(bias), _ptr(residual), _ptr(y), rows, hidden,
+                                               _dt(x), ws[1], ws[2], _stream(stream)),
+        "fuse_unfused_bias_gelu_residual")
+    return y
+
+
+def fuse_unfused_softmax_rows(x, scale=1.0, y=None, workspace=None, stream=None):
+    rows, cols = _rows_cols(x)
+    _check(x, "x")
+    if y is None:
+        y = torch.empty_like(x)
+    ws = workspace or _workspace(FUSE_OP_SOFTMAX_ROWS, rows, cols, 0, _dt(x), x.device)
+    _ok(load().fuse_unfused_softmax_rows(_ptr(x), _ptr(y), rows, cols, float(scale), _dt(x), ws[1], ws[2],
+                                         _stream(stream)), "fuse_unfused_softmax_rows")
+    return y
+
+
+def fuse_unfused_swiglu(a, b1, b2, out=None, workspace=None, stream=None):
+    M, K = a.shape
+    N = b1.shape[1]
+    _check(a, "a")
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    ws = workspace or _workspace(FUSE_OP_SWIGLU, M, N, K, _dt(a), a.device)
+    _ok(load().fuse_unfused_swiglu(_ptr(a), _ptr(b1), _ptr(b2), _ptr(out), M, N, K, _dt(a), ws[1], ws[2],
+                                   _stream(stream)), "fuse_unfused_swiglu")
+    return out
+
+
+def fuse_unfused_workspace_bytes(op: int, d0: int, d1: int, d2: int, dtype) -> int:
+    code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(load().fuse_unfused_workspace_bytes(op, d0, d1, d2, code))
+
+
+def fuse_copy(src, dst, stream=None):
+    """Byte copy of src into dst (same byte size); roofline calibration kernel."""
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("src and dst differ in size")
+    _check(src, "src")
+    _check(dst, "dst")
+    _ok(load().fuse_copy(_ptr(src), _ptr(dst), nb, _stream(stream)), "fuse_copy")
+    return dst
+
+
+def fuse_version() -> str:
+    return load().fuse_version().decode()

@@ -1,0 +1,408 @@
+// abi.hip -- the C ABI of libfuse: argument validation, path selection and dispatch.
+//
+// Every entry point checks all of its arguments before it enqueues anything, so an error leaves
+// the outputs untouched and the stream unchanged; launch failures are reported as FUSE_ERR_HIP
+// with the hipError_t kept per thread.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/libfuse.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+fuse_status_t hip_status(hipError_t e) {
+    if (e == hipSuccess) return FUSE_OK;
+    g_last_hip_error = (int)e;
+    return FUSE_ERR_HIP;
+}
+
+int elem_bytes(fuse_dtype_t d) {
+    switch (d) {
+        case FUSE_F32: return 4;
+        case FUSE_F16: return 2;
+        case FUSE_BF16: return 2;
+    }
+    return 0;
+}
+
+bool valid_dtype(fuse_dtype_t d) { return d == FUSE_F32 || d == FUSE_F16 || d == FUSE_BF16; }
+
+bool elem_aligned(const void* p, int e) { return ((uintptr_t)p % (uintptr_t)e) == 0; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// [a, a+na) and [b, b+nb) share at least one byte.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na && nb && x < y + nb && y < x + na;
+}
+// An output may be exactly an input of the same size, or disjoint from it.
+bool bad_alias(const void* out, size_t nout, const void* in, size_t nin) {
+    if (!in) return false;
+    if (out == in && nout == nin) return false;
+    return overlaps(out, nout, in, nin);
+}
+
+// rows * cols * e without overflow, capped well inside int64.
+bool tensor_bytes(int64_t rows, int64_t cols, int e, size_t* out) {
+    if (rows < 0 || cols < 0) return false;
+    if (cols && rows > (INT64_C(1) << 46) / cols) return false;
+    *out = (size_t)rows * (size_t)cols * (size_t)e;
+    return true;
+}
+
+int env_int(const char* name) {
+    const char* v = getenv(name);
+    return v ? atoi(v) : 0;
+}
+
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+template <class F> hipError_t by_dtype(fuse_dtype_t d, F&& f) {
+    switch (d) {
+        case FUSE_F32: return f.template operator()<fuse::DT::F32>();
+        case FUSE_F16: return f.template operator()<fuse::DT::F16>();
+        case FUSE_BF16: return f.template operator()<fuse::DT::BF16>();
+    }
+    return hipErrorInvalidValue;
+}
+
+// Common checks of the [rows, n] row operations.  Returns FUSE_OK and the tensor bytes.
+fuse_status_t check_rows(int64_t rows, int64_t n, int64_t nmax, fuse_dtype_t dt, size_t* bytes) {
+    if (!valid_dtype(dt)) return FUSE_ERR_BAD_DTYPE;
+    if (rows < 0 || n < 1) return FUSE_ERR_BAD_SHAPE;
+    if (nmax > 0 && n > nmax) return FUSE_ERR_UNSUPPORTED;
+    if (rows > INT64_C(0x7fffffff)) return FUSE_ERR_BAD_SHAPE;
+    if (!tensor_bytes(rows, n, elem_bytes(dt), bytes)) return FUSE_ERR_BAD_SHAPE;
+    return FUSE_OK;
+}
+
+// Elements per thread of the streaming kernels (16-byte chunks per thread); FUSE_EW_CHUNKS
+// overrides for tuning sweeps.
+int ew_chunks() {
+    const int v = env_int("FUSE_EW_CHUNKS");
+    return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 4;
+}
+
+}  // namespace
+
+namespace fuse {
+
+RowPlan plan_row(int64_t n, int eb, bool aligned, int wpr_override) {
+    const int V = 16 / eb;
+    if (aligned && (n % V) == 0) {
+        const int64_t c = n / V;
+        int wpr = 1;
+        while (c > 64 * 8 * wpr && wpr < 8) wpr *= 2;
+        if (wpr_override == 1 || wpr_override == 2 || wpr_override == 4 || wpr_override == 8) {
+            if (c <= (int64_t)64 * 16 * wpr_override) wpr = wpr_override;
+        }
+        int nv = 1;
+        while ((int64_t)nv * 64 * wpr < c) nv *= 2;
+        return {true, nv, wpr};
+    }
+    if (n <= 64) return {false, 1, 1};
+    if (n <= 256) return {false, 4, 1};
+    if (n <= 1024) return {false, 16, 1};
+    if (n <= 4096) return {false, 16, 4};
+    return {false, 32, 8};
+}
+
+}  // namespace fuse
+
+extern "C" {
+
+const char* fuse_status_string(fuse_status_t s) {
+    switch (s) {
+        case FUSE_OK: return "FUSE_OK";
+        case FUSE_ERR_NULL_PTR: return "FUSE_ERR_NULL_PTR: a required pointer is NULL";
+        case FUSE_ERR_BAD_SHAPE: return "FUSE_ERR_BAD_SHAPE: invalid or too large size";
+        case FUSE_ERR_BAD_DTYPE: return "FUSE_ERR_BAD_DTYPE: storage type not supported by this operation";
+        case FUSE_ERR_BAD_VALUE: return "FUSE_ERR_BAD_VALUE: eps or scale out of range";
+        case FUSE_ERR_ALIAS: return "FUSE_ERR_ALIAS: output partially overlaps an input";
+        case FUSE_ERR_UNSUPPORTED: return "FUSE_ERR_UNSUPPORTED: row longer than the kernel maximum";
+        case FUSE_ERR_WORKSPACE: return "FUSE_ERR_WORKSPACE: workspace missing, too small or overlapping";
+        case FUSE_ERR_MISALIGNED: return "FUSE_ERR_MISALIGNED: pointer not aligned to its element size";
+        case FUSE_ERR_HIP: return "FUSE_ERR_HIP: the HIP runtime reported an error";
+    }
+    return "unknown fuse_status_t";
+}
+
+int fuse_last_hip_error(void) { return g_last_hip_error; }
+
+const char* fuse_version(void) { return "libfuse 0.1 gfx950"; }
+
+// ------------------------------------------------------------------------------------------------
+// ResidualAdd + LayerNorm
+// ------------------------------------------------------------------------------------------------
+
+static fuse_status_t check_add_layernorm(const void* x, const void* residual, const void* gamma,
+                                         const void* beta, void* y, int64_t rows, int64_t hidden,
+                                         float eps, fuse_dtype_t dt, size_t* tb, bool* vec) {
+    fuse_status_t st = check_rows(rows, hidden, FUSE_MAX_HIDDEN, dt, tb);
+    if (st != FUSE_OK) return st;
+    if (!isfinite(eps) || eps < 0.0f) return FUSE_ERR_BAD_VALUE;
+    if (rows == 0) return FUSE_OK;
+    if (!x || !gamma || !beta || !y) return FUSE_ERR_NULL_PTR;
+    const int e = elem_bytes(dt);
+    const void* ptrs[5] = {x, residual, gamma, beta, y};
+    for (const void* p : ptrs)
+        if (p && !elem_aligned(p, e)) return FUSE_ERR_MISALIGNED;
+    const size_t pb = (size_t)hidden * e;
+    if (bad_alias(y, *tb, x, *tb) || bad_alias(y, *tb, residual, *tb) || overlaps(y, *tb, gamma, pb) ||
+        overlaps(y, *tb, beta, pb))
+        return FUSE_ERR_ALIAS;
+    bool a = (pb % 16) == 0;
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) a = false;
+    *vec = a;
+    return FUSE_OK;
+}
+
+fuse_status_t fuse_add_layernorm(const void* x, const void* residual, const void* gamma,
+                                 const void* beta, void* y, int64_t rows, int64_t hidden, float eps,
+                                 fuse_dtype_t dt, void* stream) {
+    size_t tb = 0;
+    bool vec = false;
+    fuse_status_t st = check_add_layernorm(x, residual, gamma, beta, y, rows, hidden, eps, dt, &tb, &vec);
+    if (st != FUSE_OK || rows == 0) return st;
+    const fuse::RowPlan plan = fuse::plan_row(hidden, elem_bytes(dt), vec, env_int("FUSE_ROW_WPR"));
+    return hip_status(by_dtype(dt, [&]<fuse::DT D>() {
+        return fuse::launch_add_layernorm<D>(x, residual, gamma, beta, y, rows, (int)hidden, eps, plan,
+                                             (hipStream_t)stream);
+    }));
+}
+
+// ------------------------------------------------------------------------------------------------
+// BiasAdd + GELU + Residual
+// ------------------------------------------------------------------------------------------------
+
+static fuse_status_t check_bias_gelu_residual(const void* x, const void* bias, const void* residual,
+                                              void* y, int64_t rows, int64_t hidden,
+                                              fuse_dtype_t dt, size_t* tb, bool* vec) {
+    fuse_status_t st = check_rows(rows, hidden, 0, dt, tb);
+    if (st != FUSE_OK) return st;
+    if (rows * hidden >= (INT64_C(1) << 34)) return FUSE_ERR_BAD_SHAPE;
+    if (rows == 0) return FUSE_OK;
+    if (!x || !bias || !residual || !y) return FUSE_ERR_NULL_PTR;
+    const int e = elem_bytes(dt);
+    const void* ptrs[4] = {x, bias, residual, y};
+    for (const void* p : ptrs)
+        if (!elem_aligned(p, e)) return FUSE_ERR_MISALIGNED;
+    const size_t pb = (size_t)hidden * e;
+    if (bad_alias(y, *tb, x, *tb) || bad_alias(y, *tb, residual, *tb) || overlaps(y, *tb, bias, pb))
+        return FUSE_ERR_ALIAS;
+    bool a = (pb % 16) == 0;
+    for (const void* p : ptrs)
+        if (!aligned16(p)) a = false;
+    *vec = a;
+    return FUSE_OK;
+}
+
+fuse_status_t fuse_bias_gelu_residual(const void* x, const void* bias, const void* residual, void* y,
+                                      int64_t rows, int64_t hidden, fuse_dtype_t dt, void* stream) {
+    size_t tb = 0;
+    bool vec = false;
+    fuse_status_t st = check_bias_gelu_residual(x, bias, residual, y, rows, hidden, dt, &tb, &vec);
+    if (st != FUSE_OK || rows == 0) return st;
+    const int64_t n = rows * hidden;
+    const int ch = ew_chunks();
+    return hip_status(by_dtype(dt, [&]<fuse::DT D>() {
+        return fuse::launch_ew<D>(fuse::EwOp::BiasGeluRes, vec, x, residual, bias, y, n, hidden, ch,
+                                  (hipStream_t)stream);
+    }));
+}
+
+// ------------------------------------------------------------------------------------------------
+// Row softmax
+// ------------------------------------------------------------------------------------------------
+
+static fuse_status_t check_softmax(const void* x, void* y, int64_t rows, int64_t cols, float scale,
+                                   fuse_dtype_t dt, size_t* tb, bool* vec) {
+    fuse_status_t st = check_rows(rows, cols, FUSE_MAX_SOFTMAX_COLS, dt, tb);
+    if (st != FUSE_OK) return st;
+    if (!isfinite(scale)) return FUSE_ERR_BAD_VALUE;
+    if (rows == 0) return FUSE_OK;
+    if (!x || !y) return FUSE_ERR_NULL_PTR;
+    const int e = elem_bytes(dt);
+    if (!elem_aligned(x, e) || !elem_aligned(y, e)) return FUSE_ERR_MISALIGNED;
+    if (bad_alias(y, *tb, x, *tb)) return FUSE_ERR_ALIAS;
+    *vec = aligned16(x) && aligned16(y) && ((size_t)cols * e) % 16 == 0;
+    return FUSE_OK;
+}
+
+fuse_status_t fuse_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, float scale,
+                                fuse_dtype_t dt, void* stream) {
+    size_t tb = 0;
+    bool vec = false;
+    fuse_status_t st = check_softmax(x, y, rows, cols, scale, dt, &tb, &vec);
+    if (st != FUSE_OK || rows == 0) return st;
+    const fuse::RowPlan plan = fuse::plan_row(cols, elem_bytes(dt), vec, env_int("FUSE_ROW_WPR"));
+    return hip_status(by_dtype(dt, [&]<fuse::DT D>() {
+        return fuse::launch_softmax_rows<D>(x, y, rows, (int)cols, scale, plan, (hipStream_t)stream);
+    }));
+}
+
+// ------------------------------------------------------------------------------------------------
+// SwiGLU dual GEMM
+// ------------------------------------------------------------------------------------------------
+
+static fuse_status_t check_swiglu(const void* a, const void* b1, const void* b2, void* out,
+                                  int64_t M, int64_t N, int64_t K, fuse_dtype_t dt) {
+    if (!valid_dtype(dt)) return FUSE_ERR_BAD_DTYPE;
+    if (dt != FUSE_BF16) return FUSE_ERR_BAD_DTYPE;
+    if (M < 0 || N < 1 || K < 1) return FUSE_ERR_BAD_SHAPE;
+    const int64_t lim = INT64_C(0x7fffffff);
+    if (M > lim || N > lim || K > lim) return FUSE_ERR_BAD_SHAPE;
+    size_t ab, bb, ob;
+    if (!tensor_bytes(M, K, 2, &ab) || !tensor_bytes(K, N, 2, &bb) || !tensor_bytes(M, N, 2, &ob))
+        return FUSE_ERR_BAD_SHAPE;
+    if (M == 0) return FUSE_OK;
+    if (!a || !b1 || !b2 || !out) return FUSE_ERR_NULL_PTR;
+    if (!elem_aligned(a, 2) || !elem_aligned(b1, 2) || !elem_aligned(b2, 2) || !elem_aligned(out, 2))
+        return FUSE_ERR_MISALIGNED;
+    if (overlaps(out, ob, a, ab) || overlaps(out, ob, b1, bb) || overlaps(out, ob, b2, bb))
+        return FUSE_ERR_ALIAS;
+    return FUSE_OK;
+}
+
+fuse_status_t fuse_swiglu_dualgemm(const void* a, const void* b1, const void* b2, void* out,
+                                   int64_t M, int64_t N, int64_t K, fuse_dtype_t dt, void* stream) {
+    fuse_status_t st = check_swiglu(a, b1, b2, out, M, N, K, dt);
+    if (st != FUSE_OK || M == 0) return st;
+    return hip_status(fuse::launch_swiglu(a, b1, b2, out, (int)M, (int)N, (int)K, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------------------------------------
+// Unfused baselines
+// ------------------------------------------------------------------------------------------------
+
+size_t fuse_unfused_workspace_bytes(fuse_op_t op, int64_t d0, int64_t d1, int64_t d2,
+                                    fuse_dtype_t dt) {
+    if (!valid_dtype(dt)) return 0;
+    size_t tb = 0;
+    switch (op) {
+        case FUSE_OP_ADD_LAYERNORM:
+            if (!tensor_bytes(d0, d1, elem_bytes(dt), &tb)) return 0;
+            return round256(tb);
+        case FUSE_OP_BIAS_GELU_RESIDUAL:
+            if (!tensor_bytes(d0, d1, elem_bytes(dt), &tb)) return 0;
+            return 2 * round256(tb);
+        case FUSE_OP_SOFTMAX_ROWS:
+            if (!tensor_bytes(d0, d1, elem_bytes(dt), &tb)) return 0;
+            return round256(tb) + 2 * round256((size_t)d0 * 4);
+        case FUSE_OP_SWIGLU:
+            if (dt != FUSE_BF16 || !tensor_bytes(d0, d1, 2, &tb)) return 0;
+            return 2 * round256(tb);
+    }
+    return 0;
+}
+
+static bool workspace_ok(const void* ws, size_t have, size_t need) {
+    return ws && have >= need && ((uintptr_t)ws & 255u) == 0;
+}
+
+fuse_status_t fuse_unfused_add_layernorm(const void* x, const void* residual, const void* gamma,
+                                         const void* beta, void* y, int64_t rows, int64_t hidden,
+                                         float eps, fuse_dtype_t dt, void* ws, size_t ws_bytes,
+                                         void* stream) {
+    size_t tb = 0;
+    bool vec = false;
+    fuse_status_t st = check_add_layernorm(x, residual, gamma, beta, y, rows, hidden, eps, dt, &tb, &vec);
+    if (st != FUSE_OK || rows == 0) return st;
+    if (!residual) return FUSE_ERR_NULL_PTR;
+    const size_t need = fuse_unfused_workspace_bytes(FUSE_OP_ADD_LAYERNORM, rows, hidden, 0, dt);
+    if (!workspace_ok(ws, ws_bytes, need)) return FUSE_ERR_WORKSPACE;
+    const size_t pb = (size_t)hidden * elem_bytes(dt);
+    if (overlaps(ws, need, x, tb) || overlaps(ws, need, residual, tb) || overlaps(ws, need, y, tb) ||
+        overlaps(ws, need, gamma, pb) || overlaps(ws, need, beta, pb))
+        return FUSE_ERR_WORKSPACE;
+    const fuse::RowPlan plan = fuse::plan_row(hidden, elem_bytes(dt), vec, env_int("FUSE_ROW_WPR"));
+    const int ch = ew_chunks();
+    return hip_status(by_dtype(dt, [&]<fuse::DT D>() {
+        hipError_t e = fuse::launch_ew<D>(fuse::EwOp::Add, vec, x, residual, nullptr, ws, rows * hidden,
+                                          hidden, ch, (hipStream_t)stream);
+        if (e != hipSuccess) return e;
+        return fuse::launch_add_layernorm<D>(ws, nullptr, gamma, beta, y, rows, (int)hidden, eps, plan,
+                                             (hipStream_t)stream);
+    }));
+}
+
+fuse_status_t fuse_unfused_bias_gelu_residual(const void* x, const void* bias, const void* residual,
+                                              void* y, int64_t rows, int64_t hidden, fuse_dtype_t dt,
+                                              void* ws, size_t ws_bytes, void* stream) {
+    size_t tb = 0;
+    bool vec = false;
+    fuse_status_t st = check_bias_gelu_residual(x, bias, residual, y, rows, hidden, dt, &tb, &vec);
+    if (st != FUSE_OK || rows == 0) return st;
+    const size_t need = fuse_unfused_workspace_bytes(FUSE_OP_BIAS_GELU_RESIDUAL, rows, hidden, 0, dt);
+    if (!workspace_ok(ws, ws_bytes, need)) return FUSE_ERR_WORKSPACE;
+    const size_t pb = (size_t)hidden * elem_bytes(dt);
+    if (overlaps(ws, need, x, tb) || overlaps(ws, need, residual, tb) || overlaps(ws, need, y, tb) ||
+        overlaps(ws, need, bias, pb))
+        return FUSE_ERR_WORKSPACE;
+    void* t = ws;
+    void* g = (char*)ws + round256(tb);
+    const int64_t n = rows * hidden;
+    const int ch = ew_chunks();
+    const hipStream_t s = (hipStream_t)stream;
+    return hip_status(by_dtype(dt, [&]<fuse::DT D>() {
+        hipError_t e = fuse::launch_ew<D>(fuse::EwOp::BiasAdd, vec, x, nullptr, bias, t, n, hidden, ch, s);
+        if (e != hipSuccess) return e;
+        e = fuse::launch_ew<D>(fuse::EwOp::Gelu, vec, t, nullptr, nullptr, g, n, hidden, ch, s);
+        if (e != hipSuccess) return e;
+        return fuse::launch_ew<D>(fuse::EwOp::Add, vec, g, residual, nullptr, y, n, hidden, ch, s);
+    }));
+}
+
+fuse_status_t fuse_unfused_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, float scale,
+                                        fuse_dtype_t dt, void* ws, size_t ws_bytes, void* stream) {
+    size_t tb = 0;
+    bool vec = false;
+    fuse_status_t st = check_softmax(x, y, rows, cols, scale, dt, &tb, &vec);
+    if (st != FUSE_OK || rows == 0) return st;
+    const size_t need = fuse_unfused_workspace_bytes(FUSE_OP_SOFTMAX_ROWS, rows, cols, 0, dt);
+    if (!workspace_ok(ws, ws_bytes, need)) return FUSE_ERR_WORKSPACE;
+    if (overlaps(ws, need, x, tb) || overlaps(ws, need, y, tb)) return FUSE_ERR_WORKSPACE;
+    void* e = ws;
+    float* m = (float*)((char*)ws + round256(tb));
+    float* s = (float*)((char*)m + round256((size_t)rows * 4));
+    return hip_status(by_dtype(dt, [&]<fuse::DT D>() {
+        return fuse::launch_softmax_unfused<D>(x, y, rows, (int)cols, scale, vec, e, m, s,
+                                               (hipStream_t)stream);
+    }));
+}
+
+fuse_status_t fuse_unfused_swiglu(const void* a, const void* b1, const void* b2, void* out, int64_t M,
+                                  int64_t N, int64_t K, fuse_dtype_t dt, void* ws, size_t ws_bytes,
+                                  void* stream) {
+    fuse_status_t st = check_swiglu(a, b1, b2, out, M, N, K, dt);
+    if (st != FUSE_OK || M == 0) return st;
+    const size_t need = fuse_unfused_workspace_bytes(FUSE_OP_SWIGLU, M, N, K, dt);
+    if (!workspace_ok(ws, ws_bytes, need)) return FUSE_ERR_WORKSPACE;
+    const size_t ab = (size_t)M * K * 2, bb = (size_t)K * N * 2, ob = (size_t)M * N * 2;
+    if (overlaps(ws, need, a, ab) || overlaps(ws, need, b1, bb) || overlaps(ws, need, b2, bb) ||
+        overlaps(ws, need, out, ob))
+        return FUSE_ERR_WORKSPACE;
+    void* c1 = ws;
+    void* c2 = (char*)ws + round256(ob);
+    return hip_status(fuse::launch_swiglu_unfused(a, b1, b2, out, (int)M, (int)N, (int)K, c1, c2,
+                                                  (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------------------------------------
+// Calibration copy
+// ------------------------------------------------------------------------------------------------
+
+fuse_status_t fuse_copy(const void* src, void* dst, size_t bytes, void* stream) {
+    if (bytes == 0) return FUSE_OK;
+    if (!src || !dst) return FUSE_ERR_NULL_PTR;
+    if (bytes > ((size_t)1 << 40)) return FUSE_ERR_BAD_SHAPE;
+    if (overlaps(src, bytes, dst, bytes)) return FUSE_ERR_ALIAS;
+    return hip_status(fuse::launch_copy(src, dst, bytes, (hipStream_t)stream));
+}
+
+}  // extern "C"

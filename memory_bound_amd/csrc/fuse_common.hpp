@@ -1,0 +1,180 @@
+// fuse_common.hpp -- device helpers shared by the libfuse kernels (gfx950, wave64).
+//
+// Storage types, 128-bit vector I/O, round-to-nearest-even conversions, wave-wide reductions
+// built on DPP lane permutations and one ds_swizzle, and the scalar math the fused epilogues
+// need (exp through v_exp_f32, the normal CDF through a published erfc approximation).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fuse {
+
+// ------------------------------------------------------------------------------------------------
+// storage types
+// ------------------------------------------------------------------------------------------------
+
+enum class DT : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+template <DT D> struct Elem;
+template <> struct Elem<DT::F32> { using T = float;    static constexpr int VEC = 4; };
+template <> struct Elem<DT::F16> { using T = uint16_t; static constexpr int VEC = 8; };
+template <> struct Elem<DT::BF16> { using T = uint16_t; static constexpr int VEC = 8; };
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+__device__ __forceinline__ uint32_t f32_to_f16(float f) {
+    // v_cvt_f16_f32 rounds to nearest even in the default mode
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __builtin_bit_cast(float, bits16 << 16);
+}
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // NaN stays a quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);                                // round to nearest even
+    return u >> 16;
+}
+
+template <DT D> __device__ __forceinline__ float load_scalar(const typename Elem<D>::T* p) {
+    if constexpr (D == DT::F32) return *p;
+    else if constexpr (D == DT::F16) return f16_to_f32(*p);
+    else return bf16_to_f32(*p);
+}
+template <DT D> __device__ __forceinline__ void store_scalar(typename Elem<D>::T* p, float v) {
+    if constexpr (D == DT::F32) *p = v;
+    else if constexpr (D == DT::F16) *p = (uint16_t)f32_to_f16(v);
+    else *p = (uint16_t)f32_to_bf16(v);
+}
+
+// One 128-bit word <-> VEC fp32 values.
+template <DT D> __device__ __forceinline__ void unpack(const uint4& w, float* out) {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+    if constexpr (D == DT::F32) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) out[i] = __builtin_bit_cast(float, u[i]);
+    } else if constexpr (D == DT::F16) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            out[2 * i] = f16_to_f32(u[i] & 0xffffu);
+            out[2 * i + 1] = f16_to_f32(u[i] >> 16);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            out[2 * i] = __builtin_bit_cast(float, u[i] << 16);
+            out[2 * i + 1] = __builtin_bit_cast(float, u[i] & 0xffff0000u);
+        }
+    }
+}
+
+template <DT D> __device__ __forceinline__ uint4 pack(const float* v) {
+    uint32_t u[4];
+    if constexpr (D == DT::F32) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) u[i] = __builtin_bit_cast(uint32_t, v[i]);
+    } else if constexpr (D == DT::F16) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) u[i] = f32_to_f16(v[2 * i]) | (f32_to_f16(v[2 * i + 1]) << 16);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) u[i] = f32_to_bf16(v[2 * i]) | (f32_to_bf16(v[2 * i + 1]) << 16);
+    }
+    return make_uint4(u[0], u[1], u[2], u[3]);
+}
+
+__device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void store16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// ------------------------------------------------------------------------------------------------
+// wave64 all-reduce: every lane ends with the same value, combined in a fixed order.
+//
+// Steps 1-4 are DPP permutations inside each 16-lane row (partner lane 1, 2, mirrored half
+// row, mirrored row); step 5 exchanges the two 16-lane rows of each half wave with ds_swizzle
+// (xor 16); step 6 adds lane 0 and lane 32.  Each step pairs lanes symmetrically, so all lanes
+// compute bit-identical results.
+// ------------------------------------------------------------------------------------------------
+
+enum : int {
+    DPP_QUAD_XOR1 = 0xB1,          // quad_perm [1,0,3,2]
+    DPP_QUAD_XOR2 = 0x4E,          // quad_perm [2,3,0,1]
+    DPP_ROW_HALF_MIRROR = 0x141,   // lane i <- lane 7-i within 8
+    DPP_ROW_MIRROR = 0x140,        // lane i <- lane 15-i within 16
+    SWZ_XOR16 = 0x401F             // ds_swizzle bit mode: and 0x1f, or 0, xor 0x10
+};
+
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                              0xF, 0xF, false));
+}
+__device__ __forceinline__ float swz_xor16(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), SWZ_XOR16));
+}
+__device__ __forceinline__ float lane_read(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+struct SumOp {
+    __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct MaxOp {
+    __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+template <class Op> __device__ __forceinline__ float wave_allreduce(float v, Op op) {
+    v = op(v, dpp<DPP_QUAD_XOR1>(v));
+    v = op(v, dpp<DPP_QUAD_XOR2>(v));
+    v = op(v, dpp<DPP_ROW_HALF_MIRROR>(v));
+    v = op(v, dpp<DPP_ROW_MIRROR>(v));
+    v = op(v, swz_xor16(v));
+    return op(lane_read(v, 0), lane_read(v, 32));
+}
+
+// ------------------------------------------------------------------------------------------------
+// scalar math
+// ------------------------------------------------------------------------------------------------
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+// 2^x on the transcendental unit (v_exp_f32).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+// e^x as 2^(x log2 e).
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
+
+// Complementary error function for z >= 0 with fractional error below 1.2e-7 everywhere:
+// the Chebyshev-fitted form of Press, Teukolsky, Vetterling & Flannery, "Numerical Recipes"
+// (2nd ed., §6.2, routine erfcc): erfc(z) ~ t * exp(-z^2 + P(t)), t = 1 / (1 + z/2), with P a
+// degree-9 polynomial.  Relative (not just absolute) accuracy matters here: the GELU tail
+// t * Phi(t) for negative t is built from erfc directly.
+__host__ __device__ __forceinline__ float erfc_nonneg(float z, float t) {
+    float p = 0.17087277f;
+    p = p * t + -0.82215223f;
+    p = p * t + 1.48851587f;
+    p = p * t + -1.13520398f;
+    p = p * t + 0.27886807f;
+    p = p * t + -0.18628806f;
+    p = p * t + 0.09678418f;
+    p = p * t + 0.37409196f;
+    p = p * t + 1.00002368f;
+    p = p * t + -1.26551223f;
+    return p - z * z;  // exponent; caller applies t * exp(.)
+}
+
+// GELU(t) = t * Phi(t), Phi(t) = erfc(-t / sqrt 2) / 2.
+__device__ __forceinline__ float gelu_erf(float t) {
+    const float z = fabsf(t) * 0.70710678118654752f;
+    const float w = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
+    const float ec = w * exp_fast(erfc_nonneg(z, w));  // erfc(|t|/sqrt 2)
+    const float half_ec = 0.5f * ec;
+    const float phi = t < 0.0f ? half_ec : 1.0f - half_ec;
+    return t * phi;
+}
+
+// SiLU(c) = c / (1 + e^-c).
+__device__ __forceinline__ float silu(float c) {
+    return c * __builtin_amdgcn_rcpf(1.0f + exp_fast(-c));
+}
+
+}  // namespace fuse

@@ -1,0 +1,50 @@
+// launch.hpp -- internal interface between the C ABI (abi.hip) and the kernel translation units.
+// Every launcher only enqueues on `stream`; the ABI layer has already validated the arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fuse_common.hpp"
+
+namespace fuse {
+
+// Shape of a register-resident row kernel launch: 128-bit or per-element access, chunks per
+// lane (NV) and waves per row (WPR).
+struct RowPlan {
+    bool vec;
+    int nv;
+    int wpr;
+};
+
+// Plan for a row of n elements of elem_bytes each; `aligned` = every pointer is 16-byte aligned
+// and n * elem_bytes is a multiple of 16.  `wpr_override` > 0 forces the waves per row on the
+// 128-bit path when the resulting chunks per lane stay within the compiled set.
+RowPlan plan_row(int64_t n, int elem_bytes, bool aligned, int wpr_override);
+
+enum class EwOp : int { BiasGeluRes = 0, Add = 1, BiasAdd = 2, Gelu = 3, SiluMul = 4 };
+
+template <DT D>
+hipError_t launch_add_layernorm(const void* x, const void* res, const void* gamma, const void* beta,
+                                void* y, int64_t rows, int hidden, float eps, RowPlan plan,
+                                hipStream_t stream);
+template <DT D>
+hipError_t launch_softmax_rows(const void* x, void* y, int64_t rows, int cols, float scale,
+                               RowPlan plan, hipStream_t stream);
+template <DT D>
+hipError_t launch_ew(EwOp op, bool vec, const void* a, const void* b, const void* c, void* out,
+                     int64_t n, int64_t hidden, int chunks_per_thread, hipStream_t stream);
+template <DT D>
+hipError_t launch_softmax_unfused(const void* x, void* y, int64_t rows, int cols, float scale,
+                                  bool vec, void* e, float* m, float* s, hipStream_t stream);
+
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+// SwiGLU dual GEMM, bf16.  unfused = true runs the scheme-A pair instead: the same product
+// kernel storing c1 and c2 (bf16, in `c1`, `c2`), then the element-wise SiLU(c1) * c2.
+hipError_t launch_swiglu(const void* a, const void* b1, const void* b2, void* out, int M, int N,
+                         int K, hipStream_t stream);
+hipError_t launch_swiglu_unfused(const void* a, const void* b1, const void* b2, void* out, int M,
+                                 int N, int K, void* c1, void* c2, hipStream_t stream);
+
+}  // namespace fuse

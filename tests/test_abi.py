@@ -1,0 +1,173 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header declares, and
+rejects bad arguments with the documented status before touching any device.
+
+Only argument combinations that fail validation (or are documented no-ops) are passed here, so
+nothing is ever launched.  The fake pointer values are never dereferenced: validation compares
+addresses only.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "libfuse.h")
+
+OK, NULL, SHAPE, DTYPE, VALUE, ALIAS, UNSUP, WS, MISAL, HIP = range(10)
+F32, F16, BF16 = 0, 1, 2
+P = 1 << 20  # fake, 256-byte aligned "device" addresses; never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from memory_bound_amd import api as libfuse
+    if not os.path.exists(libfuse.LIB_PATH):
+        import memory_bound_amd.build as b
+        b.build()
+    return libfuse.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fuse_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_operations():
+    names = declared_functions()
+    for n in ("fuse_add_layernorm", "fuse_bias_gelu_residual", "fuse_softmax_rows", "fuse_swiglu_dualgemm"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from memory_bound_amd import api as libfuse
+    names = declared_functions()
+    assert set(names) == set(libfuse.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    for code in range(10):
+        s = lib.fuse_status_string(code).decode()
+        assert s.startswith("FUSE_")
+    assert b"gfx950" in lib.fuse_version()
+    assert lib.fuse_last_hip_error() == 0
+
+
+def v(x):
+    return ctypes.c_void_p(x)
+
+
+def ln(lib, x=P, r=2 * P, g=3 * P, b=4 * P, y=5 * P, rows=4, hidden=64, eps=1e-5, dt=F16):
+    return lib.fuse_add_layernorm(v(x), v(r), v(g), v(b), v(y), rows, hidden, eps, dt, None)
+
+
+def test_add_layernorm_validation(lib):
+    H = 1 << 12  # bytes per 64-element... spacing between fake buffers is 1 MiB, large enough
+    assert ln(lib, x=0) == NULL
+    assert ln(lib, g=0) == NULL
+    assert ln(lib, b=0) == NULL
+    assert ln(lib, y=0) == NULL
+    assert ln(lib, rows=-1) == SHAPE
+    assert ln(lib, hidden=0) == SHAPE
+    assert ln(lib, hidden=16385) == UNSUP
+    assert ln(lib, dt=7) == DTYPE
+    assert ln(lib, eps=float("nan")) == VALUE
+    assert ln(lib, eps=float("inf")) == VALUE
+    assert ln(lib, eps=-1.0) == VALUE
+    assert ln(lib, x=P + 1) == MISAL
+    assert ln(lib, y=P + 2) == ALIAS            # partial overlap with x
+    assert ln(lib, y=3 * P + 64) == ALIAS       # overlaps gamma
+    assert ln(lib, y=3 * P) == ALIAS            # equals gamma: still not allowed
+    assert ln(lib, rows=0) == OK                # no-op, nothing launched
+    assert ln(lib, rows=0, x=0, y=0) == OK
+    assert ln(lib, rows=1 << 31) == SHAPE
+    assert H
+
+
+def test_bias_gelu_residual_validation(lib):
+    def call(x=P, bias=2 * P, r=3 * P, y=4 * P, rows=4, hidden=64, dt=F16):
+        return lib.fuse_bias_gelu_residual(v(x), v(bias), v(r), v(y), rows, hidden, dt, None)
+    assert call(bias=0) == NULL
+    assert call(r=0) == NULL
+    assert call(hidden=0) == SHAPE
+    assert call(dt=5) == DTYPE
+    assert call(y=2 * P) == ALIAS               # writes over the bias
+    assert call(y=3 * P + 16) == ALIAS          # partial overlap with residual
+    assert call(rows=1 << 20, hidden=1 << 14) == SHAPE  # 2^34 elements
+    assert call(rows=0) == OK
+
+
+def test_softmax_validation(lib):
+    def call(x=P, y=2 * P, rows=4, cols=64, scale=1.0, dt=F16):
+        return lib.fuse_softmax_rows(v(x), v(y), rows, cols, scale, dt, None)
+    assert call(x=0) == NULL
+    assert call(cols=0) == SHAPE
+    assert call(cols=16385) == UNSUP
+    assert call(scale=float("inf")) == VALUE
+    assert call(scale=float("nan")) == VALUE
+    assert call(y=P + 64) == ALIAS
+    assert call(x=P + 1) == MISAL
+    assert call(dt=3) == DTYPE
+    assert call(rows=0) == OK
+
+
+def test_swiglu_validation(lib):
+    def call(a=P, b1=8 * P, b2=16 * P, out=24 * P, M=128, N=128, K=64, dt=BF16):
+        return lib.fuse_swiglu_dualgemm(v(a), v(b1), v(b2), v(out), M, N, K, dt, None)
+    assert call(dt=F16) == DTYPE
+    assert call(dt=F32) == DTYPE
+    assert call(a=0) == NULL
+    assert call(N=0) == SHAPE
+    assert call(K=0) == SHAPE
+    assert call(M=-1) == SHAPE
+    assert call(M=1 << 31) == SHAPE
+    assert call(out=8 * P) == ALIAS             # out over b1
+    assert call(out=P) == ALIAS                 # out over a (in-place is not allowed here)
+    assert call(b1=8 * P + 1) == MISAL
+    assert call(M=0) == OK
+
+
+def test_unfused_workspace_bytes(lib):
+    f = lib.fuse_unfused_workspace_bytes
+    t = 2048 * 4096 * 2
+    assert f(0, 2048, 4096, 0, F16) == t
+    assert f(1, 2048, 4096, 0, F16) == 2 * t
+    assert f(2, 65536, 2048, 0, F16) == 65536 * 2048 * 2 + 2 * 65536 * 4
+    assert f(3, 2048, 8960, 1536, BF16) == 2 * 2048 * 8960 * 2
+    assert f(3, 2048, 8960, 1536, F16) == 0
+    assert f(0, -1, 4096, 0, F16) == 0
+    assert f(9, 1, 1, 1, F16) == 0
+
+
+def test_unfused_validation(lib):
+    need = lib.fuse_unfused_workspace_bytes(0, 4, 64, 0, F16)
+    ws = 40 * P
+    args = [v(P), v(2 * P), v(3 * P), v(4 * P), v(5 * P), 4, 64, 1e-5, F16]
+    assert lib.fuse_unfused_add_layernorm(*args, v(0), need, None) == WS
+    assert lib.fuse_unfused_add_layernorm(*args, v(ws), need - 1, None) == WS
+    assert lib.fuse_unfused_add_layernorm(*args, v(ws + 16), need, None) == WS   # not 256-aligned
+    assert lib.fuse_unfused_add_layernorm(*args, v(P), need, None) == WS         # overlaps x
+    no_res = [v(P), v(0), v(3 * P), v(4 * P), v(5 * P), 4, 64, 1e-5, F16]
+    assert lib.fuse_unfused_add_layernorm(*no_res, v(ws), need, None) == NULL
+    sw = lib.fuse_unfused_workspace_bytes(3, 128, 128, 64, BF16)
+    assert lib.fuse_unfused_swiglu(v(P), v(8 * P), v(16 * P), v(24 * P), 128, 128, 64, BF16, v(ws),
+                                   sw - 256, None) == WS
+
+
+def test_copy_validation(lib):
+    assert lib.fuse_copy(v(P), v(P + 8), 64, None) == ALIAS
+    assert lib.fuse_copy(v(0), v(P), 64, None) == NULL
+    assert lib.fuse_copy(v(P), v(2 * P), 0, None) == OK
+    assert lib.fuse_copy(v(P), v(2 * P), (1 << 40) + 1, None) == SHAPE
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    from memory_bound_amd import api as libfuse
+    x = torch.zeros(4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        libfuse.fuse_add_layernorm(x, x, x[0], x[0])

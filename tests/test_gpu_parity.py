@@ -1,0 +1,371 @@
+"""Parity of the HIP kernels with the CPU oracle, through the C ABI (GPU required).
+
+Small and medium shapes are compared element by element on every output; the full workload
+shapes run in the launch configuration the benchmark times and are compared on every output
+where the oracle is fast (Add+LayerNorm, GELU chain) and on a seeded sample of whole rows
+otherwise (softmax, SwiGLU), plus properties that hold for every row.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from memory_bound_amd import api, synth
+from oracle.tolerance import assert_close, compare
+
+pytestmark = pytest.mark.gpu
+
+KIND = {"f32": "f32", "f16": "f16", "bf16": "bf16"}
+
+
+def cuda(d):
+    return {k: (v.to("cuda") if torch.is_tensor(v) else v) for k, v in d.items()}
+
+
+def announce(msg):
+    print(f"\n[gpu-case] {msg}", flush=True)
+
+
+# ------------------------------------------------------------------------------------------------
+# ResidualAdd + LayerNorm
+# ------------------------------------------------------------------------------------------------
+
+LN_SHAPES = [
+    (64, 768, "f32"),      # small fp32 workload
+    (37, 4096, "f16"),     # odd row count: last workgroup partly empty
+    (130, 4096, "bf16"),
+    (5, 1000, "f16"),      # row not a whole number of 16-byte words: per-element path
+    (3, 7, "f32"),
+    (2, 1, "f16"),         # one-element rows: output is beta
+    (4, 8, "f16"),         # one chunk per row
+    (7, 16384, "f16"),     # longest row
+    (6, 16384, "f32"),
+    (9, 8192, "bf16"),
+    (11, 12288, "f16"),    # 3 x 4096: the last chunk group of each lane partly outside the row
+    (3, 4097, "f32"),      # per-element path with several waves per row
+    (33, 2048, "f32"),
+]
+
+
+@pytest.mark.parametrize("rows,hidden,dtype", LN_SHAPES)
+def test_add_layernorm_parity(rows, hidden, dtype):
+    announce(f"add_layernorm {rows}x{hidden} {dtype}")
+    d = synth.add_layernorm_inputs(rows, hidden, dtype, seed=rows * 131 + hidden)
+    g = cuda(d)
+    y = api.fuse_add_layernorm(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"])
+    ref = oracle.add_layernorm(d["x"], d["residual"], d["gamma"], d["beta"], np.float32(d["eps"]))
+    assert_close(y, ref, KIND[dtype], f"add_layernorm {rows}x{hidden} {dtype}")
+
+
+@pytest.mark.parametrize("name", ["addln_f32_64x768", "addln_f16_2048x4096", "addln_f16_16384x4096"])
+def test_add_layernorm_workloads_full(name):
+    w = synth.WORKLOADS[name]
+    announce(f"add_layernorm workload {name}")
+    d = w.inputs()
+    g = cuda(d)
+    y = api.fuse_add_layernorm(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"])
+    ref = oracle.add_layernorm(d["x"], d["residual"], d["gamma"], d["beta"], np.float32(d["eps"]))
+    r = assert_close(y, ref, KIND[w.dtype], name)
+    print(f"  max_abs={r['max_abs']:.3e}", flush=True)
+
+
+def test_add_layernorm_no_residual_and_inplace():
+    announce("add_layernorm residual=None and in-place")
+    d = synth.add_layernorm_inputs(64, 4096, "f16", seed=5)
+    g = cuda(d)
+    y = api.fuse_add_layernorm(g["x"], None, g["gamma"], g["beta"], d["eps"])
+    assert_close(y, oracle.add_layernorm(d["x"], None, d["gamma"], d["beta"], np.float32(d["eps"])), "f16", "no residual")
+    x = g["x"].clone()
+    api.fuse_add_layernorm(x, g["residual"], g["gamma"], g["beta"], d["eps"], y=x)  # y == x
+    ref = oracle.add_layernorm(d["x"], d["residual"], d["gamma"], d["beta"], np.float32(d["eps"]))
+    assert_close(x, ref, "f16", "in place over x")
+    r = g["residual"].clone()
+    api.fuse_add_layernorm(g["x"], r, g["gamma"], g["beta"], d["eps"], y=r)  # y == residual
+    assert_close(r, ref, "f16", "in place over residual")
+
+
+def test_add_layernorm_misaligned_pointers():
+    announce("add_layernorm misaligned views")
+    rows, hidden = 6, 4096
+    d = synth.add_layernorm_inputs(rows, hidden, "f16", seed=6)
+    # views that start one element into a larger buffer: not 16-byte aligned
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+        v = buf[1:].view(t.shape)
+        v.copy_(t.to("cuda"))
+        return v
+    x, r, gm, bt = shifted(d["x"]), shifted(d["residual"]), shifted(d["gamma"]), shifted(d["beta"])
+    y = shifted(torch.zeros(rows, hidden, dtype=torch.float16))
+    api.fuse_add_layernorm(x, r, gm, bt, d["eps"], y=y)
+    ref = oracle.add_layernorm(d["x"], d["residual"], d["gamma"], d["beta"], np.float32(d["eps"]))
+    assert_close(y, ref, "f16", "misaligned")
+
+
+def test_add_layernorm_large_mean_rows():
+    # mean 1e4, spread 1: the statistics must not lose the variance to cancellation
+    announce("add_layernorm mean 1e4 fp32")
+    gen = torch.Generator().manual_seed(7)
+    x = (1e4 + torch.randn(16, 4096, generator=gen)).float()
+    r = torch.randn(16, 4096, generator=gen).float()
+    gm = torch.ones(4096)
+    bt = torch.zeros(4096)
+    y = api.fuse_add_layernorm(x.cuda(), r.cuda(), gm.cuda(), bt.cuda(), 1e-5)
+    ref = oracle.add_layernorm(x, r, gm, bt, np.float32(1e-5))
+    # fp32 inputs near 1e4 carry 1e-3 absolute quantum; the bound below is the fp32 rule scaled
+    # by the row's condition number (mean / std ~ 1e4)
+    err = np.abs(y.cpu().double().numpy() - ref).max()
+    assert err < 2e-3, err
+
+
+def test_add_layernorm_constant_rows_give_beta():
+    announce("add_layernorm constant rows")
+    x = torch.full((8, 768), 3.0, dtype=torch.float16)
+    r = torch.full((8, 768), -1.5, dtype=torch.float16)
+    gm = torch.rand(768).half()
+    bt = torch.randn(768).half()
+    y = api.fuse_add_layernorm(x.cuda(), r.cuda(), gm.cuda(), bt.cuda(), 1e-5)
+    assert torch.equal(y.cpu(), bt.expand(8, 768))
+
+
+def test_add_layernorm_zero_rows_is_noop():
+    x = torch.empty(0, 4096, dtype=torch.float16, device="cuda")
+    g = torch.ones(4096, dtype=torch.float16, device="cuda")
+    y = api.fuse_add_layernorm(x, x, g, g, 1e-5)
+    assert y.shape == (0, 4096)
+
+
+def test_add_layernorm_deterministic():
+    announce("add_layernorm determinism")
+    g = cuda(synth.add_layernorm_inputs(2048, 4096, "f16", seed=9))
+    y1 = api.fuse_add_layernorm(g["x"], g["residual"], g["gamma"], g["beta"], 1e-5)
+    y2 = api.fuse_add_layernorm(g["x"], g["residual"], g["gamma"], g["beta"], 1e-5)
+    assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("wpr", [1, 2, 4, 8])
+def test_add_layernorm_every_waves_per_row(monkeypatch, wpr):
+    # the tuning override picks other compiled launch shapes; all must agree with the oracle
+    announce(f"add_layernorm FUSE_ROW_WPR={wpr}")
+    monkeypatch.setenv("FUSE_ROW_WPR", str(wpr))
+    d = synth.add_layernorm_inputs(67, 4096, "f16", seed=10 + wpr)
+    g = cuda(d)
+    y = api.fuse_add_layernorm(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"])
+    ref = oracle.add_layernorm(d["x"], d["residual"], d["gamma"], d["beta"], np.float32(d["eps"]))
+    assert_close(y, ref, "f16", f"wpr={wpr}")
+
+
+# ------------------------------------------------------------------------------------------------
+# BiasAdd + GELU + Residual
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,hidden,dtype", [
+    (2048, 4096, "f16"),   # the full workload
+    (33, 768, "f32"),
+    (17, 4096, "bf16"),
+    (5, 1001, "f16"),      # per-element path
+    (1, 3, "f32"),
+    (300, 520, "f16"),     # chunk count not a multiple of the workgroup's
+])
+def test_bias_gelu_residual_parity(rows, hidden, dtype):
+    announce(f"bias_gelu_residual {rows}x{hidden} {dtype}")
+    d = synth.bias_gelu_residual_inputs(rows, hidden, dtype, seed=1002 if rows == 2048 else rows + hidden)
+    g = cuda(d)
+    y = api.fuse_bias_gelu_residual(g["x"], g["bias"], g["residual"])
+    ref = oracle.bias_gelu_residual(d["x"], d["bias"], d["residual"])
+    assert_close(y, ref, KIND[dtype], f"gelu {rows}x{hidden} {dtype}")
+
+
+def test_gelu_exhaustive_fp16_domain():
+    # every finite fp16 value t as x with bias 0 and residual 0: the kernel's GELU before the
+    # output rounding is held to the 1e-4 relative rule for approximate math; after rounding to
+    # fp32 output the comparison is direct
+    announce("gelu exhaustive fp16")
+    bits = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16)
+    t = bits.view(torch.float16)
+    t = t[torch.isfinite(t)].float()
+    n = t.numel()
+    hidden = 64
+    rows = (n + hidden - 1) // hidden
+    x = torch.zeros(rows * hidden)
+    x[:n] = t
+    x = x.view(rows, hidden)
+    zb = torch.zeros(hidden)
+    zr = torch.zeros(rows, hidden)
+    y = api.fuse_bias_gelu_residual(x.cuda(), zb.cuda(), zr.cuda()).cpu().double().numpy().ravel()[:n]
+    ref = oracle.bias_gelu_residual(x, zb, zr).ravel()[:n]
+    rel = np.abs(y - ref) / np.maximum(np.abs(ref), 1e-30)
+    small = np.abs(ref) < 1e-30  # GELU underflows: require an absolute 1e-30
+    assert np.all(np.abs(y - ref)[small] < 1e-30)
+    assert rel[~small].max() < 1e-4, rel[~small].max()
+
+
+def test_bias_gelu_residual_inplace_and_deterministic():
+    announce("gelu in place")
+    d = synth.bias_gelu_residual_inputs(64, 4096, "f16", seed=3)
+    g = cuda(d)
+    ref = oracle.bias_gelu_residual(d["x"], d["bias"], d["residual"])
+    y1 = api.fuse_bias_gelu_residual(g["x"], g["bias"], g["residual"])
+    y2 = api.fuse_bias_gelu_residual(g["x"], g["bias"], g["residual"])
+    assert torch.equal(y1, y2)
+    x = g["x"].clone()
+    api.fuse_bias_gelu_residual(x, g["bias"], g["residual"], y=x)
+    assert_close(x, ref, "f16", "gelu in place")
+
+
+# ------------------------------------------------------------------------------------------------
+# Row softmax
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,cols,dtype,scale", [
+    (256, 2048, "f16", 1 / math.sqrt(128)),
+    (37, 2048, "bf16", 1 / math.sqrt(128)),
+    (19, 768, "f32", 0.5),
+    (8, 16384, "f16", 1 / math.sqrt(128)),   # longest row
+    (5, 1000, "f16", 1.0),                   # per-element path
+    (3, 1, "f16", 1.0),                      # one column: exactly 1
+    (6, 333, "f32", -0.7),                   # negative scale
+    (12, 4096, "f16", 1 / math.sqrt(128)),
+])
+def test_softmax_parity(rows, cols, dtype, scale):
+    announce(f"softmax {rows}x{cols} {dtype} scale={scale}")
+    d = synth.softmax_inputs(rows, cols, dtype, seed=rows * 7 + cols)
+    y = api.fuse_softmax_rows(d["x"].cuda(), scale)
+    ref = oracle.softmax_rows(d["x"], np.float32(scale))
+    assert_close(y, ref, KIND[dtype], f"softmax {rows}x{cols}")
+
+
+def test_softmax_workload_sampled_rows():
+    w = synth.WORKLOADS["softmax_f16_65536x2048"]
+    announce("softmax workload 65536x2048")
+    d = w.inputs()
+    y = api.fuse_softmax_rows(d["x"].cuda(), d["scale"])
+    # every row: sum of the stored fp16 outputs within 2e-3 of one (emulated error ~3e-5)
+    sums = y.float().sum(dim=1)
+    assert (sums - 1).abs().max().item() < 2e-3
+    rng = np.random.default_rng(1005)
+    rows = np.sort(rng.choice(w.shape[0], 2048, replace=False))
+    idx = torch.from_numpy(rows)
+    ref = oracle.softmax_rows(d["x"][idx], np.float32(d["scale"]))
+    assert_close(y.cpu()[idx], ref, "f16", "softmax sampled rows")
+
+
+def test_softmax_constant_rows_and_inplace():
+    announce("softmax constant rows")
+    x = torch.full((4, 2048), 2.5, dtype=torch.float16, device="cuda")
+    y = api.fuse_softmax_rows(x, 0.3)
+    assert torch.all(y == 2.0 ** -11)
+    d = synth.softmax_inputs(64, 2048, "f16", seed=4)
+    ref = oracle.softmax_rows(d["x"], np.float32(d["scale"]))
+    x = d["x"].cuda()
+    api.fuse_softmax_rows(x, d["scale"], y=x)
+    assert_close(x, ref, "f16", "softmax in place")
+
+
+def test_softmax_nan_propagates():
+    x = torch.randn(2, 2048).half()
+    x[1, 100] = float("nan")
+    y = api.fuse_softmax_rows(x.cuda(), 1.0).cpu()
+    assert torch.isfinite(y[0]).all()
+    assert torch.isnan(y[1]).all()
+
+
+# ------------------------------------------------------------------------------------------------
+# SwiGLU dual GEMM
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [
+    (128, 128, 64),     # one tile, one K step
+    (256, 384, 192),    # several tiles and K steps
+    (130, 200, 136),    # ragged M, N, K (aligned rows: K, N multiples of 8)
+    (100, 72, 70),      # K not a multiple of 8: per-element loads
+    (1, 8, 16),
+    (64, 1000, 1536),   # the workload's K with a ragged N tile
+])
+def test_swiglu_parity(M, N, K):
+    announce(f"swiglu {M}x{N}x{K}")
+    d = synth.swiglu_inputs(M, N, K, "bf16", seed=M + N + K)
+    out = api.fuse_swiglu_dualgemm(d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda())
+    ref = oracle.swiglu(d["a"], d["b1"], d["b2"])
+    r = assert_close(out, ref, "bf16", f"swiglu {M}x{N}x{K}")
+    print(f"  max_abs={r['max_abs']:.3e}", flush=True)
+
+
+def test_swiglu_workload_sampled_rows():
+    w = synth.WORKLOADS["swiglu_bf16_2048x8960x1536"]
+    announce("swiglu workload 2048x8960x1536")
+    d = w.inputs()
+    out = api.fuse_swiglu_dualgemm(d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda()).cpu()
+    rng = np.random.default_rng(1006)
+    rows = torch.from_numpy(np.sort(rng.choice(w.shape[0], 48, replace=False)))
+    ref = oracle.swiglu(d["a"][rows], d["b1"], d["b2"])
+    r = assert_close(out[rows], ref, "bf16", "swiglu sampled rows")
+    nw = float(np.abs(out[rows].double().numpy() - ref).max() / np.abs(ref).max())
+    print(f"  max_abs={r['max_abs']:.3e} normwise={nw:.2e}", flush=True)
+    assert nw < 5e-3
+    out2 = api.fuse_swiglu_dualgemm(d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda()).cpu()
+    assert torch.equal(out, out2)
+
+
+# ------------------------------------------------------------------------------------------------
+# Unfused baselines against the oracle with rounded intermediates (twice the fp16 / bf16 rule:
+# an intermediate that sits on a rounding boundary may round the other way in fp32)
+# ------------------------------------------------------------------------------------------------
+
+def _loose(y, ref, kind, what):
+    r = compare(y, ref, kind)
+    if not r["ok"]:
+        assert r["max_excess"] <= 2.0, f"{what}: {r}"
+
+
+def test_unfused_add_layernorm():
+    announce("unfused add_layernorm")
+    d = synth.add_layernorm_inputs(2048, 4096, "f16", seed=1003)
+    g = cuda(d)
+    y = api.fuse_unfused_add_layernorm(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"])
+    ref = oracle.add_layernorm_unfused(d["x"], d["residual"], d["gamma"], d["beta"], np.float32(d["eps"]), "f16")
+    _loose(y, ref, "f16", "unfused add_layernorm")
+
+
+def test_unfused_bias_gelu_residual():
+    announce("unfused gelu chain")
+    d = synth.bias_gelu_residual_inputs(512, 4096, "f16", seed=1002)
+    g = cuda(d)
+    y = api.fuse_unfused_bias_gelu_residual(g["x"], g["bias"], g["residual"])
+    ref = oracle.bias_gelu_residual_unfused(d["x"], d["bias"], d["residual"], "f16")
+    _loose(y, ref, "f16", "unfused gelu")
+
+
+def test_unfused_softmax():
+    announce("unfused softmax")
+    d = synth.softmax_inputs(512, 2048, "f16", seed=1005)
+    y = api.fuse_unfused_softmax_rows(d["x"].cuda(), d["scale"])
+    ref = oracle.softmax_rows_unfused(d["x"], np.float32(d["scale"]), "f16")
+    _loose(y, ref, "f16", "unfused softmax")
+
+
+def test_unfused_swiglu():
+    announce("unfused swiglu")
+    d = synth.swiglu_inputs(256, 384, 192, "bf16", seed=11)
+    out = api.fuse_unfused_swiglu(d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda())
+    ref = oracle.swiglu_unfused(d["a"], d["b1"], d["b2"], "bf16")
+    _loose(out, ref, "bf16", "unfused swiglu")
+
+
+def test_copy_kernel():
+    announce("copy")
+    src = torch.randint(0, 255, ((1 << 20) + 7,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros_like(src)
+    api.fuse_copy(src, dst)
+    assert torch.equal(src, dst)
+    s2 = src[3:]
+    d2 = torch.zeros_like(s2)
+    api.fuse_copy(s2, d2)
+    assert torch.equal(s2, d2)
+
+
+def test_binding_reports_status_errors():
+    x = torch.zeros(4, 64, dtype=torch.float16, device="cuda")
+    with pytest.raises(api.FuseError):
+        api.fuse_softmax_rows(x, float("inf"))
