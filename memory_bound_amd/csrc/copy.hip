@@ -8,21 +8,22 @@ namespace fuse {
 // ------------------------------------------------------------------------------------------------
 // Plain copy (roofline calibration): 16-byte chunks, CH per thread, plus a byte tail kernel.
 // ------------------------------------------------------------------------------------------------
+// Workgroup b copies 16-byte chunks [b*256*CH, (b+1)*256*CH) through buffer resources that end
+// at the copy's end: every load is issued before the first store, no per-chunk branch.
 template <int CH>
 __global__ void __launch_bounds__(256)
 copy16_kernel(const uint4* src, uint4* dst, uint64_t n16) {
-    const uint64_t base = (uint64_t)blockIdx.x * (256 * CH) + threadIdx.x;
+    const uint64_t first = (uint64_t)blockIdx.x * (256u * CH);
+    const uint64_t left = n16 - first;
+    const uint32_t bytes = (uint32_t)(left < 256u * CH ? left : 256u * CH) * 16u;
+    const rsrc_t rs = make_rsrc(src + first, bytes);
+    const rsrc_t rd = make_rsrc(dst + first, bytes);
     uint4 v[CH];
 #pragma unroll
-    for (int j = 0; j < CH; j++) {
-        const uint64_t i = base + (uint64_t)j * 256;
-        if (i < n16) v[j] = src[i];
-    }
+    for (int j = 0; j < CH; j++) v[j] = bload16<AUX_STREAM>(rs, ((uint32_t)(j * 256) + threadIdx.x) * 16u);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < CH; j++) {
-        const uint64_t i = base + (uint64_t)j * 256;
-        if (i < n16) dst[i] = v[j];
-    }
+    for (int j = 0; j < CH; j++) bstore16<AUX_STREAM>(rd, ((uint32_t)(j * 256) + threadIdx.x) * 16u, v[j]);
 }
 
 __global__ void __launch_bounds__(256)

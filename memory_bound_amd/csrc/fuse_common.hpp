@@ -32,21 +32,8 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __builtin_bit_cast(float, bits16 << 16);
 }
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // NaN stays a quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);                                // round to nearest even
-    return u >> 16;
-}
-
-template <DT D> __device__ __forceinline__ float load_scalar(const typename Elem<D>::T* p) {
-    if constexpr (D == DT::F32) return *p;
-    else if constexpr (D == DT::F16) return f16_to_f32(*p);
-    else return bf16_to_f32(*p);
-}
-template <DT D> __device__ __forceinline__ void store_scalar(typename Elem<D>::T* p, float v) {
-    if constexpr (D == DT::F32) *p = v;
-    else if constexpr (D == DT::F16) *p = (uint16_t)f32_to_f16(v);
-    else *p = (uint16_t)f32_to_bf16(v);
+    // v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // One 128-bit word <-> VEC fp32 values.
@@ -85,8 +72,66 @@ template <DT D> __device__ __forceinline__ uint4 pack(const float* v) {
     return make_uint4(u[0], u[1], u[2], u[3]);
 }
 
-__device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ void store16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+// ------------------------------------------------------------------------------------------------
+// Raw buffer access.  A buffer resource covers [base, base + bytes); a load at an offset at or
+// beyond `bytes` returns zero and a store there is dropped, in hardware.  Kernels therefore issue
+// every load of a row or block unconditionally (no per-load branch, so the loads are all in
+// flight together) and let the range check mask the tails.  Offsets are 32-bit and relative to
+// the base, so bases are taken per row / per block / per tile.
+// ------------------------------------------------------------------------------------------------
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int RSRC_WORD3 = 0x00020000;  // gfx9-family raw (untyped) buffer access
+constexpr uint32_t OOB = 0x80000000u;   // an offset no resource covers: loads 0, stores dropped
+
+// Cache policy of the buffer instructions (gfx94x/gfx950 encoding: bit 0 sc0, bit 1 nt, bit 4
+// sc1).  Tensors that are read or written exactly once per launch use the non-temporal hint so
+// that they do not displace reused data (per-column parameters, other rows' tiles) in L2 and
+// the Infinity Cache; everything else uses the default policy.
+#ifndef FUSE_STREAM_AUX
+#define FUSE_STREAM_AUX 2
+#endif
+constexpr int AUX_DEFAULT = 0;
+constexpr int AUX_STREAM = FUSE_STREAM_AUX;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, RSRC_WORD3);
+}
+template <int AUX = AUX_DEFAULT> __device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX));
+}
+template <int AUX = AUX_DEFAULT>
+__device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, const uint4& v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, AUX);
+}
+template <int AUX = AUX_DEFAULT> __device__ __forceinline__ uint32_t bload_b16(rsrc_t r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, AUX);
+}
+template <int AUX = AUX_DEFAULT>
+__device__ __forceinline__ void bstore_b16(rsrc_t r, uint32_t off, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, (int)off, 0, AUX);
+}
+template <int AUX = AUX_DEFAULT> __device__ __forceinline__ uint32_t bload_b32(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, AUX);
+}
+template <int AUX = AUX_DEFAULT>
+__device__ __forceinline__ void bstore_b32(rsrc_t r, uint32_t off, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, AUX);
+}
+
+// One element at element index i of the buffer, widened to fp32 (0 outside the buffer).
+template <DT D, int AUX = AUX_DEFAULT> __device__ __forceinline__ float bload_elem(rsrc_t r, uint32_t i) {
+    if constexpr (D == DT::F32) return __builtin_bit_cast(float, bload_b32<AUX>(r, i * 4u));
+    else if constexpr (D == DT::F16) return f16_to_f32(bload_b16<AUX>(r, i * 2u));
+    else return bf16_to_f32(bload_b16<AUX>(r, i * 2u));
+}
+template <DT D, int AUX = AUX_DEFAULT> __device__ __forceinline__ void bstore_elem(rsrc_t r, uint32_t i, float v) {
+    if constexpr (D == DT::F32) bstore_b32<AUX>(r, i * 4u, __builtin_bit_cast(uint32_t, v));
+    else if constexpr (D == DT::F16) bstore_b16<AUX>(r, i * 2u, f32_to_f16(v));
+    else bstore_b16<AUX>(r, i * 2u, f32_to_bf16(v));
+}
 
 // ------------------------------------------------------------------------------------------------
 // wave64 all-reduce: every lane ends with the same value, combined in a fixed order.

@@ -14,6 +14,8 @@
 // them in wave order.  The order is fixed, so results are bit-reproducible run to run.
 #pragma once
 
+#include <type_traits>
+
 #include "fuse_common.hpp"
 
 namespace fuse {
@@ -41,7 +43,9 @@ __device__ __forceinline__ float row_allreduce(float v, Op op, float* lds_slot) 
     }
 }
 
-// Per-lane slice of one row: NV chunks of V elements.
+// Per-lane slice of one row: NV chunks of V elements.  Rows are read and written through buffer
+// resources whose range is the row (empty for a row past the end), so chunks beyond the row
+// load as zeros and are not stored, without branches.
 template <DT D, bool VECP, int NV, int WPR> struct RowSlice {
     using T = typename Elem<D>::T;
     static constexpr int V = VECP ? Elem<D>::VEC : 1;
@@ -51,36 +55,40 @@ template <DT D, bool VECP, int NV, int WPR> struct RowSlice {
 
     __device__ __forceinline__ RowSlice(int hidden) {
         const int lane = threadIdx.x & 63;
-        const int wpos = (threadIdx.x >> 6) % WPR;
+        const int wpos = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % WPR;
         first_chunk = wpos * 64 + lane;
         nchunk = hidden / V;  // per-element path: V = 1
     }
     __device__ __forceinline__ int chunk(int j) const { return first_chunk + j * WPR * 64; }
     __device__ __forceinline__ bool ok(int j) const { return chunk(j) < nchunk; }
 
-    // Read chunk j of `row` (or zeros when out of the row) as fp32.
-    __device__ __forceinline__ void load(const T* row, int j, bool active, float* out) const {
-        const int c = chunk(j);
-        if (active && c < nchunk) {
-            if constexpr (VECP) {
-                unpack<D>(load16(row + (int64_t)c * V), out);
-            } else {
-                out[0] = load_scalar<D>(row + c);
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < V; k++) out[k] = 0.0f;
-        }
+    // Raw bits of chunk j (a 128-bit word, or one element's bits on the per-element path).
+    using Raw = typename std::conditional<VECP, uint4, uint32_t>::type;
+    template <int AUX = AUX_DEFAULT> __device__ __forceinline__ Raw load_raw(rsrc_t r, int j) const {
+        if constexpr (VECP) return bload16<AUX>(r, (uint32_t)chunk(j) * 16u);
+        else if constexpr (sizeof(T) == 4) return bload_b32<AUX>(r, (uint32_t)chunk(j) * 4u);
+        else return bload_b16<AUX>(r, (uint32_t)chunk(j) * 2u);
     }
-    __device__ __forceinline__ void store(T* row, int j, bool active, const float* v) const {
-        const int c = chunk(j);
-        if (active && c < nchunk) {
-            if constexpr (VECP) {
-                store16(row + (int64_t)c * V, pack<D>(v));
-            } else {
-                store_scalar<D>(row + c, v[0]);
-            }
-        }
+    __device__ __forceinline__ void unpack_raw(const Raw& w, float* out) const {
+        if constexpr (VECP) unpack<D>(w, out);
+        else if constexpr (D == DT::F32) out[0] = __builtin_bit_cast(float, w);
+        else if constexpr (D == DT::F16) out[0] = f16_to_f32(w);
+        else out[0] = bf16_to_f32(w);
+    }
+    // One 32-bit word of a raw chunk (used to make later code depend on the load).
+    __device__ __forceinline__ static uint32_t word0(const Raw& w) {
+        if constexpr (VECP) return w.x;
+        else return w;
+    }
+
+    // Chunk j as fp32 (zeros outside the resource's range).
+    template <int AUX = AUX_DEFAULT> __device__ __forceinline__ void load(rsrc_t r, int j, float* out) const {
+        if constexpr (VECP) unpack<D>(bload16<AUX>(r, (uint32_t)chunk(j) * 16u), out);
+        else out[0] = bload_elem<D, AUX>(r, (uint32_t)chunk(j));
+    }
+    template <int AUX = AUX_DEFAULT> __device__ __forceinline__ void store(rsrc_t r, int j, const float* v) const {
+        if constexpr (VECP) bstore16<AUX>(r, (uint32_t)chunk(j) * 16u, pack<D>(v));
+        else bstore_elem<D, AUX>(r, (uint32_t)chunk(j), v[0]);
     }
 };
 
@@ -99,58 +107,83 @@ add_layernorm_kernel(const typename Elem<D>::T* x, const typename Elem<D>::T* re
     constexpr int V = S::V;
     // Keep gamma/beta loads in flight with x and r when the slice is small; otherwise load
     // them after the statistics so that the register footprint stays bounded.
-    constexpr bool PREFETCH_AFFINE = NV * V <= 32;
+    constexpr bool PREFETCH_AFFINE = NV * V <= 64;
     __shared__ float lds_sum[8], lds_sq[8];
 
     const S s(hidden);
-    const int64_t row = (int64_t)blockIdx.x * RowShape<WPR>::ROWS_PER_BLOCK + (threadIdx.x >> 6) / WPR;
-    const bool active = row < rows;
-    const auto* xr = x + row * hidden;
-    const auto* rr = HAS_RES ? res + row * hidden : nullptr;
-    auto* yr = y + row * hidden;
+    const int64_t row = (int64_t)blockIdx.x * RowShape<WPR>::ROWS_PER_BLOCK +
+                        __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / WPR;
+    const uint32_t row_bytes = row < rows ? (uint32_t)hidden * (uint32_t)sizeof(typename S::T) : 0u;
+    const uint32_t par_bytes = (uint32_t)hidden * (uint32_t)sizeof(typename S::T);
+    const rsrc_t rx = make_rsrc(x + row * hidden, row_bytes);
+    const rsrc_t rr = make_rsrc(HAS_RES ? res + row * hidden : x, HAS_RES ? row_bytes : 0u);
+    const rsrc_t ry = make_rsrc(y + row * hidden, row_bytes);
+    const rsrc_t rg = make_rsrc(gamma, par_bytes);
+    const rsrc_t rb = make_rsrc(beta, par_bytes);
 
-    float v[NV][V], rv[NV][V], g[NV][V], b[NV][V];
+    // All loads of the row are issued here.  gamma and beta stay raw until the normalisation.
+    // Left alone the compiler sinks their loads below the reductions, which adds a cache round
+    // trip to every row's critical path; a zero-valued data dependency of the row sum on one
+    // word of each of them (masked with hidden >> 31, zero for any valid row length but unknown
+    // at compile time) keeps them in flight together with x and r.
+    typename S::Raw wx[NV], wr[NV], wg[NV], wb[NV];
 #pragma unroll
     for (int j = 0; j < NV; j++) {
-        s.load(xr, j, active, v[j]);
-        if constexpr (HAS_RES) s.load(rr, j, active, rv[j]);
+        wx[j] = s.template load_raw<AUX_STREAM>(rx, j);
+        if constexpr (HAS_RES) wr[j] = s.template load_raw<AUX_STREAM>(rr, j);
         if constexpr (PREFETCH_AFFINE) {
-            s.load(gamma, j, active, g[j]);
-            s.load(beta, j, active, b[j]);
+            wg[j] = s.load_raw(rg, j);
+            wb[j] = s.load_raw(rb, j);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);  // issue all of the above before anything below
 
+    float v[NV][V], g[NV][V], b[NV][V];
     float sum = 0.0f;
 #pragma unroll
     for (int j = 0; j < NV; j++) {
+        s.unpack_raw(wx[j], v[j]);
+        if constexpr (HAS_RES) {
+            float rv[V];
+            s.unpack_raw(wr[j], rv);
 #pragma unroll
-        for (int k = 0; k < V; k++) {
-            if constexpr (HAS_RES) v[j][k] += rv[j][k];
-            sum += v[j][k];  // zeros outside the row
+            for (int k = 0; k < V; k++) v[j][k] += rv[k];
         }
+#pragma unroll
+        for (int k = 0; k < V; k++) sum += v[j][k];  // zeros outside the row
+    }
+    if constexpr (PREFETCH_AFFINE) {
+        uint32_t dep = 0;
+#pragma unroll
+        for (int j = 0; j < NV; j++) dep |= S::word0(wg[j]) | S::word0(wb[j]);
+        sum += __builtin_bit_cast(float, dep & (uint32_t)(hidden >> 31));  // adds +0.0f
     }
     sum = row_allreduce<WPR>(sum, SumOp{}, lds_sum);
     const float mean = sum / (float)hidden;
 
+    // branch-free (a select per chunk) so that the kernel stays one basic block and the compiler
+    // cannot sink the gamma/beta loads down to their use
     float sq = 0.0f;
 #pragma unroll
     for (int j = 0; j < NV; j++) {
-        if (s.ok(j)) {
+        const bool in_row = s.ok(j);
 #pragma unroll
-            for (int k = 0; k < V; k++) {
-                const float d = v[j][k] - mean;
-                sq = fmaf(d, d, sq);
-            }
+        for (int k = 0; k < V; k++) {
+            const float d = in_row ? v[j][k] - mean : 0.0f;
+            sq = fmaf(d, d, sq);
         }
     }
     sq = row_allreduce<WPR>(sq, SumOp{}, lds_sq);
     const float rstd = 1.0f / sqrtf(sq / (float)hidden + eps);
 
-    if constexpr (!PREFETCH_AFFINE) {
 #pragma unroll
-        for (int j = 0; j < NV; j++) {
-            s.load(gamma, j, active, g[j]);
-            s.load(beta, j, active, b[j]);
+    for (int j = 0; j < NV; j++) {
+        if constexpr (PREFETCH_AFFINE) {
+            s.unpack_raw(wg[j], g[j]);
+            s.unpack_raw(wb[j], b[j]);
+        } else {
+            s.load(rg, j, g[j]);
+            s.load(rb, j, b[j]);
         }
     }
 #pragma unroll
@@ -158,7 +191,7 @@ add_layernorm_kernel(const typename Elem<D>::T* x, const typename Elem<D>::T* re
         float o[V];
 #pragma unroll
         for (int k = 0; k < V; k++) o[k] = fmaf((v[j][k] - mean) * rstd, g[j][k], b[j][k]);
-        s.store(yr, j, active, o);
+        s.template store<AUX_STREAM>(ry, j, o);
     }
 }
 
@@ -175,22 +208,24 @@ softmax_rows_kernel(const typename Elem<D>::T* x, typename Elem<D>::T* y, int64_
     __shared__ float lds_max[8], lds_sum[8];
 
     const S s(cols);
-    const int64_t row = (int64_t)blockIdx.x * RowShape<WPR>::ROWS_PER_BLOCK + (threadIdx.x >> 6) / WPR;
-    const bool active = row < rows;
-    const auto* xr = x + row * cols;
-    auto* yr = y + row * cols;
+    const int64_t row = (int64_t)blockIdx.x * RowShape<WPR>::ROWS_PER_BLOCK +
+                        __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / WPR;
+    const uint32_t row_bytes = row < rows ? (uint32_t)cols * (uint32_t)sizeof(typename S::T) : 0u;
+    const rsrc_t rx = make_rsrc(x + row * cols, row_bytes);
+    const rsrc_t ry = make_rsrc(y + row * cols, row_bytes);
 
     float z[NV][V];
 #pragma unroll
-    for (int j = 0; j < NV; j++) s.load(xr, j, active, z[j]);
+    for (int j = 0; j < NV; j++) s.template load<AUX_STREAM>(rx, j, z[j]);
 
     float m = -__builtin_inff();
 #pragma unroll
     for (int j = 0; j < NV; j++) {
+        const bool in_row = s.ok(j);
 #pragma unroll
         for (int k = 0; k < V; k++) {
             z[j][k] *= scale;
-            if (s.ok(j)) m = fmaxf(m, z[j][k]);
+            m = fmaxf(m, in_row ? z[j][k] : -__builtin_inff());
         }
     }
     m = row_allreduce<WPR>(m, MaxOp{}, lds_max);
@@ -198,12 +233,11 @@ softmax_rows_kernel(const typename Elem<D>::T* x, typename Elem<D>::T* y, int64_
     float sum = 0.0f;
 #pragma unroll
     for (int j = 0; j < NV; j++) {
-        if (s.ok(j)) {
+        const bool in_row = s.ok(j);
 #pragma unroll
-            for (int k = 0; k < V; k++) {
-                z[j][k] = exp2_fast((z[j][k] - m) * LOG2E);
-                sum += z[j][k];
-            }
+        for (int k = 0; k < V; k++) {
+            z[j][k] = exp2_fast((z[j][k] - m) * LOG2E);
+            sum += in_row ? z[j][k] : 0.0f;
         }
     }
     sum = row_allreduce<WPR>(sum, SumOp{}, lds_sum);
@@ -214,7 +248,7 @@ softmax_rows_kernel(const typename Elem<D>::T* x, typename Elem<D>::T* y, int64_
         float o[V];
 #pragma unroll
         for (int k = 0; k < V; k++) o[k] = z[j][k] * inv;
-        s.store(yr, j, active, o);
+        s.template store<AUX_STREAM>(ry, j, o);
     }
 }
 

@@ -17,18 +17,20 @@ template <int WPR> inline int64_t row_blocks(int64_t rows) {
 
 // Calls f.template operator()<VECP, NV, WPR>() for the compiled plan equal to p; returns false
 // for a plan outside the compiled set.
-//   128-bit path: WPR in {1,2,4,8} x NV in {1,2,4,8,16}
+//   128-bit path: WPR in {1,2,4,8} x NV in {1,2,4,8}, and NV = 16 for WPR in {1,2,4}
 //   per-element path: (WPR,NV) in {(1,1),(1,4),(1,16),(4,16),(8,32)}
 template <class F> bool with_plan(const RowPlan& p, F&& f) {
 #define FUSE_PLAN(VECP, NV, WPR) \
     if (p.vec == VECP && p.nv == NV && p.wpr == WPR) { f.template operator()<VECP, NV, WPR>(); return true; }
 #define FUSE_PLAN_NV(WPR) \
-    FUSE_PLAN(true, 1, WPR) FUSE_PLAN(true, 2, WPR) FUSE_PLAN(true, 4, WPR) \
-    FUSE_PLAN(true, 8, WPR) FUSE_PLAN(true, 16, WPR)
+    FUSE_PLAN(true, 1, WPR) FUSE_PLAN(true, 2, WPR) FUSE_PLAN(true, 4, WPR) FUSE_PLAN(true, 8, WPR)
     FUSE_PLAN_NV(1)
     FUSE_PLAN_NV(2)
     FUSE_PLAN_NV(4)
     FUSE_PLAN_NV(8)
+    FUSE_PLAN(true, 16, 1)
+    FUSE_PLAN(true, 16, 2)
+    FUSE_PLAN(true, 16, 4)
     FUSE_PLAN(false, 1, 1)
     FUSE_PLAN(false, 4, 1)
     FUSE_PLAN(false, 16, 1)
@@ -83,7 +85,8 @@ hipError_t launch_ew(EwOp op, bool vec, const void* a, const void* b, const void
                      int64_t n, int64_t hidden, int chunks_per_thread, hipStream_t stream) {
     using T = typename Elem<D>::T;
     const int V = vec ? Elem<D>::VEC : 1;
-    const uint64_t total = (uint64_t)(n / V), cpr = (uint64_t)(hidden / V);
+    const uint64_t total = (uint64_t)(n / V);
+    const uint32_t cpr = (uint32_t)(hidden / V);
     hipError_t err = hipErrorInvalidValue;
     auto go = [&]<class Op, bool VECP, int CH>() {
         const uint64_t per_block = 256ull * CH;

@@ -3,8 +3,9 @@
 //
 // Element-wise mapping: the tensor is a flat array of chunks (16 bytes on the 128-bit path, one
 // element otherwise); thread t of workgroup b handles chunks b*256*CH + j*256 + t, j < CH, so
-// each wave instruction covers 64 consecutive chunks.  All CH loads are issued before the
-// arithmetic.  A per-column vector (bias) is indexed by chunk modulo chunks-per-row.
+// each wave instruction covers 64 consecutive chunks.  All CH loads (of every operand) are in
+// flight before the arithmetic.  A per-column vector (bias) is indexed by chunk modulo
+// chunks-per-row.
 #pragma once
 
 #include "fuse_common.hpp"
@@ -35,53 +36,53 @@ struct OpSiluMul {  // SiLU(c1) * c2 (second kernel of the unfused SwiGLU)
     __device__ __forceinline__ float operator()(float a, float b, float) const { return silu(a) * b; }
 };
 
-template <DT D, bool VECP, int CH, class Op, class Idx>
-__device__ __forceinline__ void ew_body(const typename Elem<D>::T* a, const typename Elem<D>::T* b,
-                                        const typename Elem<D>::T* c, typename Elem<D>::T* out,
-                                        Idx total, Idx cpr) {
-    constexpr int V = VECP ? Elem<D>::VEC : 1;
-    const Op op;
-    const Idx base = (Idx)blockIdx.x * (Idx)(256 * CH) + (Idx)threadIdx.x;
-    float va[CH][V], vb[CH][V], vc[CH][V];
-#pragma unroll
-    for (int j = 0; j < CH; j++) {
-        const Idx ch = base + (Idx)(j * 256);
-        if (ch < total) {
-            if constexpr (VECP) {
-                unpack<D>(load16(a + ch * V), va[j]);
-                if constexpr (Op::USE_B) unpack<D>(load16(b + ch * V), vb[j]);
-                if constexpr (Op::USE_C) unpack<D>(load16(c + (ch % cpr) * V), vc[j]);
-            } else {
-                va[j][0] = load_scalar<D>(a + ch);
-                if constexpr (Op::USE_B) vb[j][0] = load_scalar<D>(b + ch);
-                if constexpr (Op::USE_C) vc[j][0] = load_scalar<D>(c + ch % cpr);
-            }
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < CH; j++) {
-        const Idx ch = base + (Idx)(j * 256);
-        if (ch < total) {
-            float o[V];
-#pragma unroll
-            for (int k = 0; k < V; k++)
-                o[k] = op(va[j][k], Op::USE_B ? vb[j][k] : 0.0f, Op::USE_C ? vc[j][k] : 0.0f);
-            if constexpr (VECP) store16(out + ch * V, pack<D>(o));
-            else store_scalar<D>(out + ch, o[0]);
-        }
-    }
-}
-
-// 32-bit chunk arithmetic when the tensor has fewer than 2^32 chunks (the modulo for the
-// per-column index is then a 32-bit one), 64-bit otherwise; the branch is uniform.
+// Workgroup b owns chunks [b*256*CH, (b+1)*256*CH) of the flat tensor; its buffer resources
+// start at that chunk and end at the tensor's end, so the tail needs no branches and the 32-bit
+// offsets stay small.  The per-column index is (first chunk mod chunks-per-row) + local chunk,
+// reduced once more modulo chunks-per-row.
 template <DT D, bool VECP, int CH, class Op>
 __global__ void __launch_bounds__(256)
 ew_kernel(const typename Elem<D>::T* a, const typename Elem<D>::T* b, const typename Elem<D>::T* c,
-          typename Elem<D>::T* out, uint64_t total_chunks, uint64_t chunks_per_row) {
-    if (total_chunks < (1ull << 32) - (uint64_t)(256 * CH))
-        ew_body<D, VECP, CH, Op, uint32_t>(a, b, c, out, (uint32_t)total_chunks, (uint32_t)chunks_per_row);
-    else
-        ew_body<D, VECP, CH, Op, uint64_t>(a, b, c, out, total_chunks, chunks_per_row);
+          typename Elem<D>::T* out, uint64_t total_chunks, uint32_t chunks_per_row) {
+    using T = typename Elem<D>::T;
+    constexpr int V = VECP ? Elem<D>::VEC : 1;
+    constexpr uint32_t CB = VECP ? 16u : (uint32_t)sizeof(T);  // bytes per chunk
+    const Op op;
+    const uint64_t first = (uint64_t)blockIdx.x * (256u * CH);
+    const uint64_t left = total_chunks - first;
+    const uint32_t bytes = (uint32_t)(left < 256u * CH ? left : 256u * CH) * CB;
+    const rsrc_t ra = make_rsrc(a + first * V, bytes);
+    const rsrc_t rb = make_rsrc(Op::USE_B ? b + first * V : a, Op::USE_B ? bytes : 0u);
+    const rsrc_t ro = make_rsrc(out + first * V, bytes);
+    const rsrc_t rc = make_rsrc(Op::USE_C ? c : a, Op::USE_C ? chunks_per_row * CB : 0u);
+    const uint32_t col0 = Op::USE_C ? (uint32_t)(first % chunks_per_row) : 0u;
+
+    float va[CH][V], vb[CH][V], vc[CH][V];
+#pragma unroll
+    for (int j = 0; j < CH; j++) {
+        const uint32_t local = (uint32_t)(j * 256) + threadIdx.x;
+        const uint32_t col = Op::USE_C ? (col0 + local) % chunks_per_row : 0u;
+        if constexpr (VECP) {
+            unpack<D>(bload16<AUX_STREAM>(ra, local * 16u), va[j]);
+            if constexpr (Op::USE_B) unpack<D>(bload16<AUX_STREAM>(rb, local * 16u), vb[j]);
+            if constexpr (Op::USE_C) unpack<D>(bload16(rc, col * 16u), vc[j]);
+        } else {
+            va[j][0] = bload_elem<D, AUX_STREAM>(ra, local);
+            if constexpr (Op::USE_B) vb[j][0] = bload_elem<D, AUX_STREAM>(rb, local);
+            if constexpr (Op::USE_C) vc[j][0] = bload_elem<D>(rc, col);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all loads in flight before the arithmetic
+#pragma unroll
+    for (int j = 0; j < CH; j++) {
+        const uint32_t local = (uint32_t)(j * 256) + threadIdx.x;
+        float o[V];
+#pragma unroll
+        for (int k = 0; k < V; k++)
+            o[k] = op(va[j][k], Op::USE_B ? vb[j][k] : 0.0f, Op::USE_C ? vc[j][k] : 0.0f);
+        if constexpr (VECP) bstore16<AUX_STREAM>(ro, local * 16u, pack<D>(o));
+        else bstore_elem<D, AUX_STREAM>(ro, local, o[0]);
+    }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -93,15 +94,15 @@ __global__ void __launch_bounds__(256)
 softmax_rowmax_kernel(const typename Elem<D>::T* x, float* m, int64_t rows, int cols, float scale) {
     constexpr int V = VECP ? Elem<D>::VEC : 1;
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (row >= rows) return;  // whole wave leaves together; no barrier in this kernel
-    const auto* xr = x + row * cols;
+    const rsrc_t rx = make_rsrc(x + row * cols, (uint32_t)cols * (uint32_t)sizeof(typename Elem<D>::T));
     const int nchunk = cols / V;
     float mx = -__builtin_inff();
     for (int c = lane; c < nchunk; c += 64) {
         float v[V];
-        if constexpr (VECP) unpack<D>(load16(xr + (int64_t)c * V), v);
-        else v[0] = load_scalar<D>(xr + c);
+        if constexpr (VECP) unpack<D>(bload16(rx, (uint32_t)c * 16u), v);
+        else v[0] = bload_elem<D>(rx, (uint32_t)c);
 #pragma unroll
         for (int k = 0; k < V; k++) mx = fmaxf(mx, v[k] * scale);
     }
@@ -115,24 +116,25 @@ softmax_expsum_kernel(const typename Elem<D>::T* x, const float* m, typename Ele
                       float* s, int64_t rows, int cols, float scale) {
     constexpr int V = VECP ? Elem<D>::VEC : 1;
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (row >= rows) return;
-    const auto* xr = x + row * cols;
-    auto* er = e + row * cols;
+    const uint32_t row_bytes = (uint32_t)cols * (uint32_t)sizeof(typename Elem<D>::T);
+    const rsrc_t rx = make_rsrc(x + row * cols, row_bytes);
+    const rsrc_t re = make_rsrc(e + row * cols, row_bytes);
     const int nchunk = cols / V;
     const float mx = m[row];
     float sum = 0.0f;
     for (int c = lane; c < nchunk; c += 64) {
         float v[V];
-        if constexpr (VECP) unpack<D>(load16(xr + (int64_t)c * V), v);
-        else v[0] = load_scalar<D>(xr + c);
+        if constexpr (VECP) unpack<D>(bload16(rx, (uint32_t)c * 16u), v);
+        else v[0] = bload_elem<D>(rx, (uint32_t)c);
 #pragma unroll
         for (int k = 0; k < V; k++) {
             v[k] = exp2_fast((v[k] * scale - mx) * LOG2E);
             sum += v[k];
         }
-        if constexpr (VECP) store16(er + (int64_t)c * V, pack<D>(v));
-        else store_scalar<D>(er + c, v[0]);
+        if constexpr (VECP) bstore16(re, (uint32_t)c * 16u, pack<D>(v));
+        else bstore_elem<D>(re, (uint32_t)c, v[0]);
     }
     sum = wave_allreduce(sum, SumOp{});
     if (lane == 0) s[row] = sum;
@@ -144,20 +146,21 @@ softmax_divide_kernel(const typename Elem<D>::T* e, const float* s, typename Ele
                       int64_t rows, int cols) {
     constexpr int V = VECP ? Elem<D>::VEC : 1;
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (row >= rows) return;
-    const auto* er = e + row * cols;
-    auto* yr = y + row * cols;
+    const uint32_t row_bytes = (uint32_t)cols * (uint32_t)sizeof(typename Elem<D>::T);
+    const rsrc_t re = make_rsrc(e + row * cols, row_bytes);
+    const rsrc_t ry = make_rsrc(y + row * cols, row_bytes);
     const int nchunk = cols / V;
     const float inv = 1.0f / s[row];
     for (int c = lane; c < nchunk; c += 64) {
         float v[V];
-        if constexpr (VECP) unpack<D>(load16(er + (int64_t)c * V), v);
-        else v[0] = load_scalar<D>(er + c);
+        if constexpr (VECP) unpack<D>(bload16(re, (uint32_t)c * 16u), v);
+        else v[0] = bload_elem<D>(re, (uint32_t)c);
 #pragma unroll
         for (int k = 0; k < V; k++) v[k] *= inv;
-        if constexpr (VECP) store16(yr + (int64_t)c * V, pack<D>(v));
-        else store_scalar<D>(yr + c, v[0]);
+        if constexpr (VECP) bstore16(ry, (uint32_t)c * 16u, pack<D>(v));
+        else bstore_elem<D>(ry, (uint32_t)c, v[0]);
     }
 }
 

@@ -43,14 +43,14 @@ __device__ __forceinline__ int lds_off(int r, int q) { return r * BK + ((q ^ swz
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
-// 8 bf16 starting at p[0], p[1], ...; elements at index >= avail are zero.  Per-element path for
-// operands whose rows are not 16-byte aligned.
-__device__ __forceinline__ uint4 load8_guarded(const uint16_t* p, int avail) {
+// 8 bf16 at element offset e0 of resource r; elements at index >= avail are zero (per-element
+// path for operands whose rows are not 16-byte aligned).
+__device__ __forceinline__ uint4 load8_guarded(rsrc_t r, uint32_t e0, int avail) {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const uint32_t lo = (2 * i < avail) ? p[2 * i] : 0u;
-        const uint32_t hi = (2 * i + 1 < avail) ? p[2 * i + 1] : 0u;
+        const uint32_t lo = bload_b16(r, 2 * i < avail ? (e0 + 2 * i) * 2u : OOB);
+        const uint32_t hi = bload_b16(r, 2 * i + 1 < avail ? (e0 + 2 * i + 1) * 2u : OOB);
         w[i] = lo | (hi << 16);
     }
     return make_uint4(w[0], w[1], w[2], w[3]);
@@ -87,33 +87,37 @@ __device__ __forceinline__ Tile tile_of(int bid, int tiles_m, int tiles_n) {
     return {(t % tiles_m) * BM, (t / tiles_m) * BN};
 }
 
+// Global -> registers for one K step.  The a resource spans the tile's valid rows and the b
+// resource the step's valid k rows, so rows past M or K read as zeros; columns past K (a) or N (b)
+// are sent to an offset outside the resource.  All loads are unconditional.
 template <bool ALIGNED>
 __device__ __forceinline__ void load_stage(const uint16_t* a, const uint16_t* b1, const uint16_t* b2,
                                            int M, int N, int K, int m0, int n0, int k0,
                                            uint4 (&ra)[4], uint4 (&rb)[8]) {
     const int t = threadIdx.x;
-    // a: 128 rows x 8 chunks; thread t takes chunk t&7 of rows t>>3 + 32 i
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     {
-        const int q = t & 7, k = k0 + 8 * q;
+        const int mrows = min(M - m0, BM);
+        const rsrc_t r = make_rsrc(a + (int64_t)m0 * K, (uint32_t)mrows * (uint32_t)K * 2u);
+        const int k = k0 + 8 * (t & 7);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const int m = m0 + (t >> 3) + 32 * i;
-            const uint16_t* p = a + (int64_t)m * K + k;
-            if (ALIGNED) ra[i] = (m < M && k < K) ? *reinterpret_cast<const uint4*>(p) : zero4();
-            else ra[i] = (m < M && k < K) ? load8_guarded(p, K - k) : zero4();
+            const uint32_t e0 = (uint32_t)((t >> 3) + 32 * i) * (uint32_t)K + (uint32_t)k;
+            if (ALIGNED) ra[i] = bload16(r, k < K ? e0 * 2u : OOB);
+            else ra[i] = load8_guarded(r, e0, K - k);
         }
     }
-    // b1 (threads 0..127) or b2 (128..255): the 8 x 8 block (kb, nb), kb = bt>>4, nb = bt&15
     {
+        // waves 0-1 load b1, waves 2-3 load b2: the 8 x 8 block (kb, nb), kb = bt>>4, nb = bt&15
+        const int krows = min(K - k0, BK);
+        const rsrc_t r = make_rsrc((wave < 2 ? b1 : b2) + (int64_t)k0 * N, (uint32_t)krows * (uint32_t)N * 2u);
         const int bt = t & 127;
-        const uint16_t* b = t < 128 ? b1 : b2;
-        const int n = n0 + 8 * (bt & 15), kbase = k0 + 8 * (bt >> 4);
+        const int n = n0 + 8 * (bt & 15), kb = 8 * (bt >> 4);
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            const int k = kbase + i;
-            const uint16_t* p = b + (int64_t)k * N + n;
-            if (ALIGNED) rb[i] = (k < K && n < N) ? *reinterpret_cast<const uint4*>(p) : zero4();
-            else rb[i] = (k < K && n < N) ? load8_guarded(p, N - n) : zero4();
+            const uint32_t e0 = (uint32_t)(kb + i) * (uint32_t)N + (uint32_t)n;
+            if (ALIGNED) rb[i] = bload16(r, n < N ? e0 * 2u : OOB);
+            else rb[i] = load8_guarded(r, e0, N - n);
         }
     }
 }
@@ -131,7 +135,7 @@ __device__ __forceinline__ void store_stage(uint16_t* lds_a, uint16_t* lds_b1, u
     }
     {
         const int bt = t & 127;
-        uint16_t* lb = t < 128 ? lds_b1 : lds_b2;
+        uint16_t* lb = __builtin_amdgcn_readfirstlane(t >> 6) < 2 ? lds_b1 : lds_b2;
         const int nb = bt & 15, kb = bt >> 4;
         uint4 o[8];
         transpose8x8(rb, o);
