@@ -119,8 +119,7 @@ fuse_status_t fuse_softmax_rows(const void *x, void *y, int64_t rows, int64_t co
  *
  *   a : [M, K];  b1, b2 : [K, N];  out : [M, N], must not overlap a, b1 or b2.
  *   dtype : FUSE_BF16 (bf16 inputs and output, fp32 accumulation).
- * M >= 0, N >= 1, K >= 1, each below 2^31; K above 2^22 or N above 2^23 is
- * FUSE_ERR_UNSUPPORTED.
+ * M >= 0, N >= 1, K >= 1, each below 2^31; K or N above 2^21 is FUSE_ERR_UNSUPPORTED.
  */
 fuse_status_t fuse_swiglu_dualgemm(const void *a, const void *b1, const void *b2, void *out,
                                    int64_t M, int64_t N, int64_t K, fuse_dtype_t dtype,

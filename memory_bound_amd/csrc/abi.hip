@@ -261,8 +261,8 @@ static fuse_status_t check_swiglu(const void* a, const void* b1, const void* b2,
     if (M < 0 || N < 1 || K < 1) return FUSE_ERR_BAD_SHAPE;
     const int64_t lim = INT64_C(0x7fffffff);
     if (M > lim || N > lim || K > lim) return FUSE_ERR_BAD_SHAPE;
-    // 32-bit offsets inside one 128-row tile of a and one 64-row step of b
-    if (K > (INT64_C(1) << 22) || N > (INT64_C(1) << 23)) return FUSE_ERR_UNSUPPORTED;
+    // 32-bit offsets inside one 256-row tile of a or out and one 64-row step of b
+    if (K > (INT64_C(1) << 21) || N > (INT64_C(1) << 21)) return FUSE_ERR_UNSUPPORTED;
     size_t ab, bb, ob;
     if (!tensor_bytes(M, K, 2, &ab) || !tensor_bytes(K, N, 2, &bb) || !tensor_bytes(M, N, 2, &ob))
         return FUSE_ERR_BAD_SHAPE;

@@ -1,30 +1,32 @@
 // swiglu.hip -- fused SwiGLU dual GEMM on the gfx950 matrix cores:
 //   out[M,N] = SiLU(a[M,K] . b1[K,N]) * (a[M,K] . b2[K,N]), bf16 in and out, fp32 accumulation.
 //
-// Tiling.  A 256-thread workgroup (4 waves, 2 x 2) owns a 128 x 128 tile of out and keeps two
-// fp32 accumulator sets, one per product: each wave holds 2 x 2 blocks of 32 x 32 for C1 and the
-// same for C2 (v_mfma_f32_32x32x16_bf16, 16 fp32 per lane per block, 128 accumulators per lane).
-// Per K step of 64 the workgroup stages one tile of a (128 x 64) and the matching tiles of b1 and
-// b2 (64 x 128 each) in LDS; every A fragment read from LDS feeds one MFMA against b1 and one
-// against b2, so the a tile is loaded from memory once for both products.
+// Tiling.  A 256-thread workgroup (4 waves, 2 x 2) owns a 256 x 128 tile of out and keeps two
+// fp32 accumulator sets, one per product: each wave holds 4 x 2 blocks of 32 x 32 for C1 and the
+// same for C2 (v_mfma_f32_32x32x16_bf16, 16 fp32 per lane per block, 256 accumulators per lane,
+// held in AGPRs).  Per 16-deep k slice a wave reads 8 fragments from LDS (4 of a, 2 of b1, 2 of
+// b2) for 16 MFMAs: every a fragment feeds one MFMA against b1 and one against b2, so the a tile
+// is loaded from memory once for both products.
 //
 // Layouts.  The matrix cores want both operands with 8 consecutive k values per lane.  a is
 // row-major [M,K] (k contiguous) and is copied to LDS as is.  b1 and b2 are row-major [K,N]
 // (n contiguous); each thread loads an 8 (k) x 8 (n) block with eight 128-bit loads, transposes
 // it in registers and writes eight 128-bit rows of the k-contiguous LDS tile Bt[n][k].  LDS rows
 // are 64 bf16 (eight 16-byte chunks); chunk q of row r lives at chunk q ^ ((r ^ r>>3) & 7), which
-// keeps the fragment reads (8 consecutive rows per 8 lanes) and the transposed writes (rows 8
-// apart) free of bank conflicts.
+// keeps the fragment reads (16 consecutive rows per 16 lanes, 64 banks) and the transposed writes
+// (rows 8 apart) free of bank conflicts.
 //
-// Pipeline.  LDS holds two stages (96 KiB).  While the MFMAs consume stage s, the registers
-// loaded during the previous step are written to the other LDS stage and the global loads of
-// step s + 2 are issued, so each K step needs one barrier and memory latency hides behind the
-// matrix work.  One workgroup per CU (4 waves, one per SIMD) gets up to 512 registers per lane,
-// enough for both accumulator sets without spilling.
+// Pipeline (general kernel).  LDS holds two stages of 64 KiB.  While the MFMAs consume one stage, the registers
+// loaded during the previous step are written to the other stage and the global loads of the
+// step after are issued; fragments are double-buffered in registers so the LDS reads of the next
+// k slice are in flight during the current slice's MFMAs.  One barrier per K step of 64; one
+// workgroup per CU (one wave per SIMD, up to 512 registers per lane).
 //
 // Scheduling.  Workgroups are dispatched round-robin over the 8 XCDs; the tile index is remapped
 // so that each XCD owns a contiguous range of tiles, walked with M fastest, so that workgroups
 // resident on one XCD share their b1/b2 column tiles in that XCD's L2.
+#include <stdlib.h>
+
 #include "launch.hpp"
 #include "stream_kernels.hpp"
 
@@ -34,7 +36,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 64, THREADS = 256;
+constexpr int BM = 256, BN = 128, BK = 64, THREADS = 256;
+constexpr int WM = 4, WN = 2;  // 32 x 32 blocks per wave along M and N (wave tile 128 x 64)
 constexpr int NUM_XCD = 8;
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
@@ -93,7 +96,7 @@ __device__ __forceinline__ Tile tile_of(int bid, int tiles_m, int tiles_n) {
 template <bool ALIGNED>
 __device__ __forceinline__ void load_stage(const uint16_t* a, const uint16_t* b1, const uint16_t* b2,
                                            int M, int N, int K, int m0, int n0, int k0,
-                                           uint4 (&ra)[4], uint4 (&rb)[8]) {
+                                           uint4 (&ra)[8], uint4 (&rb)[8]) {
     const int t = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     {
@@ -101,7 +104,7 @@ __device__ __forceinline__ void load_stage(const uint16_t* a, const uint16_t* b1
         const rsrc_t r = make_rsrc(a + (int64_t)m0 * K, (uint32_t)mrows * (uint32_t)K * 2u);
         const int k = k0 + 8 * (t & 7);
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < 8; i++) {
             const uint32_t e0 = (uint32_t)((t >> 3) + 32 * i) * (uint32_t)K + (uint32_t)k;
             if (ALIGNED) ra[i] = bload16(r, k < K ? e0 * 2u : OOB);
             else ra[i] = load8_guarded(r, e0, K - k);
@@ -123,12 +126,12 @@ __device__ __forceinline__ void load_stage(const uint16_t* a, const uint16_t* b1
 }
 
 __device__ __forceinline__ void store_stage(uint16_t* lds_a, uint16_t* lds_b1, uint16_t* lds_b2,
-                                            const uint4 (&ra)[4], const uint4 (&rb)[8]) {
+                                            const uint4 (&ra)[8], const uint4 (&rb)[8]) {
     const int t = threadIdx.x;
     {
         const int q = t & 7;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < 8; i++) {
             const int r = (t >> 3) + 32 * i;
             *reinterpret_cast<uint4*>(lds_a + lds_off(r, q)) = ra[i];
         }
@@ -144,86 +147,368 @@ __device__ __forceinline__ void store_stage(uint16_t* lds_a, uint16_t* lds_b1, u
     }
 }
 
+struct Frags {
+    bf16x8 a[WM], b1[WN], b2[WN];
+};
+
+// Fragments of k slice kk (16 deep) of one LDS stage for this wave.
+__device__ __forceinline__ void read_frags(const uint16_t* la, const uint16_t* lb1, const uint16_t* lb2,
+                                           int wm, int wn, int lane, int kk, Frags& f) {
+    const int q = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < WM; i++)
+        f.a[i] = *reinterpret_cast<const bf16x8*>(la + lds_off(128 * wm + 32 * i + (lane & 31), q));
+#pragma unroll
+    for (int j = 0; j < WN; j++) {
+        f.b1[j] = *reinterpret_cast<const bf16x8*>(lb1 + lds_off(64 * wn + 32 * j + (lane & 31), q));
+        f.b2[j] = *reinterpret_cast<const bf16x8*>(lb2 + lds_off(64 * wn + 32 * j + (lane & 31), q));
+    }
+}
+
+__device__ __forceinline__ void mfma_slice(const Frags& f, floatx16 (&acc1)[WM][WN], floatx16 (&acc2)[WM][WN]) {
+#pragma unroll
+    for (int i = 0; i < WM; i++)
+#pragma unroll
+        for (int j = 0; j < WN; j++) {
+            acc1[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b1[j], acc1[i][j], 0, 0, 0);
+            acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b2[j], acc2[i][j], 0, 0, 0);
+        }
+}
+
 template <bool ALIGNED, bool STORE_PRODUCTS>
 __global__ void __launch_bounds__(THREADS, 1)
 swiglu_kernel(const uint16_t* a, const uint16_t* b1, const uint16_t* b2, uint16_t* out,
               uint16_t* c1_out, uint16_t* c2_out, int M, int N, int K, int tiles_m, int tiles_n) {
-    constexpr int STAGE = (BM + 2 * BN) * BK;  // bf16 elements per LDS stage
+    constexpr int STAGE = (BM + 2 * BN) * BK;  // bf16 elements per LDS stage (64 KiB)
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
 
     const Tile tile = tile_of(blockIdx.x, tiles_m, tiles_n);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
-    floatx16 acc1[2][2], acc2[2][2];
+    floatx16 acc1[WM][WN], acc2[WM][WN];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < WM; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < WN; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc1[i][j][r] = acc2[i][j][r] = 0.0f;
 
     const int kt_n = (K + BK - 1) / BK;
-    uint4 ra[4], rb[8];
+    uint4 ra[8], rb[8];
     load_stage<ALIGNED>(a, b1, b2, M, N, K, tile.m0, tile.n0, 0, ra, rb);
     store_stage(lds, lds + BM * BK, lds + (BM + BN) * BK, ra, rb);
     if (kt_n > 1) load_stage<ALIGNED>(a, b1, b2, M, N, K, tile.m0, tile.n0, BK, ra, rb);
     __syncthreads();
 
+    Frags f[2];
+    read_frags(lds, lds + BM * BK, lds + (BM + BN) * BK, wm, wn, lane, 0, f[0]);
     for (int kt = 0; kt < kt_n; kt++) {
         const uint16_t* la = lds + (kt & 1) * STAGE;
         const uint16_t* lb1 = la + BM * BK;
         const uint16_t* lb2 = lb1 + BN * BK;
 #pragma unroll
         for (int kk = 0; kk < BK / 16; kk++) {
-            const int q = 2 * kk + (lane >> 5);
-            bf16x8 fa[2], fb1[2], fb2[2];
-#pragma unroll
-            for (int i = 0; i < 2; i++) {
-                fa[i] = *reinterpret_cast<const bf16x8*>(la + lds_off(64 * wm + 32 * i + (lane & 31), q));
-                fb1[i] = *reinterpret_cast<const bf16x8*>(lb1 + lds_off(64 * wn + 32 * i + (lane & 31), q));
-                fb2[i] = *reinterpret_cast<const bf16x8*>(lb2 + lds_off(64 * wn + 32 * i + (lane & 31), q));
+            // LDS reads of the next slice overlap this slice's MFMAs
+            if (kk + 1 < BK / 16) read_frags(la, lb1, lb2, wm, wn, lane, kk + 1, f[(kk + 1) & 1]);
+            mfma_slice(f[kk & 1], acc1, acc2);
+            if (kk == 1 && kt + 1 < kt_n) {
+                // stage kt+1 goes to the other buffer: nobody reads it until after the barrier
+                // below, and its previous contents (stage kt-1) were consumed before the last one
+                uint16_t* na = lds + ((kt + 1) & 1) * STAGE;
+                store_stage(na, na + BM * BK, na + (BM + BN) * BK, ra, rb);
+                if (kt + 2 < kt_n)
+                    load_stage<ALIGNED>(a, b1, b2, M, N, K, tile.m0, tile.n0, (kt + 2) * BK, ra, rb);
             }
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    acc1[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb1[j], acc1[i][j], 0, 0, 0);
-                    acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb2[j], acc2[i][j], 0, 0, 0);
-                }
-        }
-        if (kt + 1 < kt_n) {
-            // stage kt+1 goes to the other buffer: nobody reads it until after the barrier below,
-            // and its previous contents (stage kt-1) were consumed before the last barrier
-            uint16_t* na = lds + ((kt + 1) & 1) * STAGE;
-            store_stage(na, na + BM * BK, na + (BM + BN) * BK, ra, rb);
-            if (kt + 2 < kt_n)
-                load_stage<ALIGNED>(a, b1, b2, M, N, K, tile.m0, tile.n0, (kt + 2) * BK, ra, rb);
         }
         __syncthreads();
+        if (kt + 1 < kt_n) {
+            const uint16_t* na = lds + ((kt + 1) & 1) * STAGE;
+            read_frags(na, na + BM * BK, na + (BM + BN) * BK, wm, wn, lane, 0, f[0]);
+        }
     }
 
-    // Epilogue.  Block (i, j) element r of lane l sits at row 8 (r/4) + 4 (l/32) + r%4, column l%32.
+    // Epilogue.  Block (i, j) element r of lane l sits at row 8 (r/4) + 4 (l/32) + r%4, column l%32
+    // of the block.  Stores go through a resource spanning the tile's valid rows; columns past N
+    // are sent out of range, so there is no branch per element.
+    const int mrows = min(M - tile.m0, BM);
+    const uint32_t out_bytes = (uint32_t)mrows * (uint32_t)N * 2u;
+    const rsrc_t ro = make_rsrc(STORE_PRODUCTS ? c1_out + (int64_t)tile.m0 * N : out + (int64_t)tile.m0 * N, out_bytes);
+    const rsrc_t ro2 = make_rsrc(STORE_PRODUCTS ? c2_out + (int64_t)tile.m0 * N : out, STORE_PRODUCTS ? out_bytes : 0u);
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < WM; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
+        for (int j = 0; j < WN; j++) {
             const int col = tile.n0 + 64 * wn + 32 * j + (lane & 31);
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int row = tile.m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (row < M && col < N) {
-                    const int64_t o = (int64_t)row * N + col;
-                    const float c1 = acc1[i][j][r], c2 = acc2[i][j][r];
-                    if constexpr (STORE_PRODUCTS) {
-                        c1_out[o] = __builtin_bit_cast(uint16_t, (__bf16)c1);
-                        c2_out[o] = __builtin_bit_cast(uint16_t, (__bf16)c2);
-                    } else {
-                        out[o] = __builtin_bit_cast(uint16_t, (__bf16)(silu(c1) * c2));
-                    }
+                const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const uint32_t off = col < N ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u : OOB;
+                const float c1 = acc1[i][j][r], c2 = acc2[i][j][r];
+                if constexpr (STORE_PRODUCTS) {
+                    bstore_b16<AUX_STREAM>(ro, off, f32_to_bf16(c1));
+                    bstore_b16<AUX_STREAM>(ro2, off, f32_to_bf16(c2));
+                } else {
+                    bstore_b16<AUX_STREAM>(ro, off, f32_to_bf16(silu(c1) * c2));
                 }
             }
         }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Full-tile kernel (M % 256 == 0, N % 128 == 0, K % BK == 0, 16-byte aligned operands): operands go
+// from memory straight into LDS with global_load_lds_dwordx4 (no VGPR staging, no LDS store
+// instructions), through a ring of S stages, and b1/b2 are transposed at fragment-read time with
+// ds_read_b64_tr_b16.
+//
+// ds_read_b64_tr_b16, per group of 16 lanes: if lane j reads the four 16-bit values D[j][0..3], lane
+// i receives D[i/4][i%4], D[4+i/4][i%4], D[8+i/4][i%4], D[12+i/4][i%4].  With lane j reading
+// n = nb + 4 (j%4) .. +3 of row k = kb + j/4 of an n-contiguous tile, lane i receives
+// B[kb..kb+3][nb+i]: four consecutive k of one column, the matrix-core B operand layout.
+//
+// LDS layouts.  gfx950's LDS has 64 four-byte banks (256 bytes per cycle); a ds_read_b128 is
+// served 16 lanes at a time and a ds_read_b64 32 lanes at a time.  XOR swizzles on 16-byte chunks
+// keep both free of bank conflicts (the asynchronous writes fill 1 KiB per wave instruction in
+// lane order and never conflict):
+//   a tile  [256][BK]: chunk q of row r at q ^ ((r >> 2) & 3) (BK = 32, four 64-byte rows per
+//                      256 bytes) or q ^ ((r ^ r >> 3) & 7) (BK = 64, two 128-byte rows)
+//   b tiles [BK][128]: chunk q of row k at q ^ 4 (k & 3): the 64 bytes the two 16-lane groups of
+//                      a transposed read take from each of four consecutive rows land in four
+//                      different 64-byte quarters of the bank space
+// ------------------------------------------------------------------------------------------------
+
+template <int BK_> struct DirectCfg {
+    static constexpr int BKD = BK_;
+    static constexpr int A_ROW_BYTES = BK_ * 2;             // 64 or 128
+    static constexpr int A_CHUNKS = A_ROW_BYTES / 16;       // 4 or 8 per row
+    static constexpr int A_BYTES = BM * A_ROW_BYTES;        // 16 or 32 KiB
+    static constexpr int B_BYTES = BK_ * BN * 2;            // 8 or 16 KiB per matrix
+    static constexpr int STAGE_BYTES = A_BYTES + 2 * B_BYTES;
+    // asynchronous load instructions per wave per stage: a rows, then b1 and b2 rows
+    static constexpr int LOADS_PER_STAGE = 64 / (1024 / A_ROW_BYTES) + 2 * (BK_ / 16);
+    __device__ static int a_phys(int r, int q) {
+        if constexpr (BK_ == 32) return q ^ ((r >> 2) & 3);
+        else return q ^ ((r ^ (r >> 3)) & 7);
+    }
+};
+
+__device__ __forceinline__ int b_phys(int k, int q) { return q ^ (4 * (k & 3)); }
+
+// s_waitcnt with vmcnt = N and no wait on the other counters (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+// Asynchronous 16-byte-per-lane load from global memory straight into LDS: lane L's 16 bytes land
+// at lds + 16 L (M0 holds the wave's LDS base; one wait state between the M0 write and its use).
+// Issued as inline assembly so that the compiler adds no waits of its own around it: the caller
+// orders it with an explicit s_waitcnt vmcnt and a barrier before the data is read.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+
+// Issue the asynchronous loads of K step k0 into LDS stage `st`.  Wave w fills A rows
+// [64 w, 64 w + 64) and b rows [BK/4 w, BK/4 w + BK/4) of both b1 and b2.
+template <int BK_>
+__device__ __forceinline__ void direct_loads(const uint16_t* a, const uint16_t* b1, const uint16_t* b2,
+                                             int N, int K, int m0, int n0, int k0, char* st, int wave, int lane) {
+    using C = DirectCfg<BK_>;
+    constexpr int ROWS_PER_INSTR_A = 1024 / C::A_ROW_BYTES;  // 16 or 8
+    const uint32_t base = lds_addr(st);
+#pragma unroll
+    for (int i = 0; i < 64 / ROWS_PER_INSTR_A; i++) {
+        const int r0 = 64 * wave + ROWS_PER_INSTR_A * i;
+        const int r = r0 + lane / C::A_CHUNKS, p = lane % C::A_CHUNKS;
+        const int q = C::a_phys(r, p);  // the swizzle is its own inverse
+        dma16(a + (int64_t)(m0 + r) * K + k0 + 8 * q, base + r0 * C::A_ROW_BYTES);
+    }
+    constexpr int KR = C::BKD / 4;  // b rows per wave
+#pragma unroll
+    for (int i = 0; i < KR / 4; i++) {
+        const int k0r = KR * wave + 4 * i;
+        const int kr = k0r + lane / 16, p = lane % 16;
+        const int q = b_phys(kr, p);
+        const int64_t off = (int64_t)(k0 + kr) * N + n0 + 8 * q;
+        dma16(b1 + off, base + C::A_BYTES + k0r * 256);
+        dma16(b2 + off, base + C::A_BYTES + C::B_BYTES + k0r * 256);
+    }
+}
+
+// Load slot `slot` (0 .. LOADS_PER_STAGE-1) of direct_loads: slots 0 .. NA-1 are rows of a, the
+// rest alternate b1 / b2 rows.  Called with compile-time slot numbers from unrolled loops, so the
+// branches fold away.
+template <int BK_>
+__device__ __forceinline__ void dma_slot(int slot, const uint16_t* a, const uint16_t* b1, const uint16_t* b2,
+                                         int N, int K, int m0, int n0, int k0, uint32_t base, int wave, int lane) {
+    using C = DirectCfg<BK_>;
+    constexpr int ROWS_PER_INSTR_A = 1024 / C::A_ROW_BYTES;
+    constexpr int NA = 64 / ROWS_PER_INSTR_A;
+    if (slot < NA) {
+        const int r0 = 64 * wave + ROWS_PER_INSTR_A * slot;
+        const int r = r0 + lane / C::A_CHUNKS, p = lane % C::A_CHUNKS;
+        dma16(a + (int64_t)(m0 + r) * K + k0 + 8 * C::a_phys(r, p), base + r0 * C::A_ROW_BYTES);
+    } else {
+        const int j = slot - NA, i = j >> 1, mat = j & 1;
+        const int k0r = (C::BKD / 4) * wave + 4 * i;
+        const int kr = k0r + lane / 16, p = lane % 16;
+        const int64_t off = (int64_t)(k0 + kr) * N + n0 + 8 * b_phys(kr, p);
+        dma16((mat == 0 ? b1 : b2) + off, base + C::A_BYTES + mat * C::B_BYTES + k0r * 256);
+    }
+}
+
+// The 16 MFMAs of one k slice in WM groups (one row block each); after each group, PER of the
+// next stage's load slots starting at slot0 are issued when `issue` is set.
+template <int BK_>
+__device__ __forceinline__ void mfma_slice_dma(const Frags& f, floatx16 (&acc1)[WM][WN], floatx16 (&acc2)[WM][WN],
+                                               int slot0, bool issue, const uint16_t* a, const uint16_t* b1,
+                                               const uint16_t* b2, int N, int K, int m0, int n0, int k0,
+                                               uint32_t base, int wave, int lane) {
+    constexpr int LPS = DirectCfg<BK_>::LOADS_PER_STAGE;
+    constexpr int PER = LPS / (BK_ / 16) / WM;
+    static_assert(PER * WM * (BK_ / 16) == LPS, "load slots must spread evenly over the MFMA groups");
+#pragma unroll
+    for (int i = 0; i < WM; i++) {
+#pragma unroll
+        for (int j = 0; j < WN; j++) {
+            acc1[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b1[j], acc1[i][j], 0, 0, 0);
+            acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b2[j], acc2[i][j], 0, 0, 0);
+        }
+        if (issue) {
+#pragma unroll
+            for (int p = 0; p < PER; p++) dma_slot<BK_>(slot0 + i * PER + p, a, b1, b2, N, K, m0, n0, k0, base, wave, lane);
+        }
+    }
+}
+
+// B fragment (32 columns starting at nb, k = kb .. kb + 15) for this lane, via two transposed reads.
+__device__ __forceinline__ bf16x8 b_frag_tr(const char* bt, int nb, int kb, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const int n = nb + 16 * (g & 1) + 4 * (j & 3);
+    const int q = n >> 3, half = (n >> 2) & 1;
+    v4i16 h[2];
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+        const int k = kb + 8 * (g >> 1) + 4 * t + (j >> 2);
+        const char* p = bt + k * 256 + b_phys(k, q) * 16 + half * 8;
+        h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(__attribute__((address_space(3))) const char*)p);
+    }
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int BK_>
+__device__ __forceinline__ void read_frags_direct(const char* st, int wm, int wn, int lane, int kk, Frags& f) {
+    using C = DirectCfg<BK_>;
+    const int qa = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < WM; i++) {
+        const int r = 128 * wm + 32 * i + (lane & 31);
+        f.a[i] = *reinterpret_cast<const bf16x8*>(st + r * C::A_ROW_BYTES + C::a_phys(r, qa) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < WN; j++) {
+        f.b1[j] = b_frag_tr(st + C::A_BYTES, 64 * wn + 32 * j, 16 * kk, lane);
+        f.b2[j] = b_frag_tr(st + C::A_BYTES + C::B_BYTES, 64 * wn + 32 * j, 16 * kk, lane);
+    }
+}
+
+template <int BK_, int S, bool STORE_PRODUCTS>
+__global__ void __launch_bounds__(THREADS, 1)
+swiglu_direct_kernel(const uint16_t* a, const uint16_t* b1, const uint16_t* b2, uint16_t* out,
+                     uint16_t* c1_out, uint16_t* c2_out, int M, int N, int K, int tiles_m, int tiles_n) {
+    using C = DirectCfg<BK_>;
+    constexpr int SLICES = BK_ / 16;
+    __shared__ __attribute__((aligned(1024))) char lds[S * C::STAGE_BYTES];
+
+    const Tile tile = tile_of(blockIdx.x, tiles_m, tiles_n);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    floatx16 acc1[WM][WN], acc2[WM][WN];
+#pragma unroll
+    for (int i = 0; i < WM; i++)
+#pragma unroll
+        for (int j = 0; j < WN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc1[i][j][r] = acc2[i][j][r] = 0.0f;
+
+    const int kt_n = K / BK_;
+    // prologue: stages 0 .. S-2 in flight
+#pragma unroll
+    for (int s = 0; s < S - 1; s++)
+        if (s < kt_n) direct_loads<BK_>(a, b1, b2, N, K, tile.m0, tile.n0, s * BK_, lds + s * C::STAGE_BYTES, wave, lane);
+
+    for (int kt = 0; kt < kt_n; kt++) {
+        // This wave's loads of stage kt are done once no more than the loads of the stages issued
+        // after it (kt+1 .. kt+S-2) are pending.  After the barrier every wave's stage kt is in
+        // LDS and every wave has finished reading stage kt-1, whose buffer the loads of stage
+        // kt+S-1 then overwrite while stage kt is multiplied.
+        if (kt + S - 2 < kt_n) wait_vmcnt<C::LOADS_PER_STAGE * (S - 2)>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        // the loads of stage kt+S-1 are issued a few at a time between this step's MFMAs, so the
+        // address unit's queue never holds a wave's instruction issue for long
+        const bool issue = kt + S - 1 < kt_n;
+        const uint32_t nbase = lds_addr(lds + ((kt + S - 1) % S) * C::STAGE_BYTES);
+        const int nk0 = (kt + S - 1) * BK_;
+        const char* st = lds + (kt % S) * C::STAGE_BYTES;
+        Frags f[2];
+        read_frags_direct<BK_>(st, wm, wn, lane, 0, f[0]);
+#pragma unroll
+        for (int kk = 0; kk < SLICES; kk++) {
+            if (kk + 1 < SLICES) read_frags_direct<BK_>(st, wm, wn, lane, kk + 1, f[(kk + 1) & 1]);
+            mfma_slice_dma<BK_>(f[kk & 1], acc1, acc2, kk * (C::LOADS_PER_STAGE / SLICES), issue, a, b1, b2, N, K,
+                                tile.m0, tile.n0, nk0, nbase, wave, lane);
+        }
+    }
+
+    const uint32_t out_bytes = (uint32_t)BM * (uint32_t)N * 2u;
+    const rsrc_t ro = make_rsrc(STORE_PRODUCTS ? c1_out + (int64_t)tile.m0 * N : out + (int64_t)tile.m0 * N, out_bytes);
+    const rsrc_t ro2 = make_rsrc(STORE_PRODUCTS ? c2_out + (int64_t)tile.m0 * N : out, STORE_PRODUCTS ? out_bytes : 0u);
+#pragma unroll
+    for (int i = 0; i < WM; i++)
+#pragma unroll
+        for (int j = 0; j < WN; j++) {
+            const int col = tile.n0 + 64 * wn + 32 * j + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const uint32_t off = ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u;
+                const float c1 = acc1[i][j][r], c2 = acc2[i][j][r];
+                if constexpr (STORE_PRODUCTS) {
+                    bstore_b16<AUX_STREAM>(ro, off, f32_to_bf16(c1));
+                    bstore_b16<AUX_STREAM>(ro2, off, f32_to_bf16(c2));
+                } else {
+                    bstore_b16<AUX_STREAM>(ro, off, f32_to_bf16(silu(c1) * c2));
+                }
+            }
+        }
+}
+
+// K step and ring depth of the full-tile kernel: FUSE_SWIGLU_BK / FUSE_SWIGLU_STAGES override the
+// default (BK 32, 4 stages) for tuning sweeps; every allowed pair fits the 160 KiB of LDS.
+struct DirectPlan {
+    int bk, stages;
+};
+DirectPlan direct_plan() {
+    const char* b = getenv("FUSE_SWIGLU_BK");
+    const char* s = getenv("FUSE_SWIGLU_STAGES");
+    const int bk = (b && atoi(b) == 64) ? 64 : 32;
+    int st = s ? atoi(s) : 4;
+    if (bk == 64) st = 2;
+    else if (st < 2 || st > 4) st = 4;
+    return {bk, st};
 }
 
 template <bool STORE_PRODUCTS>
@@ -232,6 +517,19 @@ hipError_t launch(const void* a, const void* b1, const void* b2, void* out, void
     const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
     const bool aligned = (K % 8 == 0) && (N % 8 == 0) && (((uintptr_t)a | (uintptr_t)b1 | (uintptr_t)b2) & 15u) == 0;
     const dim3 grid((unsigned)(tm * tn)), block(THREADS);
+    const DirectPlan dp = direct_plan();
+    if (aligned && M % BM == 0 && N % BN == 0 && K % dp.bk == 0 && getenv("FUSE_SWIGLU_GENERAL") == nullptr) {
+#define FUSE_DIRECT(BKV, SV)                                                                          \
+    hipLaunchKernelGGL((swiglu_direct_kernel<BKV, SV, STORE_PRODUCTS>), grid, block, 0, stream,          \
+                       (const uint16_t*)a, (const uint16_t*)b1, (const uint16_t*)b2, (uint16_t*)out,     \
+                       (uint16_t*)c1, (uint16_t*)c2, M, N, K, tm, tn)
+        if (dp.bk == 64) FUSE_DIRECT(64, 2);
+        else if (dp.stages == 2) FUSE_DIRECT(32, 2);
+        else if (dp.stages == 3) FUSE_DIRECT(32, 3);
+        else FUSE_DIRECT(32, 4);
+#undef FUSE_DIRECT
+        return hipGetLastError();
+    }
     if (aligned)
         hipLaunchKernelGGL((swiglu_kernel<true, STORE_PRODUCTS>), grid, block, 0, stream, (const uint16_t*)a,
                            (const uint16_t*)b1, (const uint16_t*)b2, (uint16_t*)out, (uint16_t*)c1,
