@@ -369,14 +369,15 @@ __device__ __forceinline__ void dma_slot(int slot, const uint16_t* a, const uint
 
 // The 16 MFMAs of one k slice in WM groups (one row block each); after each group, PER of the
 // next stage's load slots starting at slot0 are issued when `issue` is set.
-template <int BK_>
+template <int BK_, bool MID = false>
 __device__ __forceinline__ void mfma_slice_dma(const Frags& f, floatx16 (&acc1)[WM][WN], floatx16 (&acc2)[WM][WN],
                                                int slot0, bool issue, const uint16_t* a, const uint16_t* b1,
                                                const uint16_t* b2, int N, int K, int m0, int n0, int k0,
                                                uint32_t base, int wave, int lane) {
     constexpr int LPS = DirectCfg<BK_>::LOADS_PER_STAGE;
-    constexpr int PER = LPS / (BK_ / 16) / WM;
-    static_assert(PER * WM * (BK_ / 16) == LPS, "load slots must spread evenly over the MFMA groups");
+    constexpr int PER = MID ? LPS / WM : LPS / (BK_ / 16) / WM;
+    static_assert(MID ? PER * WM == LPS : PER * WM * (BK_ / 16) == LPS,
+                  "load slots must spread evenly over the MFMA groups");
 #pragma unroll
     for (int i = 0; i < WM; i++) {
 #pragma unroll
@@ -496,19 +497,99 @@ swiglu_direct_kernel(const uint16_t* a, const uint16_t* b1, const uint16_t* b2, 
         }
 }
 
+// Variant with the barrier in the middle of each K step (K step 32 = two 16-deep slices, ring of
+// S >= 3 stages).  Step kt: read slice-1 fragments of stage kt while slice 0's MFMAs run; wait for
+// this wave's loads of stage kt+1 and meet at the barrier (stage kt+1 now visible to all, stage
+// kt-1 retired by all); read the slice-0 fragments of stage kt+1 while slice 1's MFMAs run, with
+// the loads of stage kt+S-1 (into stage kt-1's buffer) issued between them.  The matrix pipe
+// always has queued MFMAs when a wave reaches the barrier or waits for LDS data.
+template <int S, bool STORE_PRODUCTS>
+__global__ void __launch_bounds__(THREADS, 1)
+swiglu_direct_mid_kernel(const uint16_t* a, const uint16_t* b1, const uint16_t* b2, uint16_t* out,
+                         uint16_t* c1_out, uint16_t* c2_out, int M, int N, int K, int tiles_m, int tiles_n) {
+    static_assert(S >= 3, "the next stage must be in flight while the previous one is released");
+    constexpr int BK_ = 32;
+    using C = DirectCfg<BK_>;
+    constexpr int LPS = C::LOADS_PER_STAGE;
+    __shared__ __attribute__((aligned(1024))) char lds[S * C::STAGE_BYTES];
+
+    const Tile tile = tile_of(blockIdx.x, tiles_m, tiles_n);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    floatx16 acc1[WM][WN], acc2[WM][WN];
+#pragma unroll
+    for (int i = 0; i < WM; i++)
+#pragma unroll
+        for (int j = 0; j < WN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc1[i][j][r] = acc2[i][j][r] = 0.0f;
+
+    const int kt_n = K / BK_;
+#pragma unroll
+    for (int s = 0; s < S - 1; s++)
+        if (s < kt_n) direct_loads<BK_>(a, b1, b2, N, K, tile.m0, tile.n0, s * BK_, lds + s * C::STAGE_BYTES, wave, lane);
+    // stage 0 ready (stages 1 .. S-2 may still be in flight)
+    if (S - 2 < kt_n) wait_vmcnt<LPS * (S - 2)>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    Frags f0, f1;
+    read_frags_direct<BK_>(lds, wm, wn, lane, 0, f0);
+
+    for (int kt = 0; kt < kt_n; kt++) {
+        const char* st = lds + (kt % S) * C::STAGE_BYTES;
+        read_frags_direct<BK_>(st, wm, wn, lane, 1, f1);
+        mfma_slice(f0, acc1, acc2);
+        // stage kt+1 complete once only stages kt+2 .. kt+S-2 may be pending
+        if (kt + S - 2 < kt_n) wait_vmcnt<LPS * (S - 3)>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (kt + 1 < kt_n) read_frags_direct<BK_>(lds + ((kt + 1) % S) * C::STAGE_BYTES, wm, wn, lane, 0, f0);
+        const bool issue = kt + S - 1 < kt_n;
+        mfma_slice_dma<BK_, true>(f1, acc1, acc2, 0, issue, a, b1, b2, N, K, tile.m0, tile.n0, (kt + S - 1) * BK_,
+                            lds_addr(lds + ((kt + S - 1) % S) * C::STAGE_BYTES), wave, lane);
+    }
+
+    const uint32_t out_bytes = (uint32_t)BM * (uint32_t)N * 2u;
+    const rsrc_t ro = make_rsrc(STORE_PRODUCTS ? c1_out + (int64_t)tile.m0 * N : out + (int64_t)tile.m0 * N, out_bytes);
+    const rsrc_t ro2 = make_rsrc(STORE_PRODUCTS ? c2_out + (int64_t)tile.m0 * N : out, STORE_PRODUCTS ? out_bytes : 0u);
+#pragma unroll
+    for (int i = 0; i < WM; i++)
+#pragma unroll
+        for (int j = 0; j < WN; j++) {
+            const int col = tile.n0 + 64 * wn + 32 * j + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const uint32_t off = ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u;
+                const float c1 = acc1[i][j][r], c2 = acc2[i][j][r];
+                if constexpr (STORE_PRODUCTS) {
+                    bstore_b16<AUX_STREAM>(ro, off, f32_to_bf16(c1));
+                    bstore_b16<AUX_STREAM>(ro2, off, f32_to_bf16(c2));
+                } else {
+                    bstore_b16<AUX_STREAM>(ro, off, f32_to_bf16(silu(c1) * c2));
+                }
+            }
+        }
+}
+
 // K step and ring depth of the full-tile kernel: FUSE_SWIGLU_BK / FUSE_SWIGLU_STAGES override the
 // default (BK 32, 4 stages) for tuning sweeps; every allowed pair fits the 160 KiB of LDS.
 struct DirectPlan {
     int bk, stages;
+    bool mid;  // barrier in the middle of the K step (FUSE_SWIGLU_MID=1; 3 or 4 stages of BK 32)
 };
 DirectPlan direct_plan() {
     const char* b = getenv("FUSE_SWIGLU_BK");
     const char* s = getenv("FUSE_SWIGLU_STAGES");
+    const char* m = getenv("FUSE_SWIGLU_MID");
     const int bk = (b && atoi(b) == 64) ? 64 : 32;
     int st = s ? atoi(s) : 4;
     if (bk == 64) st = 2;
     else if (st < 2 || st > 4) st = 4;
-    return {bk, st};
+    const bool mid = bk == 32 && st >= 3 && m && atoi(m) == 1;  // measured no faster: opt-in
+    return {bk, st, mid};
 }
 
 template <bool STORE_PRODUCTS>
@@ -523,11 +604,18 @@ hipError_t launch(const void* a, const void* b1, const void* b2, void* out, void
     hipLaunchKernelGGL((swiglu_direct_kernel<BKV, SV, STORE_PRODUCTS>), grid, block, 0, stream,          \
                        (const uint16_t*)a, (const uint16_t*)b1, (const uint16_t*)b2, (uint16_t*)out,     \
                        (uint16_t*)c1, (uint16_t*)c2, M, N, K, tm, tn)
-        if (dp.bk == 64) FUSE_DIRECT(64, 2);
+#define FUSE_DIRECT_MID(SV)                                                                           \
+    hipLaunchKernelGGL((swiglu_direct_mid_kernel<SV, STORE_PRODUCTS>), grid, block, 0, stream,           \
+                       (const uint16_t*)a, (const uint16_t*)b1, (const uint16_t*)b2, (uint16_t*)out,     \
+                       (uint16_t*)c1, (uint16_t*)c2, M, N, K, tm, tn)
+        if (dp.mid && dp.bk == 32 && dp.stages == 3) FUSE_DIRECT_MID(3);
+        else if (dp.mid && dp.bk == 32) FUSE_DIRECT_MID(4);
+        else if (dp.bk == 64) FUSE_DIRECT(64, 2);
         else if (dp.stages == 2) FUSE_DIRECT(32, 2);
         else if (dp.stages == 3) FUSE_DIRECT(32, 3);
         else FUSE_DIRECT(32, 4);
 #undef FUSE_DIRECT
+#undef FUSE_DIRECT_MID
         return hipGetLastError();
     }
     if (aligned)

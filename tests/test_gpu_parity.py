@@ -295,15 +295,18 @@ def test_swiglu_parity(M, N, K):
 @pytest.mark.parametrize("env", [{"FUSE_SWIGLU_BK": "32", "FUSE_SWIGLU_STAGES": "2"},
                                  {"FUSE_SWIGLU_BK": "32", "FUSE_SWIGLU_STAGES": "3"},
                                  {"FUSE_SWIGLU_BK": "32", "FUSE_SWIGLU_STAGES": "4"},
+                                 {"FUSE_SWIGLU_BK": "32", "FUSE_SWIGLU_STAGES": "3", "FUSE_SWIGLU_MID": "1"},
+                                 {"FUSE_SWIGLU_BK": "32", "FUSE_SWIGLU_STAGES": "4", "FUSE_SWIGLU_MID": "1"},
                                  {"FUSE_SWIGLU_BK": "64"}, {"FUSE_SWIGLU_GENERAL": "1"}])
 def test_swiglu_full_tile_paths(monkeypatch, env):
     # full tiles take the direct-to-LDS kernel (either K step) unless the general kernel is forced
     for k, v in env.items():
         monkeypatch.setenv(k, v)
     announce(f"swiglu full-tile path {env}")
-    d = synth.swiglu_inputs(512, 384, 320, "bf16", seed=21)
-    out = api.fuse_swiglu_dualgemm(d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda())
-    assert_close(out, oracle.swiglu(d["a"], d["b1"], d["b2"]), "bf16", f"swiglu {env}")
+    for K in (320, 64, 32, 96):  # several steps, and rings longer than the K loop
+        d = synth.swiglu_inputs(512, 384, K, "bf16", seed=21 + K)
+        out = api.fuse_swiglu_dualgemm(d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda())
+        assert_close(out, oracle.swiglu(d["a"], d["b1"], d["b2"]), "bf16", f"swiglu K={K} {env}")
 
 
 def test_swiglu_workload_sampled_rows():
