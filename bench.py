@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 HEADLINE = "addln_f16_2048x4096"
 ROTATE_BYTES = 1 << 30
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "add_layernorm_f16_2048x4096_counters.txt")
-HEADLINE_SOURCES = ["fuse_common.hpp", "row_kernels.hpp", "row_launch.hpp", "abi.hip"]
+HEADLINE_SOURCES = ["fuse_common.hpp", "launch.hpp", "row_kernels.hpp", "row_launch.hpp", "row_plan.hip"]
 
 
 def log(msg):
