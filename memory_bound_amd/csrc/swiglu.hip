@@ -257,10 +257,10 @@ swiglu_kernel(const uint16_t* a, const uint16_t* b1, const uint16_t* b2, uint16_
 }
 
 // ------------------------------------------------------------------------------------------------
-// Full-tile kernel (M % 256 == 0, N % 128 == 0, K % BK == 0, 16-byte aligned operands): operands go
+// Full-tile kernel (M % 256 == 0, N % 128 == 0, K % 32 == 0, 16-byte aligned operands): operands go
 // from memory straight into LDS with global_load_lds_dwordx4 (no VGPR staging, no LDS store
-// instructions), through a ring of S stages, and b1/b2 are transposed at fragment-read time with
-// ds_read_b64_tr_b16.
+// instructions), through a ring of S stages of one 32-deep K step each, and b1/b2 are transposed at
+// fragment-read time with ds_read_b64_tr_b16.
 //
 // ds_read_b64_tr_b16, per group of 16 lanes: if lane j reads the four 16-bit values D[j][0..3], lane
 // i receives D[i/4][i%4], D[4+i/4][i%4], D[8+i/4][i%4], D[12+i/4][i%4].  With lane j reading
@@ -271,26 +271,31 @@ swiglu_kernel(const uint16_t* a, const uint16_t* b1, const uint16_t* b2, uint16_
 // served 16 lanes at a time and a ds_read_b64 32 lanes at a time.  XOR swizzles on 16-byte chunks
 // keep both free of bank conflicts (the asynchronous writes fill 1 KiB per wave instruction in
 // lane order and never conflict):
-//   a tile  [256][BK]: chunk q of row r at q ^ ((r >> 2) & 3) (BK = 32, four 64-byte rows per
-//                      256 bytes) or q ^ ((r ^ r >> 3) & 7) (BK = 64, two 128-byte rows)
-//   b tiles [BK][128]: chunk q of row k at q ^ 4 (k & 3): the 64 bytes the two 16-lane groups of
+//   a tile  [256][32]: chunk q of row r at q ^ ((r >> 2) & 3) (four 64-byte rows per 256 bytes)
+//   b tiles [32][128]: chunk q of row k at q ^ 4 (k & 3): the 64 bytes the two 16-lane groups of
 //                      a transposed read take from each of four consecutive rows land in four
 //                      different 64-byte quarters of the bank space
+//
+// Pipeline.  The fragments of a K step's first 16-deep slice are read during the previous step,
+// so the matrix cores resume right after the step's barrier: in step kt the MFMAs of slice 0
+// (registers f0, stage kt) run while slice 1 of stage kt is read into f1, and the MFMAs of slice 1
+// run while slice 0 of stage kt+1 is read into f0.  Each LDS read is issued after an MFMA, in the
+// order the next slice consumes them; the eight loads of stage kt+S-1 go out between the later
+// MFMAs.  The barrier closing step kt therefore needs stages kt+1 and kt+2 complete (this wave's
+// loads via vmcnt, everyone's via the barrier) and retires stage kt, whose buffer the loads of
+// step kt+1 overwrite.
 // ------------------------------------------------------------------------------------------------
 
-template <int BK_> struct DirectCfg {
-    static constexpr int BKD = BK_;
-    static constexpr int A_ROW_BYTES = BK_ * 2;             // 64 or 128
-    static constexpr int A_CHUNKS = A_ROW_BYTES / 16;       // 4 or 8 per row
-    static constexpr int A_BYTES = BM * A_ROW_BYTES;        // 16 or 32 KiB
-    static constexpr int B_BYTES = BK_ * BN * 2;            // 8 or 16 KiB per matrix
+struct DirectCfg {
+    static constexpr int BKD = 32;
+    static constexpr int A_ROW_BYTES = 64, A_CHUNKS = 4;
+    static constexpr int A_BYTES = BM * A_ROW_BYTES;  // 16 KiB
+    static constexpr int B_BYTES = BKD * BN * 2;      // 8 KiB per matrix
     static constexpr int STAGE_BYTES = A_BYTES + 2 * B_BYTES;
-    // asynchronous load instructions per wave per stage: a rows, then b1 and b2 rows
-    static constexpr int LOADS_PER_STAGE = 64 / (1024 / A_ROW_BYTES) + 2 * (BK_ / 16);
-    __device__ static int a_phys(int r, int q) {
-        if constexpr (BK_ == 32) return q ^ ((r >> 2) & 3);
-        else return q ^ ((r ^ (r >> 3)) & 7);
-    }
+    // asynchronous load instructions per wave per stage: 4 of a rows, 2 each of b1 and b2 rows
+    static constexpr int A_LOADS = 4;
+    static constexpr int LOADS_PER_STAGE = 8;
+    __device__ static int a_phys(int r, int q) { return q ^ ((r >> 2) & 3); }
 };
 
 __device__ __forceinline__ int b_phys(int k, int q) { return q ^ (4 * (k & 3)); }
@@ -318,199 +323,94 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
 }
 
-// Issue the asynchronous loads of K step k0 into LDS stage `st`.  Wave w fills A rows
-// [64 w, 64 w + 64) and b rows [BK/4 w, BK/4 w + BK/4) of both b1 and b2.
-template <int BK_>
-__device__ __forceinline__ void direct_loads(const uint16_t* a, const uint16_t* b1, const uint16_t* b2,
-                                             int N, int K, int m0, int n0, int k0, char* st, int wave, int lane) {
-    using C = DirectCfg<BK_>;
-    constexpr int ROWS_PER_INSTR_A = 1024 / C::A_ROW_BYTES;  // 16 or 8
-    const uint32_t base = lds_addr(st);
-#pragma unroll
-    for (int i = 0; i < 64 / ROWS_PER_INSTR_A; i++) {
-        const int r0 = 64 * wave + ROWS_PER_INSTR_A * i;
-        const int r = r0 + lane / C::A_CHUNKS, p = lane % C::A_CHUNKS;
-        const int q = C::a_phys(r, p);  // the swizzle is its own inverse
-        dma16(a + (int64_t)(m0 + r) * K + k0 + 8 * q, base + r0 * C::A_ROW_BYTES);
-    }
-    constexpr int KR = C::BKD / 4;  // b rows per wave
-#pragma unroll
-    for (int i = 0; i < KR / 4; i++) {
-        const int k0r = KR * wave + 4 * i;
-        const int kr = k0r + lane / 16, p = lane % 16;
-        const int q = b_phys(kr, p);
-        const int64_t off = (int64_t)(k0 + kr) * N + n0 + 8 * q;
-        dma16(b1 + off, base + C::A_BYTES + k0r * 256);
-        dma16(b2 + off, base + C::A_BYTES + C::B_BYTES + k0r * 256);
-    }
-}
-
-// Load slot `slot` (0 .. LOADS_PER_STAGE-1) of direct_loads: slots 0 .. NA-1 are rows of a, the
-// rest alternate b1 / b2 rows.  Called with compile-time slot numbers from unrolled loops, so the
-// branches fold away.
-template <int BK_>
+// Load slot `slot` (0 .. 7) of K step k0 into the stage at LDS address `base`: slots 0-3 fill a rows
+// [64 w, 64 w + 64) of wave w (16 rows of 64 bytes per instruction), slots 4-7 four rows each of
+// the b1 and b2 tiles, wave w taking rows [8 w, 8 w + 8).  Called with compile-time slot numbers
+// from unrolled loops, so the branch folds away.
 __device__ __forceinline__ void dma_slot(int slot, const uint16_t* a, const uint16_t* b1, const uint16_t* b2,
                                          int N, int K, int m0, int n0, int k0, uint32_t base, int wave, int lane) {
-    using C = DirectCfg<BK_>;
-    constexpr int ROWS_PER_INSTR_A = 1024 / C::A_ROW_BYTES;
-    constexpr int NA = 64 / ROWS_PER_INSTR_A;
-    if (slot < NA) {
-        const int r0 = 64 * wave + ROWS_PER_INSTR_A * slot;
+    using C = DirectCfg;
+    if (slot < C::A_LOADS) {
+        const int r0 = 64 * wave + 16 * slot;
         const int r = r0 + lane / C::A_CHUNKS, p = lane % C::A_CHUNKS;
         dma16(a + (int64_t)(m0 + r) * K + k0 + 8 * C::a_phys(r, p), base + r0 * C::A_ROW_BYTES);
     } else {
-        const int j = slot - NA, i = j >> 1, mat = j & 1;
-        const int k0r = (C::BKD / 4) * wave + 4 * i;
+        const int j = slot - C::A_LOADS, i = j >> 1, mat = j & 1;
+        const int k0r = 8 * wave + 4 * i;
         const int kr = k0r + lane / 16, p = lane % 16;
         const int64_t off = (int64_t)(k0 + kr) * N + n0 + 8 * b_phys(kr, p);
         dma16((mat == 0 ? b1 : b2) + off, base + C::A_BYTES + mat * C::B_BYTES + k0r * 256);
     }
 }
 
-// The 16 MFMAs of one k slice in WM groups (one row block each); after each group, PER of the
-// next stage's load slots starting at slot0 are issued when `issue` is set.
-template <int BK_, bool MID = false>
-__device__ __forceinline__ void mfma_slice_dma(const Frags& f, floatx16 (&acc1)[WM][WN], floatx16 (&acc2)[WM][WN],
-                                               int slot0, bool issue, const uint16_t* a, const uint16_t* b1,
-                                               const uint16_t* b2, int N, int K, int m0, int n0, int k0,
-                                               uint32_t base, int wave, int lane) {
-    constexpr int LPS = DirectCfg<BK_>::LOADS_PER_STAGE;
-    constexpr int PER = MID ? LPS / WM : LPS / (BK_ / 16) / WM;
-    static_assert(MID ? PER * WM == LPS : PER * WM * (BK_ / 16) == LPS,
-                  "load slots must spread evenly over the MFMA groups");
-#pragma unroll
-    for (int i = 0; i < WM; i++) {
-#pragma unroll
-        for (int j = 0; j < WN; j++) {
-            acc1[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b1[j], acc1[i][j], 0, 0, 0);
-            acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b2[j], acc2[i][j], 0, 0, 0);
-        }
-        if (issue) {
-#pragma unroll
-            for (int p = 0; p < PER; p++) dma_slot<BK_>(slot0 + i * PER + p, a, b1, b2, N, K, m0, n0, k0, base, wave, lane);
-        }
-    }
-}
-
-// B fragment (32 columns starting at nb, k = kb .. kb + 15) for this lane, via two transposed reads.
-__device__ __forceinline__ bf16x8 b_frag_tr(const char* bt, int nb, int kb, int lane) {
+// One 16-byte piece of a B fragment (32 columns from nb, k = kb .. kb + 15): transposed read t of 2.
+__device__ __forceinline__ v4i16 b_frag_half(const char* bt, int nb, int kb, int lane, int t) {
     const int g = lane >> 4, j = lane & 15;
     const int n = nb + 16 * (g & 1) + 4 * (j & 3);
     const int q = n >> 3, half = (n >> 2) & 1;
-    v4i16 h[2];
-#pragma unroll
-    for (int t = 0; t < 2; t++) {
-        const int k = kb + 8 * (g >> 1) + 4 * t + (j >> 2);
-        const char* p = bt + k * 256 + b_phys(k, q) * 16 + half * 8;
-        h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(__attribute__((address_space(3))) const char*)p);
-    }
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    const int k = kb + 8 * (g >> 1) + 4 * t + (j >> 2);
+    const char* p = bt + k * 256 + b_phys(k, q) * 16 + half * 8;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(__attribute__((address_space(3))) const char*)p);
 }
 
-template <int BK_>
-__device__ __forceinline__ void read_frags_direct(const char* st, int wm, int wn, int lane, int kk, Frags& f) {
-    using C = DirectCfg<BK_>;
-    const int qa = 2 * kk + (lane >> 5);
+__device__ __forceinline__ bf16x8 join(v4i16 lo, v4i16 hi) {
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ bf16x8 a_frag(const char* st, int wm, int lane, int kk, int i) {
+    using C = DirectCfg;
+    const int r = 128 * wm + 32 * i + (lane & 31), qa = 2 * kk + (lane >> 5);
+    return *reinterpret_cast<const bf16x8*>(st + r * C::A_ROW_BYTES + C::a_phys(r, qa) * 16);
+}
+
+// The 16 MFMAs of one k slice on fragments `f`, interleaved with the LDS reads of the fragments `nx`
+// of slice rk of stage `rs` (one read after each of the first MFMAs, in the order the next slice
+// uses them) and with load slots slot0 .. slot0 + 3 of the stage at LDS address `base` (after
+// MFMAs 9, 11, 13 and 15).
+__device__ __forceinline__ void slice_step(const Frags& f, Frags& nx, const char* rs, int rk,
+                                           floatx16 (&acc1)[WM][WN], floatx16 (&acc2)[WM][WN], int slot0,
+                                           const uint16_t* a, const uint16_t* b1, const uint16_t* b2, int N,
+                                           int K, int m0, int n0, int k0, uint32_t base, int wm, int wn,
+                                           int wave, int lane) {
+    using C = DirectCfg;
+    const char* bt1 = rs + C::A_BYTES;
+    const char* bt2 = rs + C::A_BYTES + C::B_BYTES;
+    v4i16 h[8];
 #pragma unroll
-    for (int i = 0; i < WM; i++) {
-        const int r = 128 * wm + 32 * i + (lane & 31);
-        f.a[i] = *reinterpret_cast<const bf16x8*>(st + r * C::A_ROW_BYTES + C::a_phys(r, qa) * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < WN; j++) {
-        f.b1[j] = b_frag_tr(st + C::A_BYTES, 64 * wn + 32 * j, 16 * kk, lane);
-        f.b2[j] = b_frag_tr(st + C::A_BYTES + C::B_BYTES, 64 * wn + 32 * j, 16 * kk, lane);
+    for (int m = 0; m < 16; m++) {
+        const int i = m >> 2, j = (m >> 1) & 1;
+        if (m & 1) acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b2[j], acc2[i][j], 0, 0, 0);
+        else acc1[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b1[j], acc1[i][j], 0, 0, 0);
+        // reads, in the order slice rk's MFMAs need them: a0, b1[0], b2[0], b1[1], b2[1], a1, a2, a3
+        switch (m) {
+            case 0: nx.a[0] = a_frag(rs, wm, lane, rk, 0); break;
+            case 1: h[0] = b_frag_half(bt1, 64 * wn, 16 * rk, lane, 0); break;
+            case 2: h[1] = b_frag_half(bt1, 64 * wn, 16 * rk, lane, 1); nx.b1[0] = join(h[0], h[1]); break;
+            case 3: h[2] = b_frag_half(bt2, 64 * wn, 16 * rk, lane, 0); break;
+            case 4: h[3] = b_frag_half(bt2, 64 * wn, 16 * rk, lane, 1); nx.b2[0] = join(h[2], h[3]); break;
+            case 5: h[4] = b_frag_half(bt1, 64 * wn + 32, 16 * rk, lane, 0); break;
+            case 6: h[5] = b_frag_half(bt1, 64 * wn + 32, 16 * rk, lane, 1); nx.b1[1] = join(h[4], h[5]); break;
+            case 7: h[6] = b_frag_half(bt2, 64 * wn + 32, 16 * rk, lane, 0); break;
+            case 8: h[7] = b_frag_half(bt2, 64 * wn + 32, 16 * rk, lane, 1); nx.b2[1] = join(h[6], h[7]); break;
+            case 9: nx.a[1] = a_frag(rs, wm, lane, rk, 1); break;
+            case 10: nx.a[2] = a_frag(rs, wm, lane, rk, 2); break;
+            case 11: nx.a[3] = a_frag(rs, wm, lane, rk, 3); break;
+            default: break;
+        }
+        if (m >= 9 && (m & 1))
+            dma_slot(slot0 + (m - 9) / 2, a, b1, b2, N, K, m0, n0, k0, base, wave, lane);
+        // keep this order: the scheduler would otherwise bunch the reads and the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-template <int BK_, int S, bool STORE_PRODUCTS>
+template <int S, bool STORE_PRODUCTS>
 __global__ void __launch_bounds__(THREADS, 1)
 swiglu_direct_kernel(const uint16_t* a, const uint16_t* b1, const uint16_t* b2, uint16_t* out,
                      uint16_t* c1_out, uint16_t* c2_out, int M, int N, int K, int tiles_m, int tiles_n) {
-    using C = DirectCfg<BK_>;
-    constexpr int SLICES = BK_ / 16;
-    __shared__ __attribute__((aligned(1024))) char lds[S * C::STAGE_BYTES];
-
-    const Tile tile = tile_of(blockIdx.x, tiles_m, tiles_n);
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
-
-    floatx16 acc1[WM][WN], acc2[WM][WN];
-#pragma unroll
-    for (int i = 0; i < WM; i++)
-#pragma unroll
-        for (int j = 0; j < WN; j++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) acc1[i][j][r] = acc2[i][j][r] = 0.0f;
-
-    const int kt_n = K / BK_;
-    // prologue: stages 0 .. S-2 in flight
-#pragma unroll
-    for (int s = 0; s < S - 1; s++)
-        if (s < kt_n) direct_loads<BK_>(a, b1, b2, N, K, tile.m0, tile.n0, s * BK_, lds + s * C::STAGE_BYTES, wave, lane);
-
-    for (int kt = 0; kt < kt_n; kt++) {
-        // This wave's loads of stage kt are done once no more than the loads of the stages issued
-        // after it (kt+1 .. kt+S-2) are pending.  After the barrier every wave's stage kt is in
-        // LDS and every wave has finished reading stage kt-1, whose buffer the loads of stage
-        // kt+S-1 then overwrite while stage kt is multiplied.
-        if (kt + S - 2 < kt_n) wait_vmcnt<C::LOADS_PER_STAGE * (S - 2)>();
-        else wait_vmcnt<0>();
-        __syncthreads();
-        // the loads of stage kt+S-1 are issued a few at a time between this step's MFMAs, so the
-        // address unit's queue never holds a wave's instruction issue for long
-        const bool issue = kt + S - 1 < kt_n;
-        const uint32_t nbase = lds_addr(lds + ((kt + S - 1) % S) * C::STAGE_BYTES);
-        const int nk0 = (kt + S - 1) * BK_;
-        const char* st = lds + (kt % S) * C::STAGE_BYTES;
-        Frags f[2];
-        read_frags_direct<BK_>(st, wm, wn, lane, 0, f[0]);
-#pragma unroll
-        for (int kk = 0; kk < SLICES; kk++) {
-            if (kk + 1 < SLICES) read_frags_direct<BK_>(st, wm, wn, lane, kk + 1, f[(kk + 1) & 1]);
-            mfma_slice_dma<BK_>(f[kk & 1], acc1, acc2, kk * (C::LOADS_PER_STAGE / SLICES), issue, a, b1, b2, N, K,
-                                tile.m0, tile.n0, nk0, nbase, wave, lane);
-        }
-    }
-
-    const uint32_t out_bytes = (uint32_t)BM * (uint32_t)N * 2u;
-    const rsrc_t ro = make_rsrc(STORE_PRODUCTS ? c1_out + (int64_t)tile.m0 * N : out + (int64_t)tile.m0 * N, out_bytes);
-    const rsrc_t ro2 = make_rsrc(STORE_PRODUCTS ? c2_out + (int64_t)tile.m0 * N : out, STORE_PRODUCTS ? out_bytes : 0u);
-#pragma unroll
-    for (int i = 0; i < WM; i++)
-#pragma unroll
-        for (int j = 0; j < WN; j++) {
-            const int col = tile.n0 + 64 * wn + 32 * j + (lane & 31);
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const uint32_t off = ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u;
-                const float c1 = acc1[i][j][r], c2 = acc2[i][j][r];
-                if constexpr (STORE_PRODUCTS) {
-                    bstore_b16<AUX_STREAM>(ro, off, f32_to_bf16(c1));
-                    bstore_b16<AUX_STREAM>(ro2, off, f32_to_bf16(c2));
-                } else {
-                    bstore_b16<AUX_STREAM>(ro, off, f32_to_bf16(silu(c1) * c2));
-                }
-            }
-        }
-}
-
-// Variant with the barrier in the middle of each K step (K step 32 = two 16-deep slices, ring of
-// S >= 3 stages).  Step kt: read slice-1 fragments of stage kt while slice 0's MFMAs run; wait for
-// this wave's loads of stage kt+1 and meet at the barrier (stage kt+1 now visible to all, stage
-// kt-1 retired by all); read the slice-0 fragments of stage kt+1 while slice 1's MFMAs run, with
-// the loads of stage kt+S-1 (into stage kt-1's buffer) issued between them.  The matrix pipe
-// always has queued MFMAs when a wave reaches the barrier or waits for LDS data.
-template <int S, bool STORE_PRODUCTS>
-__global__ void __launch_bounds__(THREADS, 1)
-swiglu_direct_mid_kernel(const uint16_t* a, const uint16_t* b1, const uint16_t* b2, uint16_t* out,
-                         uint16_t* c1_out, uint16_t* c2_out, int M, int N, int K, int tiles_m, int tiles_n) {
-    static_assert(S >= 3, "the next stage must be in flight while the previous one is released");
-    constexpr int BK_ = 32;
-    using C = DirectCfg<BK_>;
+    using C = DirectCfg;
     constexpr int LPS = C::LOADS_PER_STAGE;
+    static_assert(S >= 3 && S * C::STAGE_BYTES <= 160 * 1024, "ring of 3 to 5 stages of 32 KiB");
     __shared__ __attribute__((aligned(1024))) char lds[S * C::STAGE_BYTES];
 
     const Tile tile = tile_of(blockIdx.x, tiles_m, tiles_n);
@@ -526,31 +426,44 @@ swiglu_direct_mid_kernel(const uint16_t* a, const uint16_t* b1, const uint16_t* 
 #pragma unroll
             for (int r = 0; r < 16; r++) acc1[i][j][r] = acc2[i][j][r] = 0.0f;
 
-    const int kt_n = K / BK_;
+    const int kt_n = K / C::BKD;
+    // Prologue: stages 0 .. S-2.  Every step issues the loads of one stage; past the last K step
+    // they reload the last stage into a buffer nobody reads again, which keeps the vmcnt
+    // bookkeeping the same on every step.
 #pragma unroll
-    for (int s = 0; s < S - 1; s++)
-        if (s < kt_n) direct_loads<BK_>(a, b1, b2, N, K, tile.m0, tile.n0, s * BK_, lds + s * C::STAGE_BYTES, wave, lane);
-    // stage 0 ready (stages 1 .. S-2 may still be in flight)
-    if (S - 2 < kt_n) wait_vmcnt<LPS * (S - 2)>();
-    else wait_vmcnt<0>();
+    for (int s = 0; s < S - 1; s++) {
+        const uint32_t base = lds_addr(lds + s * C::STAGE_BYTES);
+        const int k0 = min(s, kt_n - 1) * C::BKD;
+#pragma unroll
+        for (int l = 0; l < LPS; l++) dma_slot(l, a, b1, b2, N, K, tile.m0, tile.n0, k0, base, wave, lane);
+    }
+    wait_vmcnt<LPS * (S - 3)>();  // stages 0 and 1 are in
     __syncthreads();
     Frags f0, f1;
-    read_frags_direct<BK_>(lds, wm, wn, lane, 0, f0);
+#pragma unroll
+    for (int i = 0; i < WM; i++) f0.a[i] = a_frag(lds, wm, lane, 0, i);
+#pragma unroll
+    for (int j = 0; j < WN; j++) {
+        f0.b1[j] = join(b_frag_half(lds + C::A_BYTES, 64 * wn + 32 * j, 0, lane, 0),
+                        b_frag_half(lds + C::A_BYTES, 64 * wn + 32 * j, 0, lane, 1));
+        f0.b2[j] = join(b_frag_half(lds + C::A_BYTES + C::B_BYTES, 64 * wn + 32 * j, 0, lane, 0),
+                        b_frag_half(lds + C::A_BYTES + C::B_BYTES, 64 * wn + 32 * j, 0, lane, 1));
+    }
 
     for (int kt = 0; kt < kt_n; kt++) {
         const char* st = lds + (kt % S) * C::STAGE_BYTES;
-        read_frags_direct<BK_>(st, wm, wn, lane, 1, f1);
-        mfma_slice(f0, acc1, acc2);
-        // stage kt+1 complete once only stages kt+2 .. kt+S-2 may be pending
-        if (kt + S - 2 < kt_n) wait_vmcnt<LPS * (S - 3)>();
-        else wait_vmcnt<0>();
+        const char* sn = lds + ((kt + 1) % S) * C::STAGE_BYTES;
+        const uint32_t nbase = lds_addr(lds + ((kt + S - 1) % S) * C::STAGE_BYTES);
+        const int nk0 = min(kt + S - 1, kt_n - 1) * C::BKD;
+        slice_step(f0, f1, st, 1, acc1, acc2, 0, a, b1, b2, N, K, tile.m0, tile.n0, nk0, nbase, wm, wn, wave, lane);
+        slice_step(f1, f0, sn, 0, acc1, acc2, 4, a, b1, b2, N, K, tile.m0, tile.n0, nk0, nbase, wm, wn, wave, lane);
+        wait_vmcnt<LPS * (S - 3)>();
         __syncthreads();
-        if (kt + 1 < kt_n) read_frags_direct<BK_>(lds + ((kt + 1) % S) * C::STAGE_BYTES, wm, wn, lane, 0, f0);
-        const bool issue = kt + S - 1 < kt_n;
-        mfma_slice_dma<BK_, true>(f1, acc1, acc2, 0, issue, a, b1, b2, N, K, tile.m0, tile.n0, (kt + S - 1) * BK_,
-                            lds_addr(lds + ((kt + S - 1) % S) * C::STAGE_BYTES), wave, lane);
     }
+    wait_vmcnt<0>();  // no load may still be writing this workgroup's LDS when it ends
 
+    // Epilogue.  Block (i, j) element r of lane l sits at row 8 (r/4) + 4 (l/32) + r%4, column l%32
+    // of the block.
     const uint32_t out_bytes = (uint32_t)BM * (uint32_t)N * 2u;
     const rsrc_t ro = make_rsrc(STORE_PRODUCTS ? c1_out + (int64_t)tile.m0 * N : out + (int64_t)tile.m0 * N, out_bytes);
     const rsrc_t ro2 = make_rsrc(STORE_PRODUCTS ? c2_out + (int64_t)tile.m0 * N : out, STORE_PRODUCTS ? out_bytes : 0u);
@@ -574,22 +487,14 @@ swiglu_direct_mid_kernel(const uint16_t* a, const uint16_t* b1, const uint16_t* 
         }
 }
 
-// K step and ring depth of the full-tile kernel: FUSE_SWIGLU_BK / FUSE_SWIGLU_STAGES override the
-// default (BK 32, 4 stages) for tuning sweeps; every allowed pair fits the 160 KiB of LDS.
-struct DirectPlan {
-    int bk, stages;
-    bool mid;  // barrier in the middle of the K step (FUSE_SWIGLU_MID=1; 3 or 4 stages of BK 32)
-};
-DirectPlan direct_plan() {
-    const char* b = getenv("FUSE_SWIGLU_BK");
+// Ring depth of the full-tile kernel (FUSE_SWIGLU_STAGES, 3 to 5, overrides the default for tuning
+// sweeps; five stages take all 160 KiB of LDS).  0: no full-tile kernel for this shape.
+int direct_stages(int M, int N, int K, bool aligned) {
+    if (!aligned || M % BM != 0 || N % BN != 0 || K % DirectCfg::BKD != 0) return 0;
+    if (getenv("FUSE_SWIGLU_GENERAL") != nullptr) return 0;
     const char* s = getenv("FUSE_SWIGLU_STAGES");
-    const char* m = getenv("FUSE_SWIGLU_MID");
-    const int bk = (b && atoi(b) == 64) ? 64 : 32;
-    int st = s ? atoi(s) : 4;
-    if (bk == 64) st = 2;
-    else if (st < 2 || st > 4) st = 4;
-    const bool mid = bk == 32 && st >= 3 && m && atoi(m) == 1;  // measured no faster: opt-in
-    return {bk, st, mid};
+    const int st = s ? atoi(s) : 4;
+    return (st >= 3 && st <= 5) ? st : 4;
 }
 
 template <bool STORE_PRODUCTS>
@@ -598,24 +503,16 @@ hipError_t launch(const void* a, const void* b1, const void* b2, void* out, void
     const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
     const bool aligned = (K % 8 == 0) && (N % 8 == 0) && (((uintptr_t)a | (uintptr_t)b1 | (uintptr_t)b2) & 15u) == 0;
     const dim3 grid((unsigned)(tm * tn)), block(THREADS);
-    const DirectPlan dp = direct_plan();
-    if (aligned && M % BM == 0 && N % BN == 0 && K % dp.bk == 0 && getenv("FUSE_SWIGLU_GENERAL") == nullptr) {
-#define FUSE_DIRECT(BKV, SV)                                                                          \
-    hipLaunchKernelGGL((swiglu_direct_kernel<BKV, SV, STORE_PRODUCTS>), grid, block, 0, stream,          \
+    const int st = direct_stages(M, N, K, aligned);
+    if (st != 0) {
+#define FUSE_DIRECT(SV)                                                                               \
+    hipLaunchKernelGGL((swiglu_direct_kernel<SV, STORE_PRODUCTS>), grid, block, 0, stream,              \
                        (const uint16_t*)a, (const uint16_t*)b1, (const uint16_t*)b2, (uint16_t*)out,     \
                        (uint16_t*)c1, (uint16_t*)c2, M, N, K, tm, tn)
-#define FUSE_DIRECT_MID(SV)                                                                           \
-    hipLaunchKernelGGL((swiglu_direct_mid_kernel<SV, STORE_PRODUCTS>), grid, block, 0, stream,           \
-                       (const uint16_t*)a, (const uint16_t*)b1, (const uint16_t*)b2, (uint16_t*)out,     \
-                       (uint16_t*)c1, (uint16_t*)c2, M, N, K, tm, tn)
-        if (dp.mid && dp.bk == 32 && dp.stages == 3) FUSE_DIRECT_MID(3);
-        else if (dp.mid && dp.bk == 32) FUSE_DIRECT_MID(4);
-        else if (dp.bk == 64) FUSE_DIRECT(64, 2);
-        else if (dp.stages == 2) FUSE_DIRECT(32, 2);
-        else if (dp.stages == 3) FUSE_DIRECT(32, 3);
-        else FUSE_DIRECT(32, 4);
+        if (st == 3) FUSE_DIRECT(3);
+        else if (st == 5) FUSE_DIRECT(5);
+        else FUSE_DIRECT(4);
 #undef FUSE_DIRECT
-#undef FUSE_DIRECT_MID
         return hipGetLastError();
     }
     if (aligned)

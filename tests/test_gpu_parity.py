@@ -292,26 +292,29 @@ def test_swiglu_parity(M, N, K):
     print(f"  max_abs={r['max_abs']:.3e}", flush=True)
 
 
-@pytest.mark.parametrize("env", [{"FUSE_SWIGLU_BK": "32", "FUSE_SWIGLU_STAGES": "2"},
-                                 {"FUSE_SWIGLU_BK": "32", "FUSE_SWIGLU_STAGES": "3"},
-                                 {"FUSE_SWIGLU_BK": "32", "FUSE_SWIGLU_STAGES": "4"},
-                                 {"FUSE_SWIGLU_BK": "32", "FUSE_SWIGLU_STAGES": "3", "FUSE_SWIGLU_MID": "1"},
-                                 {"FUSE_SWIGLU_BK": "32", "FUSE_SWIGLU_STAGES": "4", "FUSE_SWIGLU_MID": "1"},
-                                 {"FUSE_SWIGLU_BK": "64"}, {"FUSE_SWIGLU_GENERAL": "1"}])
+@pytest.mark.parametrize("env", [{"FUSE_SWIGLU_STAGES": "3"}, {"FUSE_SWIGLU_STAGES": "4"},
+                                 {"FUSE_SWIGLU_STAGES": "5"}, {"FUSE_SWIGLU_GENERAL": "1"}])
 def test_swiglu_full_tile_paths(monkeypatch, env):
-    # full tiles take the direct-to-LDS kernel (either K step) unless the general kernel is forced
+    # full tiles (N = 384, 640) take the direct-to-LDS kernel with a ring of 3 to 5 stages unless
+    # the general kernel is forced; N = 480 is not a multiple of the tile width and takes the
+    # general kernel
     for k, v in env.items():
         monkeypatch.setenv(k, v)
     announce(f"swiglu full-tile path {env}")
-    for K in (320, 64, 32, 96):  # several steps, and rings longer than the K loop
-        d = synth.swiglu_inputs(512, 384, K, "bf16", seed=21 + K)
-        out = api.fuse_swiglu_dualgemm(d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda())
-        assert_close(out, oracle.swiglu(d["a"], d["b1"], d["b2"]), "bf16", f"swiglu K={K} {env}")
+    for N in (384, 480, 640):
+        for K in (320, 64, 32, 96):  # several steps, and rings longer than the K loop
+            d = synth.swiglu_inputs(512, N, K, "bf16", seed=21 + K + N)
+            out = api.fuse_swiglu_dualgemm(d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda())
+            assert_close(out, oracle.swiglu(d["a"], d["b1"], d["b2"]), "bf16", f"swiglu N={N} K={K} {env}")
 
 
-def test_swiglu_workload_sampled_rows():
+@pytest.mark.parametrize("stages", [None, "3", "5"])
+def test_swiglu_workload_sampled_rows(monkeypatch, stages):
+    # the default ring depth and the shallowest and deepest rings at the full size
+    if stages:
+        monkeypatch.setenv("FUSE_SWIGLU_STAGES", stages)
     w = synth.WORKLOADS["swiglu_bf16_2048x8960x1536"]
-    announce("swiglu workload 2048x8960x1536")
+    announce(f"swiglu workload 2048x8960x1536 stages {stages or 'default'}")
     d = w.inputs()
     out = api.fuse_swiglu_dualgemm(d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda()).cpu()
     rng = np.random.default_rng(1006)
