@@ -58,6 +58,8 @@ def _load():
     dp = ctypes.POINTER(ctypes.c_double)
     i64 = ctypes.c_int64
     lib.oracle_add_layernorm.argtypes = [dp, dp, dp, dp, dp, i64, i64, ctypes.c_double]
+    lib.oracle_add_layernorm_ex.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i64, i64, ctypes.c_double,
+                                            ctypes.c_int]
     lib.oracle_bias_gelu_residual.argtypes = [dp, dp, dp, dp, i64, i64]
     lib.oracle_softmax_rows.argtypes = [dp, dp, i64, i64, ctypes.c_double]
     lib.oracle_matmul.argtypes = [dp, dp, dp, i64, i64, i64]
@@ -65,7 +67,7 @@ def _load():
     lib.oracle_round.argtypes = [dp, dp, i64, ctypes.c_int]
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
-    for name in ("oracle_add_layernorm", "oracle_bias_gelu_residual", "oracle_softmax_rows",
+    for name in ("oracle_add_layernorm", "oracle_add_layernorm_ex", "oracle_bias_gelu_residual", "oracle_softmax_rows",
                  "oracle_matmul", "oracle_swiglu", "oracle_round"):
         getattr(lib, name).restype = None
     _lib = lib
@@ -109,6 +111,26 @@ def add_layernorm(x, residual, gamma, beta, eps: float) -> np.ndarray:
     _load().oracle_add_layernorm(_p(x), _p(r) if r is not None else None, _p(g), _p(b), _p(y),
                                  rows, hidden, float(eps))
     return y
+
+
+def add_layernorm_ex(x, residual, gamma, beta, eps: float, relu: bool = False):
+    """LayerNorm variants; [P1] §二.1 (LayerNorm + ReLU), [P2] §4.4 (multi-output fusion).
+
+    Returns (y, sum, mean, var): y = LN(x + residual) * gamma + beta, clamped below at 0 when
+    relu; sum = x + residual; mean and var (population, without eps) per row.
+    """
+    x = f64(x)
+    rows, hidden = x.shape
+    r = f64(residual) if residual is not None else None
+    g, b = f64(gamma), f64(beta)
+    assert g.shape == (hidden,) and b.shape == (hidden,)
+    if r is not None:
+        assert r.shape == x.shape
+    y, sm = np.empty_like(x), np.empty_like(x)
+    mean, var = np.empty(rows), np.empty(rows)
+    _load().oracle_add_layernorm_ex(_p(x), _p(r) if r is not None else None, _p(g), _p(b), _p(y),
+                                    _p(sm), _p(mean), _p(var), rows, hidden, float(eps), int(bool(relu)))
+    return y, sm, mean, var
 
 
 def bias_gelu_residual(x, bias, residual) -> np.ndarray:

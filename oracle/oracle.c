@@ -69,6 +69,62 @@ void oracle_add_layernorm(const double *x, const double *residual,
 }
 
 /*
+ * Variants of the same residual-add + LayerNorm row operation.
+ *
+ * [P1] §二.1 lists "LayerNorm + ReLU" as one vertical fusion: the
+ * activation is applied to the normalised value before it is stored,
+ * y = max(LN(v), 0); relu != 0 selects it.  A NaN stays NaN (the test is
+ * "below zero", which a NaN is not).
+ * [P2] §4.4 (multi-output fusion): one pass over the input yields several
+ * outputs, with mean and var computed together as its example.  Besides y,
+ * any of these may be requested (NULL = not wanted):
+ *   sum  [rows, hidden]  the pre-norm sum v = x + residual (the residual
+ *                        stream a pre-norm block carries on);
+ *   mean [rows]          mean of v;
+ *   var  [rows]          population variance of v (without eps).
+ * The statistics are those of oracle_add_layernorm, computed the same way.
+ */
+void oracle_add_layernorm_ex(const double *x, const double *residual,
+                             const double *gamma, const double *beta, double *y,
+                             double *sum, double *mean, double *var,
+                             int64_t rows, int64_t hidden, double eps, int relu)
+{
+    int64_t row;
+#pragma omp parallel for schedule(static)
+    for (row = 0; row < rows; row++) {
+        const double *xr = x + row * hidden;
+        const double *rr = residual ? residual + row * hidden : NULL;
+        double *v = y + row * hidden; /* holds x + r until overwritten */
+        double s = 0.0, q = 0.0, mu, std;
+        int64_t i;
+
+        for (i = 0; i < hidden; i++)
+            v[i] = rr ? xr[i] + rr[i] : xr[i];
+        if (sum)
+            for (i = 0; i < hidden; i++)
+                sum[row * hidden + i] = v[i];
+
+        for (i = 0; i < hidden; i++)
+            s += v[i];
+        mu = s / (double)hidden;
+
+        for (i = 0; i < hidden; i++)
+            q += (v[i] - mu) * (v[i] - mu);
+        std = sqrt(q / (double)hidden + eps);
+        if (mean)
+            mean[row] = mu;
+        if (var)
+            var[row] = q / (double)hidden;
+
+        for (i = 0; i < hidden; i++) {
+            v[i] = gamma[i] * (v[i] - mu) / std + beta[i];
+            if (relu && v[i] < 0.0)
+                v[i] = 0.0;
+        }
+    }
+}
+
+/*
  * Gaussian error linear unit, exact (erf) form: GELU(t) = t * Phi(t) with
  * Phi the standard normal CDF, Phi(t) = (1 + erf(t / sqrt 2)) / 2.
  * The pages name GELU without defining it; the erf form is the one the

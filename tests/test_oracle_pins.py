@@ -49,6 +49,53 @@ def test_ln_two_element_hand_formula():
     np.testing.assert_allclose(y[0], [-s, s], rtol=0, atol=1e-15)
 
 
+# LayerNorm variants ([P1] §二.1 LayerNorm + ReLU; [P2] §4.4 multi-output: mean and var)
+
+@pytest.mark.parametrize("n,a,d", [(7, -3.0, 0.5), (64, 10.0, -0.25), (4096, 0.0, 1.0)])
+def test_ln_ex_stats_of_arithmetic_progression(n, a, d):
+    # v_i = a + d i: mean a + d (n-1)/2, population variance d^2 (n^2 - 1) / 12 (closed forms;
+    # an n-1 divisor or a missing mean term fails)
+    i = np.arange(n, dtype=np.float64)
+    v = a + d * i
+    h = np.round(np.sin(i) * 64) / 64  # dyadic split, x + r exact
+    y, sm, mean, var = oracle.add_layernorm_ex((v - h)[None, :], h[None, :], np.ones(n), np.zeros(n), EPS)
+    mu, sig2 = a + d * (n - 1) / 2, d * d * (n * n - 1) / 12
+    assert abs(mean[0] - mu) <= 1e-12 * max(1.0, abs(mu))
+    assert abs(var[0] - sig2) <= 1e-12 * sig2
+    np.testing.assert_array_equal(sm[0], v)  # the pre-norm sum, exactly x + r
+    np.testing.assert_allclose(y[0], (v - mu) / math.sqrt(sig2 + EPS), rtol=0, atol=1e-11)
+
+
+def test_ln_ex_relu_closed_form():
+    # symmetric row: the lower half of the normalised values is negative and clamps to 0, the
+    # upper half keeps the closed form; beta shifts the threshold column by column
+    n = 10
+    i = np.arange(n, dtype=np.float64)
+    v = (i - 4.5)[None, :]
+    sig2 = (n * n - 1) / 12
+    xhat = (i - 4.5) / math.sqrt(sig2 + EPS)
+    y, _, _, _ = oracle.add_layernorm_ex(v, None, np.ones(n), np.zeros(n), EPS, relu=True)
+    np.testing.assert_allclose(y[0], np.where(i < 5, 0.0, xhat), rtol=0, atol=1e-14)
+    beta = np.full(n, 0.3)
+    y, _, _, _ = oracle.add_layernorm_ex(v, None, np.full(n, 2.0), beta, EPS, relu=True)
+    np.testing.assert_allclose(y[0], np.maximum(2.0 * xhat + 0.3, 0.0), rtol=0, atol=1e-14)
+    assert (y[0][:5] == 0).all() and y[0][5] > 0  # 2 * (-0.5 / sqrt(8.25)) + 0.3 < 0 still
+
+
+def test_ln_ex_matches_plain_ln_and_keeps_nan():
+    rng = np.random.default_rng(5)
+    x, r = rng.standard_normal((6, 48)), rng.standard_normal((6, 48))
+    g, b = rng.uniform(0.5, 1.5, 48), rng.normal(0, 0.1, 48)
+    y, _, _, _ = oracle.add_layernorm_ex(x, r, g, b, EPS)
+    np.testing.assert_array_equal(y, oracle.add_layernorm(x, r, g, b, EPS))
+    yr, _, _, _ = oracle.add_layernorm_ex(x, r, g, b, EPS, relu=True)
+    np.testing.assert_array_equal(yr, np.where(y < 0, 0.0, y))
+    x[2, 7] = np.nan
+    yr, _, mean, var = oracle.add_layernorm_ex(x, r, g, b, EPS, relu=True)
+    assert np.isnan(yr[2]).all() and np.isnan(mean[2]) and np.isnan(var[2])
+    assert not np.isnan(yr[[0, 1, 3, 4, 5]]).any()
+
+
 def test_ln_gamma_beta_indexed_by_column():
     n = 16
     v = _alternating(n, 1.0, 0.0)[None, :]
