@@ -210,6 +210,34 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
         record("add_layernorm_f32_64x768", w.op, w.shape, w.dtype, True, ev, n_launch,
                {"note": "596 KB, cache resident and launch-latency bound; GB/s not an HBM figure"})
 
+        # LayerNorm variants at the headline shape: ReLU, pre-norm sum and per-row statistics
+        w = synth.WORKLOADS[HEADLINE]
+        d = w.inputs()
+        gamma, beta = d["gamma"].cuda(), d["beta"].cuda()
+        sets = rotation_sets(torch, {"x": d["x"], "r": d["residual"]}, {"y": d["x"], "s": d["x"]}, ROTATE_BYTES)
+        stats = [(torch.empty(w.shape[0], device="cuda"), torch.empty(w.shape[0], device="cuda")) for _ in sets]
+
+        def ln_ex(i):
+            s, (m, v) = sets[i % len(sets)], stats[i % len(sets)]
+            api.fuse_add_layernorm_ex(s["x"], s["r"], gamma, beta, d["eps"], relu=True, y=s["y"], sum_out=s["s"],
+                                      mean_out=m, var_out=v)
+        _, ev = time_launches(torch, stream, ln_ex, n_launch)
+        record("add_layernorm_ex_relu_sum_stats_f16_2048x4096", "add_layernorm_ex", w.shape, w.dtype, True, ev,
+               n_launch, {"note": "LayerNorm+ReLU with the pre-norm sum and fp32 mean/var also stored"})
+        del sets, stats
+
+        # bf16 I/O at the headline shape
+        xb, rb = d["x"].bfloat16(), d["residual"].bfloat16()
+        gb, bb = d["gamma"].bfloat16().cuda(), d["beta"].bfloat16().cuda()
+        sets = rotation_sets(torch, {"x": xb, "r": rb}, {"y": xb}, ROTATE_BYTES)
+
+        def ln_bf16(i):
+            s = sets[i % len(sets)]
+            api.fuse_add_layernorm(s["x"], s["r"], gb, bb, d["eps"], y=s["y"])
+        _, ev = time_launches(torch, stream, ln_bf16, n_launch)
+        record("add_layernorm_bf16_2048x4096", "add_layernorm", w.shape, "bf16", True, ev, n_launch)
+        del sets
+
         w = synth.WORKLOADS["gelu_f16_2048x4096"]
         d = w.inputs()
         bias = d["bias"].cuda()

@@ -82,6 +82,30 @@ fuse_status_t fuse_add_layernorm(const void *x, const void *residual, const void
                                  float eps, fuse_dtype_t dtype, void *stream);
 
 /*
+ * Variants of the fused ResidualAdd + LayerNorm, same single pass over HBM:
+ *   y = gamma * (v - mean) / sqrt(var + eps) + beta, then y = max(y, 0) with FUSE_LN_RELU,
+ * plus optional extra outputs of the same pass.
+ * [P1] §二.1 lists "LayerNorm + ReLU" as one vertical fusion (the activation is applied in
+ * registers before the single store).  [P2] §4.4 multi-output fusion: one pass over the input
+ * yields several outputs, its example being mean and var computed together.
+ *
+ *   x, residual, gamma, beta, y, eps : as fuse_add_layernorm.
+ *   sum_out  : [rows, hidden] in the I/O type, or NULL: the pre-norm sum v = x + residual (the
+ *              residual stream of a pre-norm block).  May equal x or residual (in place); must
+ *              not overlap y, gamma or beta.
+ *   mean_out : [rows] fp32, or NULL: mean of v.
+ *   var_out  : [rows] fp32, or NULL: population variance of v (eps not added).
+ *              The statistics buffers must not overlap each other or any tensor argument.
+ *   flags    : 0 or FUSE_LN_RELU; any other bit is FUSE_ERR_BAD_VALUE.  A NaN stays NaN
+ *              through the ReLU.
+ */
+#define FUSE_LN_RELU 1u
+fuse_status_t fuse_add_layernorm_ex(const void *x, const void *residual, const void *gamma,
+                                    const void *beta, void *y, void *sum_out, float *mean_out,
+                                    float *var_out, int64_t rows, int64_t hidden, float eps,
+                                    unsigned flags, fuse_dtype_t dtype, void *stream);
+
+/*
  * Fused BiasAdd + GELU + ResidualAdd, one pass over HBM.
  *   t = x + bias[col];  g = t * Phi(t) = t/2 * (1 + erf(t / sqrt 2));  y = g + residual.
  * [P3] intro diagram and §1: the three kernels BiasAdd, GELU and Residual become one kernel

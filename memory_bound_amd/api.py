@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfuse.so"
 FUSE_F32, FUSE_F16, FUSE_BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: FUSE_F32, torch.float16: FUSE_F16, torch.bfloat16: FUSE_BF16}
 
+FUSE_LN_RELU = 1
+
 FUSE_OP_ADD_LAYERNORM, FUSE_OP_BIAS_GELU_RESIDUAL, FUSE_OP_SOFTMAX_ROWS, FUSE_OP_SWIGLU = 0, 1, 2, 3
 
 STATUS = {0: "FUSE_OK", 1: "FUSE_ERR_NULL_PTR", 2: "FUSE_ERR_BAD_SHAPE", 3: "FUSE_ERR_BAD_DTYPE",
@@ -27,7 +29,7 @@ STATUS = {0: "FUSE_OK", 1: "FUSE_ERR_NULL_PTR", 2: "FUSE_ERR_BAD_SHAPE", 3: "FUS
 
 # Every symbol include/libfuse.h declares.
 EXPORTS = [
-    "fuse_add_layernorm", "fuse_bias_gelu_residual", "fuse_softmax_rows", "fuse_swiglu_dualgemm",
+    "fuse_add_layernorm", "fuse_add_layernorm_ex", "fuse_bias_gelu_residual", "fuse_softmax_rows", "fuse_swiglu_dualgemm",
     "fuse_unfused_workspace_bytes", "fuse_unfused_add_layernorm", "fuse_unfused_bias_gelu_residual",
     "fuse_unfused_softmax_rows", "fuse_unfused_swiglu", "fuse_copy", "fuse_status_string",
     "fuse_last_hip_error", "fuse_version",
@@ -59,6 +61,7 @@ def load() -> ctypes.CDLL:
     vp, i64, f32, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
     sig = {
         "fuse_add_layernorm": [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp],
+        "fuse_add_layernorm_ex": [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, ctypes.c_uint, i32, vp],
         "fuse_bias_gelu_residual": [vp, vp, vp, vp, i64, i64, i32, vp],
         "fuse_softmax_rows": [vp, vp, i64, i64, f32, i32, vp],
         "fuse_swiglu_dualgemm": [vp, vp, vp, vp, i64, i64, i64, i32, vp],
@@ -152,6 +155,35 @@ def fuse_add_layernorm(x, residual, gamma, beta, eps=1e-5, y=None, stream=None):
     _ok(load().fuse_add_layernorm(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y), rows, hidden,
                                   float(eps), _dt(x), _stream(stream)), "fuse_add_layernorm")
     return y
+
+
+def fuse_add_layernorm_ex(x, residual, gamma, beta, eps=1e-5, relu=False, want_sum=False, want_stats=False,
+                          y=None, sum_out=None, mean_out=None, var_out=None, stream=None):
+    """LayerNorm variants in one pass: y (clamped at 0 when relu) and, on request, the pre-norm
+    sum x + residual and the per-row fp32 mean and population variance.  Returns
+    (y, sum, mean, var), None for an output not requested."""
+    rows, hidden = _rows_cols(x)
+    _check(x, "x")
+    _check(residual, "residual", x.dtype, x.shape)
+    _check(gamma, "gamma", x.dtype, (hidden,))
+    _check(beta, "beta", x.dtype, (hidden,))
+    if y is None:
+        y = torch.empty_like(x)
+    if want_sum and sum_out is None:
+        sum_out = torch.empty_like(x)
+    if want_stats and mean_out is None:
+        mean_out = torch.empty(rows, dtype=torch.float32, device=x.device)
+    if want_stats and var_out is None:
+        var_out = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(y, "y", x.dtype, x.shape)
+    _check(sum_out, "sum_out", x.dtype, x.shape)
+    _check(mean_out, "mean_out", torch.float32, (rows,))
+    _check(var_out, "var_out", torch.float32, (rows,))
+    _ok(load().fuse_add_layernorm_ex(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(sum_out),
+                                     _ptr(mean_out), _ptr(var_out), rows, hidden, float(eps),
+                                     FUSE_LN_RELU if relu else 0, _dt(x), _stream(stream)),
+        "fuse_add_layernorm_ex")
+    return y, sum_out, mean_out, var_out
 
 
 def fuse_bias_gelu_residual(x, bias, residual, y=None, stream=None):

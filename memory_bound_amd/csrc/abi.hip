@@ -152,6 +152,43 @@ fuse_status_t fuse_add_layernorm(const void* x, const void* residual, const void
     }));
 }
 
+fuse_status_t fuse_add_layernorm_ex(const void* x, const void* residual, const void* gamma,
+                                    const void* beta, void* y, void* sum_out, float* mean_out,
+                                    float* var_out, int64_t rows, int64_t hidden, float eps,
+                                    unsigned flags, fuse_dtype_t dt, void* stream) {
+    size_t tb = 0;
+    bool vec = false;
+    fuse_status_t st = check_add_layernorm(x, residual, gamma, beta, y, rows, hidden, eps, dt, &tb, &vec);
+    if (st != FUSE_OK) return st;
+    if (flags & ~(unsigned)FUSE_LN_RELU) return FUSE_ERR_BAD_VALUE;
+    if (rows == 0) return FUSE_OK;
+    const int e = elem_bytes(dt);
+    const size_t pb = (size_t)hidden * e, sb = (size_t)rows * sizeof(float);
+    if (sum_out) {
+        if (!elem_aligned(sum_out, e)) return FUSE_ERR_MISALIGNED;
+        if (bad_alias(sum_out, tb, x, tb) || bad_alias(sum_out, tb, residual, tb) || overlaps(sum_out, tb, y, tb) ||
+            overlaps(sum_out, tb, gamma, pb) || overlaps(sum_out, tb, beta, pb))
+            return FUSE_ERR_ALIAS;
+        if (!aligned16(sum_out)) vec = false;
+    }
+    const void* tensors[6] = {x, residual, y, sum_out, gamma, beta};
+    const size_t sizes[6] = {tb, tb, tb, tb, pb, pb};
+    float* const stats[2] = {mean_out, var_out};
+    for (float* p : stats) {
+        if (!p) continue;
+        if (!elem_aligned(p, 4)) return FUSE_ERR_MISALIGNED;
+        for (int i = 0; i < 6; i++)
+            if (overlaps(p, sb, tensors[i], tensors[i] ? sizes[i] : 0)) return FUSE_ERR_ALIAS;
+    }
+    if (overlaps(mean_out, mean_out ? sb : 0, var_out, var_out ? sb : 0)) return FUSE_ERR_ALIAS;
+    const fuse::RowPlan plan = fuse::plan_row(hidden, e, vec, env_int("FUSE_ROW_WPR"));
+    return hip_status(by_dtype(dt, [&]<fuse::DT D>() {
+        return fuse::launch_add_layernorm_ex<D>(x, residual, gamma, beta, y, sum_out, mean_out, var_out,
+                                                (flags & FUSE_LN_RELU) != 0, rows, (int)hidden, eps, plan,
+                                                (hipStream_t)stream);
+    }));
+}
+
 // ------------------------------------------------------------------------------------------------
 // BiasAdd + GELU + Residual
 // ------------------------------------------------------------------------------------------------

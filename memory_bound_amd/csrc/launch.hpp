@@ -29,6 +29,10 @@ hipError_t launch_add_layernorm(const void* x, const void* res, const void* gamm
                                 void* y, int64_t rows, int hidden, float eps, RowPlan plan,
                                 hipStream_t stream);
 template <DT D>
+hipError_t launch_add_layernorm_ex(const void* x, const void* res, const void* gamma, const void* beta,
+                                   void* y, void* sum, float* mean, float* var, bool relu, int64_t rows,
+                                   int hidden, float eps, RowPlan plan, hipStream_t stream);
+template <DT D>
 hipError_t launch_softmax_rows(const void* x, void* y, int64_t rows, int cols, float scale,
                                RowPlan plan, hipStream_t stream);
 template <DT D>

@@ -97,12 +97,25 @@ template <DT D, bool VECP, int NV, int WPR> struct RowSlice {
 // sweep over the registers, not over HBM); y = (v - mean) * rstd * gamma + beta with
 // rstd = 1 / sqrt(var + eps).  HAS_RES = false gives the plain LayerNorm (the second kernel of
 // the unfused chain).
+//
+// EX adds the variants: y clamped below at 0 (LayerNorm + ReLU), and any of the pre-norm sum v
+// (stored in the I/O type) and the per-row mean and population variance (fp32) as extra
+// outputs.  A missing output gets an empty buffer resource, so its stores are dropped without a
+// branch.
 // ------------------------------------------------------------------------------------------------
-template <DT D, bool VECP, int NV, int WPR, bool HAS_RES>
-__global__ void __launch_bounds__(RowShape<WPR>::THREADS)
-add_layernorm_kernel(const typename Elem<D>::T* x, const typename Elem<D>::T* res,
-                     const typename Elem<D>::T* gamma, const typename Elem<D>::T* beta,
-                     typename Elem<D>::T* y, int64_t rows, int hidden, float eps) {
+template <class T> struct LnExtra {
+    T* sum;       // [rows, hidden] pre-norm sum, or null
+    float* mean;  // [rows], or null
+    float* var;   // [rows], or null
+    int relu;     // nonzero: y = max(y, 0) (a NaN stays NaN)
+};
+
+template <DT D, bool VECP, int NV, int WPR, bool HAS_RES, bool EX>
+__device__ __forceinline__ void add_layernorm_row(const typename Elem<D>::T* x, const typename Elem<D>::T* res,
+                                                  const typename Elem<D>::T* gamma,
+                                                  const typename Elem<D>::T* beta, typename Elem<D>::T* y,
+                                                  int64_t rows, int hidden, float eps,
+                                                  const LnExtra<typename Elem<D>::T>& ex) {
     using S = RowSlice<D, VECP, NV, WPR>;
     constexpr int V = S::V;
     // Keep gamma/beta loads in flight with x and r when the slice is small; otherwise load
@@ -120,6 +133,7 @@ add_layernorm_kernel(const typename Elem<D>::T* x, const typename Elem<D>::T* re
     const rsrc_t ry = make_rsrc(y + row * hidden, row_bytes);
     const rsrc_t rg = make_rsrc(gamma, par_bytes);
     const rsrc_t rb = make_rsrc(beta, par_bytes);
+    const rsrc_t rsum = make_rsrc(EX && ex.sum ? ex.sum + row * hidden : y, EX && ex.sum ? row_bytes : 0u);
 
     // All loads of the row are issued here.  gamma and beta stay raw until the normalisation.
     // Left alone the compiler sinks their loads below the reductions, which adds a cache round
@@ -151,6 +165,7 @@ add_layernorm_kernel(const typename Elem<D>::T* x, const typename Elem<D>::T* re
         }
 #pragma unroll
         for (int k = 0; k < V; k++) sum += v[j][k];  // zeros outside the row
+        if constexpr (EX) s.template store<AUX_STREAM>(rsum, j, v[j]);
     }
     if constexpr (PREFETCH_AFFINE) {
         uint32_t dep = 0;
@@ -175,6 +190,14 @@ add_layernorm_kernel(const typename Elem<D>::T* x, const typename Elem<D>::T* re
     }
     sq = row_allreduce<WPR>(sq, SumOp{}, lds_sq);
     const float rstd = 1.0f / sqrtf(sq / (float)hidden + eps);
+    if constexpr (EX) {
+        // one lane of the row's first wave writes the statistics
+        const bool leader = (threadIdx.x & 63) == 0 && (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % WPR) == 0;
+        const rsrc_t rm = make_rsrc(ex.mean ? ex.mean + row : (float*)y, ex.mean && row < rows ? 4u : 0u);
+        const rsrc_t rv = make_rsrc(ex.var ? ex.var + row : (float*)y, ex.var && row < rows ? 4u : 0u);
+        bstore_b32(rm, leader ? 0u : OOB, __builtin_bit_cast(uint32_t, mean));
+        bstore_b32(rv, leader ? 0u : OOB, __builtin_bit_cast(uint32_t, sq / (float)hidden));
+    }
 
 #pragma unroll
     for (int j = 0; j < NV; j++) {
@@ -191,8 +214,30 @@ add_layernorm_kernel(const typename Elem<D>::T* x, const typename Elem<D>::T* re
         float o[V];
 #pragma unroll
         for (int k = 0; k < V; k++) o[k] = fmaf((v[j][k] - mean) * rstd, g[j][k], b[j][k]);
+        if constexpr (EX) {
+#pragma unroll
+            for (int k = 0; k < V; k++) o[k] = (ex.relu && o[k] < 0.0f) ? 0.0f : o[k];
+        }
         s.template store<AUX_STREAM>(ry, j, o);
     }
+}
+
+template <DT D, bool VECP, int NV, int WPR, bool HAS_RES>
+__global__ void __launch_bounds__(RowShape<WPR>::THREADS)
+add_layernorm_kernel(const typename Elem<D>::T* x, const typename Elem<D>::T* res,
+                     const typename Elem<D>::T* gamma, const typename Elem<D>::T* beta,
+                     typename Elem<D>::T* y, int64_t rows, int hidden, float eps) {
+    add_layernorm_row<D, VECP, NV, WPR, HAS_RES, false>(x, res, gamma, beta, y, rows, hidden, eps,
+                                                        LnExtra<typename Elem<D>::T>{nullptr, nullptr, nullptr, 0});
+}
+
+template <DT D, bool VECP, int NV, int WPR, bool HAS_RES>
+__global__ void __launch_bounds__(RowShape<WPR>::THREADS)
+add_layernorm_ex_kernel(const typename Elem<D>::T* x, const typename Elem<D>::T* res,
+                        const typename Elem<D>::T* gamma, const typename Elem<D>::T* beta,
+                        typename Elem<D>::T* y, int64_t rows, int hidden, float eps,
+                        LnExtra<typename Elem<D>::T> ex) {
+    add_layernorm_row<D, VECP, NV, WPR, HAS_RES, true>(x, res, gamma, beta, y, rows, hidden, eps, ex);
 }
 
 // ------------------------------------------------------------------------------------------------

@@ -66,6 +66,29 @@ hipError_t launch_add_layernorm(const void* x, const void* res, const void* gamm
 }
 
 template <DT D>
+hipError_t launch_add_layernorm_ex(const void* x, const void* res, const void* gamma, const void* beta,
+                                   void* y, void* sum, float* mean, float* var, bool relu, int64_t rows,
+                                   int hidden, float eps, RowPlan plan, hipStream_t stream) {
+    using T = typename Elem<D>::T;
+    hipError_t err = hipErrorInvalidValue;
+    const LnExtra<T> ex{(T*)sum, mean, var, relu ? 1 : 0};
+    auto go = [&]<bool VECP, int NV, int WPR>() {
+        const dim3 grid((unsigned)detail::row_blocks<WPR>(rows)), block(RowShape<WPR>::THREADS);
+        if (res)
+            hipLaunchKernelGGL((add_layernorm_ex_kernel<D, VECP, NV, WPR, true>), grid, block, 0, stream,
+                               (const T*)x, (const T*)res, (const T*)gamma, (const T*)beta, (T*)y,
+                               rows, hidden, eps, ex);
+        else
+            hipLaunchKernelGGL((add_layernorm_ex_kernel<D, VECP, NV, WPR, false>), grid, block, 0, stream,
+                               (const T*)x, (const T*)nullptr, (const T*)gamma, (const T*)beta, (T*)y,
+                               rows, hidden, eps, ex);
+        err = hipGetLastError();
+    };
+    if (!detail::with_plan(plan, go)) return hipErrorInvalidValue;
+    return err;
+}
+
+template <DT D>
 hipError_t launch_softmax_rows(const void* x, void* y, int64_t rows, int cols, float scale,
                                RowPlan plan, hipStream_t stream) {
     using T = typename Elem<D>::T;
@@ -144,6 +167,9 @@ hipError_t launch_softmax_unfused(const void* x, void* y, int64_t rows, int cols
     template hipError_t launch_add_layernorm<D>(const void*, const void*, const void*,       \
                                                       const void*, void*, int64_t, int, float,     \
                                                       RowPlan, hipStream_t);                       \
+    template hipError_t launch_add_layernorm_ex<D>(const void*, const void*, const void*,    \
+                                                   const void*, void*, void*, float*, float*, bool, \
+                                                   int64_t, int, float, RowPlan, hipStream_t);     \
     template hipError_t launch_softmax_rows<D>(const void*, void*, int64_t, int, float,      \
                                                      RowPlan, hipStream_t);                        \
     template hipError_t launch_ew<D>(EwOp, bool, const void*, const void*, const void*,      \

@@ -29,6 +29,15 @@ def add_layernorm_bytes(rows: int, hidden: int, dtype: str, fused: bool = True) 
     return _t("fused" if fused else "unfused", passes * t, 2 * hidden * e)
 
 
+def add_layernorm_ex_bytes(rows: int, hidden: int, dtype: str, fused: bool = True) -> dict:
+    """The LayerNorm variants with every extra output: the fused Add+LN traffic plus the stored
+    pre-norm sum (one more tensor pass) and the fp32 mean and variance (8 bytes per row).  The
+    ReLU adds no traffic."""
+    d = add_layernorm_bytes(rows, hidden, dtype, fused)
+    e = ELEM_BYTES[dtype]
+    return _t("fused", d["tensor_bytes"] + rows * hidden * e, d["param_bytes"], 8 * rows)
+
+
 def bias_gelu_residual_bytes(rows: int, hidden: int, dtype: str, fused: bool = True) -> dict:
     """Fused: read x and r, write y, read bias.  Unfused: bias kernel (read x, write t), GELU
     kernel (read t, write g), residual kernel (read g and r, write y): 7 tensor passes."""
@@ -66,6 +75,8 @@ def swiglu_flops(M: int, N: int, K: int) -> int:
 def workload_work(op: str, shape: tuple, dtype: str, fused: bool = True) -> dict:
     if op == "add_layernorm":
         return add_layernorm_bytes(*shape, dtype, fused)
+    if op == "add_layernorm_ex":
+        return add_layernorm_ex_bytes(*shape, dtype, fused)
     if op == "bias_gelu_residual":
         return bias_gelu_residual_bytes(*shape, dtype, fused)
     if op == "softmax_rows":

@@ -88,6 +88,35 @@ def test_add_layernorm_validation(lib):
     assert H
 
 
+def ln_ex(lib, x=P, r=2 * P, g=3 * P, b=4 * P, y=5 * P, s=6 * P, m=7 * P, var=8 * P, rows=4, hidden=64,
+          eps=1e-5, flags=1, dt=F16):
+    return lib.fuse_add_layernorm_ex(v(x), v(r), v(g), v(b), v(y), v(s), v(m), v(var), rows, hidden, eps, flags,
+                                     dt, None)
+
+
+def test_add_layernorm_ex_validation(lib):
+    # the checks of the plain entry point first
+    assert ln_ex(lib, x=0) == NULL
+    assert ln_ex(lib, hidden=16385) == UNSUP
+    assert ln_ex(lib, eps=float("nan")) == VALUE
+    assert ln_ex(lib, y=P + 2) == ALIAS
+    # then the variants' own arguments
+    assert ln_ex(lib, flags=2) == VALUE
+    assert ln_ex(lib, flags=0xFFFFFFFF) == VALUE
+    assert ln_ex(lib, s=5 * P) == ALIAS          # sum_out equal to y
+    assert ln_ex(lib, s=5 * P + 128) == ALIAS    # sum_out overlapping y
+    assert ln_ex(lib, s=3 * P) == ALIAS          # sum_out on gamma
+    assert ln_ex(lib, s=P + 64) == ALIAS         # sum_out partially over x
+    assert ln_ex(lib, s=6 * P + 1) == MISAL
+    assert ln_ex(lib, m=7 * P + 2) == MISAL
+    assert ln_ex(lib, m=P) == ALIAS              # mean_out inside x
+    assert ln_ex(lib, var=5 * P + 256) == ALIAS  # var_out inside y
+    assert ln_ex(lib, var=7 * P + 8) == ALIAS    # var_out overlapping mean_out
+    assert ln_ex(lib, m=6 * P) == ALIAS          # mean_out inside sum_out
+    assert ln_ex(lib, rows=0) == OK              # no-op, nothing launched
+    assert ln_ex(lib, rows=0, flags=4) == VALUE  # flags are checked even for an empty call
+
+
 def test_bias_gelu_residual_validation(lib):
     def call(x=P, bias=2 * P, r=3 * P, y=4 * P, rows=4, hidden=64, dt=F16):
         return lib.fuse_bias_gelu_residual(v(x), v(bias), v(r), v(y), rows, hidden, dt, None)

@@ -103,6 +103,77 @@ def test_add_layernorm_misaligned_pointers():
     assert_close(y, ref, "f16", "misaligned")
 
 
+# LayerNorm variants: ReLU epilogue, pre-norm sum, per-row mean and variance
+
+_FROM_D = object()
+
+
+def _check_ln_ex(outs, d, relu, kind, what, residual=_FROM_D):
+    y, sm, mean, var = outs
+    x = d["x"]
+    residual = d["residual"] if residual is _FROM_D else residual
+    ry, rs, rm, rv = oracle.add_layernorm_ex(x, residual, d["gamma"], d["beta"], np.float32(d["eps"]), relu)
+    assert_close(y, ry, kind, f"{what} y")
+    if sm is not None:
+        # x + r is exact in fp32 for fp16/bf16 inputs and correctly rounded for fp32 ones, so
+        # the stored sum is the round-to-nearest-even of the exact sum: bit-exact
+        exp = oracle.round_to(rs, kind)
+        got = sm.float().cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, exp), f"{what} sum: max diff {np.nanmax(np.abs(got - exp))}"
+    if mean is not None:
+        # fp32 tree sums of H terms: allow 1e-5 of the mean magnitude, 2e-5 of the variance
+        absmean = np.abs(oracle.f64(x) + (oracle.f64(residual) if residual is not None else 0)).mean(axis=1)
+        gm, gv = mean.cpu().numpy().astype(np.float64), var.cpu().numpy().astype(np.float64)
+        assert (np.abs(gm - rm) <= 1e-5 * absmean + 1e-30).all(), f"{what} mean: {np.abs(gm - rm).max()}"
+        assert (np.abs(gv - rv) <= 2e-5 * rv + 1e-30).all(), f"{what} var: {(np.abs(gv - rv) / rv).max()}"
+
+
+@pytest.mark.parametrize("rows,hidden,dtype", [s for s in LN_SHAPES if s[1] != 1])
+@pytest.mark.parametrize("relu", [False, True])
+def test_add_layernorm_ex_parity(rows, hidden, dtype, relu):
+    announce(f"add_layernorm_ex {rows}x{hidden} {dtype} relu={relu}")
+    d = synth.add_layernorm_inputs(rows, hidden, dtype, seed=rows * 17 + hidden)
+    g = cuda(d)
+    outs = api.fuse_add_layernorm_ex(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"], relu=relu,
+                                     want_sum=True, want_stats=True)
+    _check_ln_ex(outs, d, relu, KIND[dtype], f"ln_ex {rows}x{hidden} {dtype} relu={relu}")
+
+
+def test_add_layernorm_ex_workload_full():
+    w = synth.WORKLOADS["addln_f16_2048x4096"]
+    announce("add_layernorm_ex workload 2048x4096 fp16, relu and every output")
+    d = w.inputs()
+    g = cuda(d)
+    outs = api.fuse_add_layernorm_ex(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"], relu=True,
+                                     want_sum=True, want_stats=True)
+    _check_ln_ex(outs, d, True, "f16", "ln_ex workload")
+    # the same y as the plain fused kernel before the clamp, and only the requested outputs
+    y0 = api.fuse_add_layernorm(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"])
+    assert torch.equal(outs[0], torch.where(y0 < 0, torch.zeros_like(y0), y0))
+    y1, s1, m1, v1 = api.fuse_add_layernorm_ex(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"])
+    assert torch.equal(y1, y0) and s1 is None and m1 is None and v1 is None
+    _, s2, m2, v2 = api.fuse_add_layernorm_ex(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"], want_stats=True)
+    assert s2 is None and torch.equal(m2, outs[2]) and torch.equal(v2, outs[3])
+
+
+def test_add_layernorm_ex_inplace_sum_and_nan():
+    announce("add_layernorm_ex sum_out over x, NaN row, no residual")
+    d = synth.add_layernorm_inputs(24, 1024, "bf16", seed=41)
+    d["x"][5, 100] = float("nan")
+    g = cuda(d)
+    x = g["x"].clone()
+    y, sm, mean, var = api.fuse_add_layernorm_ex(x, g["residual"], g["gamma"], g["beta"], d["eps"], relu=True,
+                                                 sum_out=x, want_stats=True)
+    assert sm is x
+    ok = [i for i in range(24) if i != 5]
+    dd = {k: (v[ok] if torch.is_tensor(v) and v.dim() == 2 else v) for k, v in d.items()}
+    _check_ln_ex((y[ok], sm[ok], mean[ok], var[ok]), dd, True, "bf16", "ln_ex in place")
+    assert torch.isnan(y[5].float()).all() and torch.isnan(mean[5]) and torch.isnan(var[5])
+    outs = api.fuse_add_layernorm_ex(g["x"][ok].contiguous(), None, g["gamma"], g["beta"], d["eps"],
+                                     want_sum=True, want_stats=True)
+    _check_ln_ex(outs, dd, False, "bf16", "ln_ex no residual", residual=None)
+
+
 def test_add_layernorm_large_mean_rows():
     # mean 1e4, spread 1: the statistics must not lose the variance to cancellation
     announce("add_layernorm mean 1e4 fp32")
