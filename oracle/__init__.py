@@ -62,12 +62,14 @@ def _load():
                                             ctypes.c_int]
     lib.oracle_bias_gelu_residual.argtypes = [dp, dp, dp, dp, i64, i64]
     lib.oracle_softmax_rows.argtypes = [dp, dp, i64, i64, ctypes.c_double]
+    lib.oracle_cumsum_scale_rows.argtypes = [dp, dp, i64, i64, ctypes.c_double]
     lib.oracle_matmul.argtypes = [dp, dp, dp, i64, i64, i64]
     lib.oracle_swiglu.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64]
     lib.oracle_round.argtypes = [dp, dp, i64, ctypes.c_int]
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
     for name in ("oracle_add_layernorm", "oracle_add_layernorm_ex", "oracle_bias_gelu_residual", "oracle_softmax_rows",
+                 "oracle_cumsum_scale_rows",
                  "oracle_matmul", "oracle_swiglu", "oracle_round"):
         getattr(lib, name).restype = None
     _lib = lib
@@ -152,6 +154,15 @@ def softmax_rows(x, scale: float) -> np.ndarray:
     return y
 
 
+def cumsum_scale_rows(x, scale: float) -> np.ndarray:
+    """y = scale * inclusive prefix sum along each row; [P2] §4.4 (Cumsum + Scale)."""
+    x = f64(x)
+    rows, cols = x.shape
+    y = np.empty_like(x)
+    _load().oracle_cumsum_scale_rows(_p(x), _p(y), rows, cols, float(scale))
+    return y
+
+
 def matmul(a, b) -> np.ndarray:
     """Plain row-major product a[M,K] . b[K,N] with ascending-k sums."""
     a, b = f64(a), f64(b)
@@ -219,6 +230,11 @@ def softmax_rows_unfused(x, scale: float, kind: str) -> np.ndarray:
     e = np.exp(z - m)
     s = e.sum(axis=1, keepdims=True)
     return round_to(e, kind) / s
+
+
+def cumsum_scale_rows_unfused(x, scale: float, kind: str) -> np.ndarray:
+    """Scan kernel stores the prefix sums S in the I/O type; scale kernel reads S: y = scale * S."""
+    return float(scale) * round_to(cumsum_scale_rows(x, 1.0), kind)
 
 
 def swiglu_unfused(a, b1, b2, kind: str) -> np.ndarray:

@@ -162,6 +162,30 @@ void oracle_bias_gelu_residual(const double *x, const double *bias,
 }
 
 /*
+ * Row prefix sum followed by a scale (the "Scan-Elementwise" pattern of
+ * [P2] §4.4, example "Cumsum + Scale"; [P2] §4.3 on scans needing the
+ * prefix sums of what precedes each element).
+ *
+ * y[row][j] = scale * (x[row][0] + ... + x[row][j]): the inclusive running
+ * sum along the row, accumulated left to right, then multiplied by the
+ * scalar.
+ */
+void oracle_cumsum_scale_rows(const double *x, double *y, int64_t rows,
+                              int64_t cols, double scale)
+{
+    int64_t row;
+#pragma omp parallel for schedule(static)
+    for (row = 0; row < rows; row++) {
+        double run = 0.0;
+        int64_t j;
+        for (j = 0; j < cols; j++) {
+            run += x[row * cols + j];
+            y[row * cols + j] = scale * run;
+        }
+    }
+}
+
+/*
  * Row softmax of scaled scores.
  *
  * [P1] §二.1 lists "Softmax + Scale" as one vertical fusion: z = scale * x.

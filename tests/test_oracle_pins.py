@@ -268,6 +268,36 @@ def test_softmax_matches_torch_fp64():
 
 
 # ------------------------------------------------------------------------------------------------
+# Row cumsum + scale ([P2] §4.4 Scan-Elementwise)
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 2, 7, 768, 4096])
+def test_cumsum_closed_forms(n):
+    j = np.arange(n, dtype=np.float64)
+    x = np.stack([np.ones(n), j, np.where(j % 2 == 0, 1.0, -1.0), (-1.0) ** j * (j + 1)])
+    y = oracle.cumsum_scale_rows(x, 0.5)
+    np.testing.assert_array_equal(y[0], 0.5 * (j + 1))              # running count
+    np.testing.assert_array_equal(y[1], 0.5 * j * (j + 1) / 2)      # triangular numbers
+    np.testing.assert_array_equal(y[2], 0.5 * (j % 2 == 0))         # 1, 0, 1, 0, ...
+    # 1 - 2 + 3 - 4 ...: (j + 2) / 2 after an even index j, -(j + 1) / 2 after an odd one
+    np.testing.assert_array_equal(y[3], 0.5 * np.where(j % 2 == 0, (j + 2) / 2, -(j + 1) / 2))
+
+
+def test_cumsum_library_and_properties():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((5, 300))
+    y = oracle.cumsum_scale_rows(x, -0.125)
+    np.testing.assert_allclose(y, -0.125 * np.cumsum(x, axis=1), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(y[:, -1], -0.125 * x.sum(axis=1), rtol=0, atol=1e-12)  # last = scaled total
+    np.testing.assert_allclose(np.diff(y, axis=1), -0.125 * x[:, 1:], rtol=0, atol=1e-12)  # differences
+    np.testing.assert_array_equal(y[:, 0], -0.125 * x[:, 0])
+    # each row independently: permuting rows permutes the output
+    np.testing.assert_array_equal(oracle.cumsum_scale_rows(x[::-1], -0.125), y[::-1])
+    t = torch.from_numpy(x)
+    np.testing.assert_allclose(y, (-0.125 * torch.cumsum(t, dim=1)).numpy(), rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------------------
 # SwiGLU dual GEMM
 # ------------------------------------------------------------------------------------------------
 
