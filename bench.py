@@ -238,6 +238,25 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
         record("add_layernorm_bf16_2048x4096", "add_layernorm", w.shape, "bf16", True, ev, n_launch)
         del sets
 
+        w = synth.WORKLOADS["cumsum_f16_2048x4096"]
+        d = w.inputs()
+        sets = rotation_sets(torch, {"x": d["x"]}, {"y": d["x"]}, ROTATE_BYTES)
+        ws = api._workspace(api.FUSE_OP_CUMSUM_SCALE, *w.shape, 0, api.FUSE_F16, "cuda")
+
+        def cs(i):
+            s = sets[i % len(sets)]
+            api.fuse_cumsum_scale_rows(s["x"], d["scale"], y=s["y"])
+
+        def cs_unf(i):
+            s = sets[i % len(sets)]
+            api.fuse_unfused_cumsum_scale_rows(s["x"], d["scale"], y=s["y"], workspace=ws)
+        _, ev = time_launches(torch, stream, cs, n_launch)
+        record("cumsum_scale_f16_2048x4096", w.op, w.shape, w.dtype, True, ev, n_launch)
+        _, ev = time_launches(torch, stream, cs_unf, n_launch)
+        record("cumsum_scale_unfused_f16_2048x4096", w.op, w.shape, w.dtype, False, ev, n_launch,
+               {"note": "scan kernel storing the prefix sums + scale kernel"})
+        del sets, ws
+
         w = synth.WORKLOADS["gelu_f16_2048x4096"]
         d = w.inputs()
         bias = d["bias"].cuda()

@@ -135,6 +135,22 @@ fuse_status_t fuse_softmax_rows(const void *x, void *y, int64_t rows, int64_t co
                                 fuse_dtype_t dtype, void *stream);
 
 /*
+ * Fused row cumsum + scale, one pass over HBM (the Scan-Elementwise pattern of [P2] §4.4,
+ * example "Cumsum + Scale"; [P2] §4.3 on scans, which need the prefix sums of all that precedes
+ * each element):
+ *   y[r][j] = scale * (x[r][0] + ... + x[r][j])   (inclusive running sum along the row).
+ * The row stays in registers: the running sum is built per lane, across the wave and across
+ * the waves of the row, and the scale is applied before the single store.
+ *
+ *   x : [rows, cols];  y : [rows, cols], may equal x.
+ *   scale : finite, any sign.
+ *   dtype : FUSE_F32, FUSE_F16 or FUSE_BF16 (sums in fp32).
+ * cols must be in [1, FUSE_MAX_HIDDEN].
+ */
+fuse_status_t fuse_cumsum_scale_rows(const void *x, void *y, int64_t rows, int64_t cols, float scale,
+                                     fuse_dtype_t dtype, void *stream);
+
+/*
  * Fused SwiGLU dual GEMM (scheme B of [P4] 对比对象定义):
  *   out = SiLU(a . b1) * (a . b2),  SiLU(c) = c / (1 + e^-c).
  * Each workgroup loads its tile of a once and multiplies it with the matching tiles of b1 and
@@ -154,7 +170,8 @@ fuse_status_t fuse_swiglu_dualgemm(const void *a, const void *b1, const void *b2
  * kernels that store every intermediate in HBM in the I/O type, as the pages' "before
  * fusion" pictures do ([P3] §1: Add kernel writes A, LayerNorm kernel reads it; [P3] intro
  * diagram: BiasAdd, GELU, Residual; [P2] §4.3: row max, exp and sum, divide; [P4] scheme A:
- * one kernel for both products, one for SiLU and the product).  They exist so that the
+ * one kernel for both products, one for SiLU and the product; [P2] §4.4: the scan kernel
+ * storing the prefix sums, then the scale).  They exist so that the
  * traffic and time fusion saves can be measured, and they are the semantic reference the
  * pages recommend keeping ([P4] 迁移与使用注意事项 §3).
  *
@@ -165,7 +182,8 @@ typedef enum {
     FUSE_OP_ADD_LAYERNORM = 0,
     FUSE_OP_BIAS_GELU_RESIDUAL = 1,
     FUSE_OP_SOFTMAX_ROWS = 2,
-    FUSE_OP_SWIGLU = 3
+    FUSE_OP_SWIGLU = 3,
+    FUSE_OP_CUMSUM_SCALE = 4
 } fuse_op_t;
 
 /* Workspace bytes for an unfused baseline: (rows, hidden, -) for the row operations,
@@ -191,6 +209,10 @@ fuse_status_t fuse_unfused_softmax_rows(const void *x, void *y, int64_t rows, in
 fuse_status_t fuse_unfused_swiglu(const void *a, const void *b1, const void *b2, void *out,
                                   int64_t M, int64_t N, int64_t K, fuse_dtype_t dtype,
                                   void *workspace, size_t workspace_bytes, void *stream);
+
+fuse_status_t fuse_unfused_cumsum_scale_rows(const void *x, void *y, int64_t rows, int64_t cols,
+                                             float scale, fuse_dtype_t dtype, void *workspace,
+                                             size_t workspace_bytes, void *stream);
 
 /*
  * Plain device-to-device copy of `bytes` bytes, the calibration kernel of the roofline: its

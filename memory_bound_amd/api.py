@@ -21,7 +21,7 @@ _DTYPE_CODE = {torch.float32: FUSE_F32, torch.float16: FUSE_F16, torch.bfloat16:
 
 FUSE_LN_RELU = 1
 
-FUSE_OP_ADD_LAYERNORM, FUSE_OP_BIAS_GELU_RESIDUAL, FUSE_OP_SOFTMAX_ROWS, FUSE_OP_SWIGLU = 0, 1, 2, 3
+FUSE_OP_ADD_LAYERNORM, FUSE_OP_BIAS_GELU_RESIDUAL, FUSE_OP_SOFTMAX_ROWS, FUSE_OP_SWIGLU, FUSE_OP_CUMSUM_SCALE = 0, 1, 2, 3, 4
 
 STATUS = {0: "FUSE_OK", 1: "FUSE_ERR_NULL_PTR", 2: "FUSE_ERR_BAD_SHAPE", 3: "FUSE_ERR_BAD_DTYPE",
           4: "FUSE_ERR_BAD_VALUE", 5: "FUSE_ERR_ALIAS", 6: "FUSE_ERR_UNSUPPORTED",
@@ -29,10 +29,11 @@ STATUS = {0: "FUSE_OK", 1: "FUSE_ERR_NULL_PTR", 2: "FUSE_ERR_BAD_SHAPE", 3: "FUS
 
 # Every symbol include/libfuse.h declares.
 EXPORTS = [
-    "fuse_add_layernorm", "fuse_add_layernorm_ex", "fuse_bias_gelu_residual", "fuse_softmax_rows", "fuse_swiglu_dualgemm",
+    "fuse_add_layernorm", "fuse_add_layernorm_ex", "fuse_bias_gelu_residual", "fuse_softmax_rows",
+    "fuse_cumsum_scale_rows", "fuse_swiglu_dualgemm",
     "fuse_unfused_workspace_bytes", "fuse_unfused_add_layernorm", "fuse_unfused_bias_gelu_residual",
-    "fuse_unfused_softmax_rows", "fuse_unfused_swiglu", "fuse_copy", "fuse_status_string",
-    "fuse_last_hip_error", "fuse_version",
+    "fuse_unfused_softmax_rows", "fuse_unfused_cumsum_scale_rows", "fuse_unfused_swiglu", "fuse_copy",
+    "fuse_status_string", "fuse_last_hip_error", "fuse_version",
 ]
 
 
@@ -64,6 +65,8 @@ def load() -> ctypes.CDLL:
         "fuse_add_layernorm_ex": [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, ctypes.c_uint, i32, vp],
         "fuse_bias_gelu_residual": [vp, vp, vp, vp, i64, i64, i32, vp],
         "fuse_softmax_rows": [vp, vp, i64, i64, f32, i32, vp],
+        "fuse_cumsum_scale_rows": [vp, vp, i64, i64, f32, i32, vp],
+        "fuse_unfused_cumsum_scale_rows": [vp, vp, i64, i64, f32, i32, vp, sz, vp],
         "fuse_swiglu_dualgemm": [vp, vp, vp, vp, i64, i64, i64, i32, vp],
         "fuse_unfused_add_layernorm": [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp, sz, vp],
         "fuse_unfused_bias_gelu_residual": [vp, vp, vp, vp, i64, i64, i32, vp, sz, vp],
@@ -212,6 +215,18 @@ def fuse_softmax_rows(x, scale=1.0, y=None, stream=None):
     return y
 
 
+def fuse_cumsum_scale_rows(x, scale=1.0, y=None, stream=None):
+    """y = scale * cumsum(x) over the last dim (inclusive running sum)."""
+    rows, cols = _rows_cols(x)
+    _check(x, "x")
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", x.dtype, x.shape)
+    _ok(load().fuse_cumsum_scale_rows(_ptr(x), _ptr(y), rows, cols, float(scale), _dt(x), _stream(stream)),
+        "fuse_cumsum_scale_rows")
+    return y
+
+
 def fuse_swiglu_dualgemm(a, b1, b2, out=None, stream=None):
     """out = SiLU(a @ b1) * (a @ b2); a [M,K], b1 and b2 [K,N], bf16."""
     M, K = a.shape
@@ -264,6 +279,17 @@ def fuse_unfused_softmax_rows(x, scale=1.0, y=None, workspace=None, stream=None)
     ws = workspace or _workspace(FUSE_OP_SOFTMAX_ROWS, rows, cols, 0, _dt(x), x.device)
     _ok(load().fuse_unfused_softmax_rows(_ptr(x), _ptr(y), rows, cols, float(scale), _dt(x), ws[1], ws[2],
                                          _stream(stream)), "fuse_unfused_softmax_rows")
+    return y
+
+
+def fuse_unfused_cumsum_scale_rows(x, scale=1.0, y=None, workspace=None, stream=None):
+    rows, cols = _rows_cols(x)
+    _check(x, "x")
+    if y is None:
+        y = torch.empty_like(x)
+    ws = workspace or _workspace(FUSE_OP_CUMSUM_SCALE, rows, cols, 0, _dt(x), x.device)
+    _ok(load().fuse_unfused_cumsum_scale_rows(_ptr(x), _ptr(y), rows, cols, float(scale), _dt(x), ws[1], ws[2],
+                                              _stream(stream)), "fuse_unfused_cumsum_scale_rows")
     return y
 
 

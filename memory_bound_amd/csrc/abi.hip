@@ -260,6 +260,36 @@ fuse_status_t fuse_softmax_rows(const void* x, void* y, int64_t rows, int64_t co
 }
 
 // ------------------------------------------------------------------------------------------------
+// Row cumsum + scale
+// ------------------------------------------------------------------------------------------------
+
+static fuse_status_t check_cumsum(const void* x, void* y, int64_t rows, int64_t cols, float scale,
+                                  fuse_dtype_t dt, size_t* tb, bool* vec) {
+    fuse_status_t st = check_rows(rows, cols, FUSE_MAX_HIDDEN, dt, tb);
+    if (st != FUSE_OK) return st;
+    if (!isfinite(scale)) return FUSE_ERR_BAD_VALUE;
+    if (rows == 0) return FUSE_OK;
+    if (!x || !y) return FUSE_ERR_NULL_PTR;
+    const int e = elem_bytes(dt);
+    if (!elem_aligned(x, e) || !elem_aligned(y, e)) return FUSE_ERR_MISALIGNED;
+    if (bad_alias(y, *tb, x, *tb)) return FUSE_ERR_ALIAS;
+    *vec = aligned16(x) && aligned16(y) && ((size_t)cols * e) % 16 == 0;
+    return FUSE_OK;
+}
+
+fuse_status_t fuse_cumsum_scale_rows(const void* x, void* y, int64_t rows, int64_t cols, float scale,
+                                     fuse_dtype_t dt, void* stream) {
+    size_t tb = 0;
+    bool vec = false;
+    fuse_status_t st = check_cumsum(x, y, rows, cols, scale, dt, &tb, &vec);
+    if (st != FUSE_OK || rows == 0) return st;
+    const fuse::RowPlan plan = fuse::plan_row(cols, elem_bytes(dt), vec, env_int("FUSE_ROW_WPR"));
+    return hip_status(by_dtype(dt, [&]<fuse::DT D>() {
+        return fuse::launch_cumsum_scale<D>(x, y, rows, (int)cols, scale, plan, (hipStream_t)stream);
+    }));
+}
+
+// ------------------------------------------------------------------------------------------------
 // SwiGLU dual GEMM
 // ------------------------------------------------------------------------------------------------
 
@@ -312,6 +342,9 @@ size_t fuse_unfused_workspace_bytes(fuse_op_t op, int64_t d0, int64_t d1, int64_
         case FUSE_OP_SWIGLU:
             if (dt != FUSE_BF16 || !tensor_bytes(d0, d1, 2, &tb)) return 0;
             return 2 * round256(tb);
+        case FUSE_OP_CUMSUM_SCALE:
+            if (!tensor_bytes(d0, d1, elem_bytes(dt), &tb)) return 0;
+            return round256(tb);
     }
     return 0;
 }
@@ -388,6 +421,26 @@ fuse_status_t fuse_unfused_softmax_rows(const void* x, void* y, int64_t rows, in
     return hip_status(by_dtype(dt, [&]<fuse::DT D>() {
         return fuse::launch_softmax_unfused<D>(x, y, rows, (int)cols, scale, vec, e, m, s,
                                                (hipStream_t)stream);
+    }));
+}
+
+fuse_status_t fuse_unfused_cumsum_scale_rows(const void* x, void* y, int64_t rows, int64_t cols, float scale,
+                                             fuse_dtype_t dt, void* ws, size_t ws_bytes, void* stream) {
+    size_t tb = 0;
+    bool vec = false;
+    fuse_status_t st = check_cumsum(x, y, rows, cols, scale, dt, &tb, &vec);
+    if (st != FUSE_OK || rows == 0) return st;
+    const size_t need = fuse_unfused_workspace_bytes(FUSE_OP_CUMSUM_SCALE, rows, cols, 0, dt);
+    if (!workspace_ok(ws, ws_bytes, need)) return FUSE_ERR_WORKSPACE;
+    if (overlaps(ws, need, x, tb) || overlaps(ws, need, y, tb)) return FUSE_ERR_WORKSPACE;
+    const bool wvec = vec;  // the workspace is 256-byte aligned
+    const fuse::RowPlan plan = fuse::plan_row(cols, elem_bytes(dt), wvec, env_int("FUSE_ROW_WPR"));
+    return hip_status(by_dtype(dt, [&]<fuse::DT D>() {
+        // scan kernel stores the prefix sums S in the I/O type, the element-wise kernel y = scale * S
+        hipError_t e = fuse::launch_cumsum_scale<D>(x, ws, rows, (int)cols, 1.0f, plan, (hipStream_t)stream);
+        if (e != hipSuccess) return e;
+        return fuse::launch_ew<D>(fuse::EwOp::Scale, vec, ws, nullptr, nullptr, y, rows * cols, cols, ew_chunks(),
+                                  (hipStream_t)stream, scale);
     }));
 }
 

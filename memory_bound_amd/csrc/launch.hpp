@@ -22,7 +22,7 @@ struct RowPlan {
 // 128-bit path when the resulting chunks per lane stay within the compiled set.
 RowPlan plan_row(int64_t n, int elem_bytes, bool aligned, int wpr_override);
 
-enum class EwOp : int { BiasGeluRes = 0, Add = 1, BiasAdd = 2, Gelu = 3, SiluMul = 4 };
+enum class EwOp : int { BiasGeluRes = 0, Add = 1, BiasAdd = 2, Gelu = 3, SiluMul = 4, Scale = 5 };
 
 template <DT D>
 hipError_t launch_add_layernorm(const void* x, const void* res, const void* gamma, const void* beta,
@@ -35,9 +35,14 @@ hipError_t launch_add_layernorm_ex(const void* x, const void* res, const void* g
 template <DT D>
 hipError_t launch_softmax_rows(const void* x, void* y, int64_t rows, int cols, float scale,
                                RowPlan plan, hipStream_t stream);
+// alpha is used by EwOp::Scale only.
 template <DT D>
 hipError_t launch_ew(EwOp op, bool vec, const void* a, const void* b, const void* c, void* out,
-                     int64_t n, int64_t hidden, int chunks_per_thread, hipStream_t stream);
+                     int64_t n, int64_t hidden, int chunks_per_thread, hipStream_t stream,
+                     float alpha = 0.0f);
+template <DT D>
+hipError_t launch_cumsum_scale(const void* x, void* y, int64_t rows, int cols, float scale,
+                               RowPlan plan, hipStream_t stream);
 template <DT D>
 hipError_t launch_softmax_unfused(const void* x, void* y, int64_t rows, int cols, float scale,
                                   bool vec, void* e, float* m, float* s, hipStream_t stream);

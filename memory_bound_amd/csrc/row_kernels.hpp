@@ -297,4 +297,99 @@ softmax_rows_kernel(const typename Elem<D>::T* x, typename Elem<D>::T* y, int64_
     }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Row cumsum + scale.  y_j = scale * (x_0 + ... + x_j).  The row's chunks are spread over the lanes
+// as in the other row kernels (chunk c = (j * WPR + w) * 64 + lane), so the running sum is built
+// in three levels: each lane scans its V-element chunks in registers; a DPP scan over the 64
+// lanes turns the chunk totals into per-lane offsets within each (j, wave) block of 64 chunks; the
+// block totals go through LDS and every wave adds the totals of the blocks before its own (blocks
+// are ordered j first, then wave).
+// ------------------------------------------------------------------------------------------------
+
+// v moved by a DPP control, 0 where the lane has no source (or its row is masked off).
+template <int CTRL, int ROW_MASK> __device__ __forceinline__ float dpp_zero(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK,
+                                                                 0xF, true));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8 lanes within each
+// 16-lane row (row_shr), then the gfx9 row broadcasts carry the row totals on: lane 15 of each
+// row into the next row (rows 1 and 3), lane 31 into rows 2 and 3.
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+    v += dpp_zero<0x111, 0xF>(v);
+    v += dpp_zero<0x112, 0xF>(v);
+    v += dpp_zero<0x114, 0xF>(v);
+    v += dpp_zero<0x118, 0xF>(v);
+    v += dpp_zero<0x142, 0xA>(v);
+    v += dpp_zero<0x143, 0xC>(v);
+    return v;
+}
+
+template <DT D, bool VECP, int NV, int WPR>
+__global__ void __launch_bounds__(RowShape<WPR>::THREADS)
+cumsum_scale_kernel(const typename Elem<D>::T* x, typename Elem<D>::T* y, int64_t rows, int cols,
+                    float scale) {
+    using S = RowSlice<D, VECP, NV, WPR>;
+    constexpr int V = S::V;
+    constexpr int RPB = RowShape<WPR>::ROWS_PER_BLOCK;
+    __shared__ float lds_tot[RPB][NV][WPR];
+
+    const S s(cols);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rib = wave / WPR, wpos = wave % WPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + rib;
+    const uint32_t row_bytes = row < rows ? (uint32_t)cols * (uint32_t)sizeof(typename S::T) : 0u;
+    const rsrc_t rx = make_rsrc(x + row * cols, row_bytes);
+    const rsrc_t ry = make_rsrc(y + row * cols, row_bytes);
+
+    float v[NV][V];
+#pragma unroll
+    for (int j = 0; j < NV; j++) s.template load<AUX_STREAM>(rx, j, v[j]);  // zeros past the row
+
+    // chunk-local inclusive scans, then the exclusive scan of the chunk totals over the wave
+    float excl[NV], btot[NV];
+#pragma unroll
+    for (int j = 0; j < NV; j++) {
+#pragma unroll
+        for (int k = 1; k < V; k++) v[j][k] += v[j][k - 1];
+        const float inc = wave_inclusive_scan(v[j][V - 1]);
+        excl[j] = dpp_zero<0x138, 0xF>(inc);  // wave_shr:1 -- lane 0 gets 0
+        btot[j] = lane_read(inc, 63);
+    }
+
+    // offsets of the blocks before this wave's (j, wpos) blocks
+    float pre[NV];
+    if constexpr (WPR == 1) {
+        float off = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NV; j++) {
+            pre[j] = off;
+            off += btot[j];
+        }
+    } else {
+        if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+            for (int j = 0; j < NV; j++) lds_tot[rib][j][wpos] = btot[j];
+        }
+        __syncthreads();
+        float off = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NV; j++)
+#pragma unroll
+            for (int w = 0; w < WPR; w++) {
+                if (w == wpos) pre[j] = off;
+                off += lds_tot[rib][j][w];
+            }
+    }
+
+#pragma unroll
+    for (int j = 0; j < NV; j++) {
+        const float base = pre[j] + excl[j];
+        float o[V];
+#pragma unroll
+        for (int k = 0; k < V; k++) o[k] = scale * (base + v[j][k]);
+        s.template store<AUX_STREAM>(ry, j, o);
+    }
+}
+
 }  // namespace fuse

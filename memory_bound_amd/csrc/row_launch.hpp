@@ -104,8 +104,23 @@ hipError_t launch_softmax_rows(const void* x, void* y, int64_t rows, int cols, f
 }
 
 template <DT D>
+hipError_t launch_cumsum_scale(const void* x, void* y, int64_t rows, int cols, float scale,
+                               RowPlan plan, hipStream_t stream) {
+    using T = typename Elem<D>::T;
+    hipError_t err = hipErrorInvalidValue;
+    auto go = [&]<bool VECP, int NV, int WPR>() {
+        const dim3 grid((unsigned)detail::row_blocks<WPR>(rows)), block(RowShape<WPR>::THREADS);
+        hipLaunchKernelGGL((cumsum_scale_kernel<D, VECP, NV, WPR>), grid, block, 0, stream,
+                           (const T*)x, (T*)y, rows, cols, scale);
+        err = hipGetLastError();
+    };
+    if (!detail::with_plan(plan, go)) return hipErrorInvalidValue;
+    return err;
+}
+
+template <DT D>
 hipError_t launch_ew(EwOp op, bool vec, const void* a, const void* b, const void* c, void* out,
-                     int64_t n, int64_t hidden, int chunks_per_thread, hipStream_t stream) {
+                     int64_t n, int64_t hidden, int chunks_per_thread, hipStream_t stream, float alpha) {
     using T = typename Elem<D>::T;
     const int V = vec ? Elem<D>::VEC : 1;
     const uint64_t total = (uint64_t)(n / V);
@@ -115,7 +130,7 @@ hipError_t launch_ew(EwOp op, bool vec, const void* a, const void* b, const void
         const uint64_t per_block = 256ull * CH;
         const dim3 grid((unsigned)((total + per_block - 1) / per_block)), block(256);
         hipLaunchKernelGGL((ew_kernel<D, VECP, CH, Op>), grid, block, 0, stream, (const T*)a,
-                           (const T*)b, (const T*)c, (T*)out, total, cpr);
+                           (const T*)b, (const T*)c, (T*)out, total, cpr, alpha);
         err = hipGetLastError();
     };
     auto by_ch = [&]<class Op, bool VECP>() {
@@ -137,6 +152,7 @@ hipError_t launch_ew(EwOp op, bool vec, const void* a, const void* b, const void
         case EwOp::BiasAdd: by_vec.template operator()<OpBiasAdd>(); break;
         case EwOp::Gelu: by_vec.template operator()<OpGelu>(); break;
         case EwOp::SiluMul: by_vec.template operator()<OpSiluMul>(); break;
+        case EwOp::Scale: by_vec.template operator()<OpScale>(); break;
     }
     return err;
 }
@@ -173,6 +189,8 @@ hipError_t launch_softmax_unfused(const void* x, void* y, int64_t rows, int cols
     template hipError_t launch_softmax_rows<D>(const void*, void*, int64_t, int, float,      \
                                                      RowPlan, hipStream_t);                        \
     template hipError_t launch_ew<D>(EwOp, bool, const void*, const void*, const void*,      \
-                                           void*, int64_t, int64_t, int, hipStream_t);             \
+                                           void*, int64_t, int64_t, int, hipStream_t, float);      \
+    template hipError_t launch_cumsum_scale<D>(const void*, void*, int64_t, int, float,      \
+                                                     RowPlan, hipStream_t);                        \
     template hipError_t launch_softmax_unfused<D>(const void*, void*, int64_t, int, float,   \
                                                         bool, void*, float*, float*, hipStream_t);

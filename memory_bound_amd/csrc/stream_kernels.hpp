@@ -35,6 +35,11 @@ struct OpSiluMul {  // SiLU(c1) * c2 (second kernel of the unfused SwiGLU)
     static constexpr bool USE_B = true, USE_C = false;
     __device__ __forceinline__ float operator()(float a, float b, float) const { return silu(a) * b; }
 };
+struct OpScale {  // alpha * s (second kernel of the unfused cumsum + scale)
+    static constexpr bool USE_B = false, USE_C = false;
+    float alpha;
+    __device__ __forceinline__ float operator()(float a, float, float) const { return alpha * a; }
+};
 
 // Workgroup b owns chunks [b*256*CH, (b+1)*256*CH) of the flat tensor; its buffer resources
 // start at that chunk and end at the tensor's end, so the tail needs no branches and the 32-bit
@@ -43,11 +48,12 @@ struct OpSiluMul {  // SiLU(c1) * c2 (second kernel of the unfused SwiGLU)
 template <DT D, bool VECP, int CH, class Op>
 __global__ void __launch_bounds__(256)
 ew_kernel(const typename Elem<D>::T* a, const typename Elem<D>::T* b, const typename Elem<D>::T* c,
-          typename Elem<D>::T* out, uint64_t total_chunks, uint32_t chunks_per_row) {
+          typename Elem<D>::T* out, uint64_t total_chunks, uint32_t chunks_per_row, float alpha) {
     using T = typename Elem<D>::T;
     constexpr int V = VECP ? Elem<D>::VEC : 1;
     constexpr uint32_t CB = VECP ? 16u : (uint32_t)sizeof(T);  // bytes per chunk
-    const Op op;
+    Op op;
+    if constexpr (requires { op.alpha; }) op.alpha = alpha;
     const uint64_t first = (uint64_t)blockIdx.x * (256u * CH);
     const uint64_t left = total_chunks - first;
     const uint32_t bytes = (uint32_t)(left < 256u * CH ? left : 256u * CH) * CB;

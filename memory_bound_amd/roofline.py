@@ -57,6 +57,13 @@ def softmax_rows_bytes(rows: int, cols: int, dtype: str, fused: bool = True) -> 
     return _t("unfused", 5 * t, 0, 4 * rows * 4)
 
 
+def cumsum_scale_rows_bytes(rows: int, cols: int, dtype: str, fused: bool = True) -> dict:
+    """Fused: read x, write y.  Unfused: the scan kernel reads x and writes S, the scale kernel
+    reads S and writes y (4 tensor passes)."""
+    t = rows * cols * ELEM_BYTES[dtype]
+    return _t("fused" if fused else "unfused", (2 if fused else 4) * t)
+
+
 def swiglu_bytes(M: int, N: int, K: int, dtype: str, fused: bool = True) -> dict:
     """Minimum traffic: read a, b1, b2 once, write out once.  Unfused adds c1 and c2 written by the
     GEMM kernel and read back by the element-wise kernel."""
@@ -81,6 +88,8 @@ def workload_work(op: str, shape: tuple, dtype: str, fused: bool = True) -> dict
         return bias_gelu_residual_bytes(*shape, dtype, fused)
     if op == "softmax_rows":
         return softmax_rows_bytes(*shape, dtype, fused)
+    if op == "cumsum_scale_rows":
+        return cumsum_scale_rows_bytes(*shape, dtype, fused)
     if op == "swiglu":
         d = swiglu_bytes(*shape, dtype, fused)
         d["flops"] = swiglu_flops(*shape)

@@ -66,6 +66,13 @@ def softmax_inputs(rows: int, cols: int, dtype: str, seed: int, head_dim: int = 
     return {"x": x, "scale": 1.0 / math.sqrt(head_dim)}
 
 
+def cumsum_inputs(rows: int, cols: int, dtype: str, seed: int) -> dict:
+    """x ~ N(0,1); the scale 1/sqrt(cols) keeps the scaled running sums of order one."""
+    g = _gen(seed)
+    x = _randn(g, rows, cols).to(DTYPES[dtype])
+    return {"x": x, "scale": 1.0 / math.sqrt(cols)}
+
+
 def swiglu_inputs(M: int, N: int, K: int, dtype: str, seed: int) -> dict:
     g = _gen(seed)
     t = DTYPES[dtype]
@@ -96,10 +103,12 @@ class Workload:
             return softmax_inputs(*self.shape, self.dtype, self.seed)
         if self.op == "swiglu":
             return swiglu_inputs(*self.shape, self.dtype, self.seed)
+        if self.op == "cumsum_scale_rows":
+            return cumsum_inputs(*self.shape, self.dtype, self.seed)
         raise ValueError(self.op)
 
 
-# The five workloads of the hot path (B*S flattened into rows).
+# The workloads of the hot path (B*S flattened into rows).
 WORKLOADS = {
     w.name: w
     for w in [
@@ -115,5 +124,7 @@ WORKLOADS = {
                  "row softmax fp16, 32 heads x 2048 x 2048 scores"),
         Workload("swiglu_bf16_2048x8960x1536", "swiglu", (2048, 8960, 1536), "bf16", 1006,
                  "SwiGLU dual GEMM bf16, M=2048 N=8960 K=1536"),
+        Workload("cumsum_f16_2048x4096", "cumsum_scale_rows", (2048, 4096), "f16", 1007,
+                 "row cumsum + scale fp16, [B,S,H]=[1,2048,4096], scale 1/64"),
     ]
 }

@@ -144,6 +144,28 @@ def test_softmax_validation(lib):
     assert call(rows=0) == OK
 
 
+def test_cumsum_validation(lib):
+    def call(x=P, y=2 * P, rows=4, cols=64, scale=0.5, dt=F16):
+        return lib.fuse_cumsum_scale_rows(v(x), v(y), rows, cols, scale, dt, None)
+    assert call(x=0) == NULL
+    assert call(y=0) == NULL
+    assert call(cols=0) == SHAPE
+    assert call(rows=-2) == SHAPE
+    assert call(cols=16385) == UNSUP
+    assert call(dt=5) == DTYPE
+    assert call(scale=float("inf")) == VALUE
+    assert call(scale=float("nan")) == VALUE
+    assert call(y=P + 2) == ALIAS
+    assert call(x=P + 1) == MISAL
+    assert call(rows=0) == OK
+    n = lib.fuse_unfused_workspace_bytes(4, 4, 64, 0, F16)
+    assert n == 512
+    assert lib.fuse_unfused_cumsum_scale_rows(v(P), v(2 * P), 4, 64, 0.5, F16, v(0), n, None) == WS
+    assert lib.fuse_unfused_cumsum_scale_rows(v(P), v(2 * P), 4, 64, 0.5, F16, v(3 * P), n - 1, None) == WS
+    assert lib.fuse_unfused_cumsum_scale_rows(v(P), v(2 * P), 4, 64, 0.5, F16, v(3 * P + 16), n, None) == WS
+    assert lib.fuse_unfused_cumsum_scale_rows(v(P), v(2 * P), 4, 64, 0.5, F16, v(P), n, None) == WS
+
+
 def test_swiglu_validation(lib):
     def call(a=P, b1=8 * P, b2=16 * P, out=24 * P, M=128, N=128, K=64, dt=BF16):
         return lib.fuse_swiglu_dualgemm(v(a), v(b1), v(b2), v(out), M, N, K, dt, None)

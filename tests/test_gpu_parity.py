@@ -343,6 +343,56 @@ def test_softmax_nan_propagates():
 
 
 # ------------------------------------------------------------------------------------------------
+# Row cumsum + scale
+# ------------------------------------------------------------------------------------------------
+
+CUMSUM_SHAPES = [
+    (37, 4096, "f16"), (64, 768, "f32"), (130, 4096, "bf16"), (5, 1000, "f16"), (3, 7, "f32"),
+    (2, 1, "f16"), (4, 8, "f16"), (9, 64, "f32"), (7, 16384, "f16"), (6, 16384, "f32"), (9, 8192, "bf16"),
+    (11, 12288, "f16"), (3, 4097, "f32"), (33, 2048, "f32"), (17, 520, "bf16"),
+]
+
+
+@pytest.mark.parametrize("rows,cols,dtype", CUMSUM_SHAPES)
+def test_cumsum_parity(rows, cols, dtype):
+    announce(f"cumsum_scale {rows}x{cols} {dtype}")
+    d = synth.cumsum_inputs(rows, cols, dtype, seed=rows * 7 + cols)
+    y = api.fuse_cumsum_scale_rows(d["x"].cuda(), d["scale"])
+    assert_close(y, oracle.cumsum_scale_rows(d["x"], np.float32(d["scale"])), KIND[dtype],
+                 f"cumsum {rows}x{cols} {dtype}")
+
+
+@pytest.mark.parametrize("wpr", [1, 2, 4, 8])
+def test_cumsum_exact_counts_every_wpr(monkeypatch, wpr):
+    # integer inputs make every partial sum exact in fp32, so any misplaced carry between chunks,
+    # lanes, DPP rows or waves shows up as an exact mismatch
+    monkeypatch.setenv("FUSE_ROW_WPR", str(wpr))
+    announce(f"cumsum exact counts FUSE_ROW_WPR={wpr}")
+    for cols in (4096, 2048, 1000):
+        x = torch.ones(6, cols, dtype=torch.float32)
+        x[1] = torch.arange(cols) % 5 - 2.0
+        x[2] = -1.0
+        x[3, ::64] = 7.0
+        y = api.fuse_cumsum_scale_rows(x.cuda(), 1.0).cpu()
+        assert torch.equal(y, torch.cumsum(x.double(), dim=1).float()), f"cols={cols} wpr={wpr}"
+
+
+def test_cumsum_workload_full_and_inplace():
+    w = synth.WORKLOADS["cumsum_f16_2048x4096"]
+    announce("cumsum workload 2048x4096 fp16")
+    d = w.inputs()
+    ref = oracle.cumsum_scale_rows(d["x"], np.float32(d["scale"]))
+    x = d["x"].cuda()
+    y = api.fuse_cumsum_scale_rows(x, d["scale"])
+    r = assert_close(y, ref, "f16", "cumsum workload")
+    print(f"  max_abs={r['max_abs']:.3e}", flush=True)
+    y2 = api.fuse_cumsum_scale_rows(x, d["scale"], y=x)  # in place
+    assert torch.equal(y2, y)
+    yn = api.fuse_cumsum_scale_rows(d["x"].cuda(), -2.0)
+    assert_close(yn, oracle.cumsum_scale_rows(d["x"], -2.0), "f16", "cumsum scale -2")
+
+
+# ------------------------------------------------------------------------------------------------
 # SwiGLU dual GEMM
 # ------------------------------------------------------------------------------------------------
 
@@ -434,6 +484,14 @@ def test_unfused_softmax():
     y = api.fuse_unfused_softmax_rows(d["x"].cuda(), d["scale"])
     ref = oracle.softmax_rows_unfused(d["x"], np.float32(d["scale"]), "f16")
     _loose(y, ref, "f16", "unfused softmax")
+
+
+def test_unfused_cumsum():
+    announce("unfused cumsum + scale")
+    d = synth.cumsum_inputs(300, 4096, "f16", seed=1007)
+    y = api.fuse_unfused_cumsum_scale_rows(d["x"].cuda(), d["scale"])
+    ref = oracle.cumsum_scale_rows_unfused(d["x"], np.float32(d["scale"]), "f16")
+    _loose(y, ref, "f16", "unfused cumsum")
 
 
 def test_unfused_swiglu():

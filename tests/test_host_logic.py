@@ -44,7 +44,11 @@ def test_workload_table():
     assert w["addln_f16_16384x4096"].shape == (8 * 2048, 4096)
     assert w["softmax_f16_65536x2048"].shape == (32 * 2048, 2048)
     assert w["swiglu_bf16_2048x8960x1536"].shape == (2048, 8960, 1536)
+    assert w["cumsum_f16_2048x4096"].shape == (2048, 4096)
     assert len({x.seed for x in w.values()}) == len(w)
+    c = w["cumsum_f16_2048x4096"].inputs()
+    assert c["x"].dtype == torch.float16 and c["scale"] == 1 / 64
+    assert abs(c["x"].double().std().item() - 1) < 0.01
 
 
 # ---- comparison rules --------------------------------------------------------------------------
@@ -101,3 +105,8 @@ def test_other_algorithmic_work():
     assert roofline.swiglu_flops(2048, 8960, 1536) == 112_742_891_520
     assert roofline.add_layernorm_bytes(64, 768, "f32")["bytes"] == 595_968
     assert roofline.add_layernorm_bytes(16384, 4096, "f16")["bytes"] == 402_669_568
+    # LayerNorm variants: one more tensor (the pre-norm sum) and 8 bytes of statistics per row
+    assert roofline.add_layernorm_ex_bytes(2048, 4096, "f16")["bytes"] == 50_348_032 + 16_777_216 + 16_384
+    # cumsum + scale: read x, write y; unfused adds the stored prefix sums and their reload
+    assert roofline.cumsum_scale_rows_bytes(2048, 4096, "f16")["bytes"] == 33_554_432
+    assert roofline.cumsum_scale_rows_bytes(2048, 4096, "f16", fused=False)["bytes"] == 67_108_864
