@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 HEADLINE = "addln_f16_2048x4096"
 ROTATE_BYTES = 1 << 30
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "add_layernorm_f16_2048x4096_counters.txt")
-HEADLINE_SOURCES = ["fuse_common.hpp", "launch.hpp", "row_kernels.hpp", "row_launch.hpp", "row_plan.hip"]
+HEADLINE_SOURCES = ["fuse_common.hpp", "row_plan.hpp", "row_plan.hip", "row_kernels.hpp", "row_launch.hpp"]
 
 
 def log(msg):
@@ -368,6 +368,73 @@ def counters_pass(torch, api, synth, n=8):
     log(f"counters: {n} x copy of {nbytes} bytes")
 
 
+def launch_study(torch, api, synth, n_empty=4000, n_graph=1000, n_steps=200):
+    """Launch cost on this GPU ([P2] §4.5, [P3] §2): an empty kernel enqueued from a loop inside
+    the library (host cost per call, back-to-back interval on the GPU, cost per kernel inside a
+    replayed graph), and small latency-bound rows fused vs unfused, host-launched from Python vs
+    replayed from a graph."""
+    stream = torch.cuda.Stream()
+    out = {}
+    with torch.cuda.stream(stream):
+        api.fuse_empty_kernels(200)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        api.fuse_empty_kernels(n_empty)
+        t1 = time.perf_counter()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out["empty_kernel_host_enqueue_us"] = round((t1 - t0) * 1e6 / n_empty, 3)
+        out["empty_kernel_back_to_back_us"] = round(e0.elapsed_time(e1) * 1e3 / n_empty, 3)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            api.fuse_empty_kernels(n_graph)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out["empty_kernel_in_graph_us"] = round(e0.elapsed_time(e1) * 1e3 / n_graph, 3)
+        del g
+
+        def steps(name, launch, kernels):
+            for i in range(3):
+                launch(i)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(n_steps):
+                launch(i)
+            torch.cuda.synchronize()
+            eager = (time.perf_counter() - t0) * 1e6 / n_steps
+            _, ev = time_launches(torch, stream, launch, n_steps)
+            out[name] = {"kernels_per_step": kernels, "eager_python_us_per_step": round(eager, 2),
+                         "graph_us_per_step": round(ev * 1e3 / n_steps, 3)}
+            log(f"{name}: eager {eager:.1f} us, graph {ev * 1e3 / n_steps:.2f} us per step")
+
+        d = synth.WORKLOADS["addln_f32_64x768"].inputs()
+        g_ = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in d.items()}
+        y = torch.empty_like(g_["x"])
+        ws = api._workspace(api.FUSE_OP_ADD_LAYERNORM, 64, 768, 0, api.FUSE_F32, "cuda")
+        steps("add_layernorm_f32_64x768_fused",
+              lambda i: api.fuse_add_layernorm(g_["x"], g_["residual"], g_["gamma"], g_["beta"], d["eps"], y=y), 1)
+        steps("add_layernorm_f32_64x768_unfused",
+              lambda i: api.fuse_unfused_add_layernorm(g_["x"], g_["residual"], g_["gamma"], g_["beta"], d["eps"],
+                                                       y=y, workspace=ws), 2)
+        d = synth.bias_gelu_residual_inputs(64, 4096, "f16", 1002)
+        g_ = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in d.items()}
+        y = torch.empty_like(g_["x"])
+        ws = api._workspace(api.FUSE_OP_BIAS_GELU_RESIDUAL, 64, 4096, 0, api.FUSE_F16, "cuda")
+        steps("bias_gelu_residual_f16_64x4096_fused",
+              lambda i: api.fuse_bias_gelu_residual(g_["x"], g_["bias"], g_["residual"], y=y), 1)
+        steps("bias_gelu_residual_f16_64x4096_unfused",
+              lambda i: api.fuse_unfused_bias_gelu_residual(g_["x"], g_["bias"], g_["residual"], y=y, workspace=ws), 3)
+    log(f"empty kernel: host {out['empty_kernel_host_enqueue_us']} us, back-to-back "
+        f"{out['empty_kernel_back_to_back_us']} us, in graph {out['empty_kernel_in_graph_us']} us")
+    return out
+
+
 def cpu_baseline(synth, roofline, budget_s=10.0):
     import numpy as np
 
@@ -421,6 +488,7 @@ def main():
     h = headline(torch, api, synth, roofline, a.steps, a.warmup)
     log(f"headline: {h['avg_launch_us']:.2f} us/launch, value {h['value_gbps']:.0f} GB/s")
     rows = {} if a.no_rows else other_rows(torch, api, synth, roofline)
+    study = None if a.no_rows else launch_study(torch, api, synth)
     cpu = None if a.no_cpu else cpu_baseline(synth, roofline)
 
     traffic = read_counters()
@@ -449,6 +517,7 @@ def main():
                      "avg_launch_us": round(h["avg_launch_us"], 3)},
         "cpu_baseline": cpu,
         "rows": rows,
+        "launch_study": study,
     }
     print(json.dumps(line), flush=True)
 

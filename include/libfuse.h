@@ -222,6 +222,16 @@ fuse_status_t fuse_unfused_cumsum_scale_rows(const void *x, void *y, int64_t row
  */
 fuse_status_t fuse_copy(const void *src, void *dst, size_t bytes, void *stream);
 
+/*
+ * Launch-cost probe ([P2] §4.5 and [P3] §2 argue that per-launch cost, not only traffic, is what
+ * fusion and graph capture remove): enqueues `count` launches of a kernel that does nothing (one
+ * 64-thread workgroup each) on `stream`, from a plain loop inside the library, so the host cost
+ * per launch, the back-to-back dispatch interval and the per-kernel cost inside a captured graph
+ * can be timed without any binding overhead in between.  0 <= count <= FUSE_MAX_EMPTY_KERNELS.
+ */
+#define FUSE_MAX_EMPTY_KERNELS 1048576
+fuse_status_t fuse_empty_kernels(int64_t count, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *fuse_status_string(fuse_status_t status);
 

@@ -32,7 +32,7 @@ EXPORTS = [
     "fuse_add_layernorm", "fuse_add_layernorm_ex", "fuse_bias_gelu_residual", "fuse_softmax_rows",
     "fuse_cumsum_scale_rows", "fuse_swiglu_dualgemm",
     "fuse_unfused_workspace_bytes", "fuse_unfused_add_layernorm", "fuse_unfused_bias_gelu_residual",
-    "fuse_unfused_softmax_rows", "fuse_unfused_cumsum_scale_rows", "fuse_unfused_swiglu", "fuse_copy",
+    "fuse_unfused_softmax_rows", "fuse_unfused_cumsum_scale_rows", "fuse_unfused_swiglu", "fuse_copy", "fuse_empty_kernels",
     "fuse_status_string", "fuse_last_hip_error", "fuse_version",
 ]
 
@@ -73,6 +73,7 @@ def load() -> ctypes.CDLL:
         "fuse_unfused_softmax_rows": [vp, vp, i64, i64, f32, i32, vp, sz, vp],
         "fuse_unfused_swiglu": [vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp],
         "fuse_copy": [vp, vp, sz, vp],
+        "fuse_empty_kernels": [i64, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -319,6 +320,11 @@ def fuse_copy(src, dst, stream=None):
     _check(dst, "dst")
     _ok(load().fuse_copy(_ptr(src), _ptr(dst), nb, _stream(stream)), "fuse_copy")
     return dst
+
+
+def fuse_empty_kernels(count, stream=None):
+    """Enqueue `count` launches of the empty probe kernel (launch-cost measurement)."""
+    _ok(load().fuse_empty_kernels(int(count), _stream(stream)), "fuse_empty_kernels")
 
 
 def fuse_version() -> str:

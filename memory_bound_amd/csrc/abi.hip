@@ -473,4 +473,9 @@ fuse_status_t fuse_copy(const void* src, void* dst, size_t bytes, void* stream) 
     return hip_status(fuse::launch_copy(src, dst, bytes, (hipStream_t)stream));
 }
 
+fuse_status_t fuse_empty_kernels(int64_t count, void* stream) {
+    if (count < 0 || count > FUSE_MAX_EMPTY_KERNELS) return FUSE_ERR_BAD_SHAPE;
+    return hip_status(fuse::launch_empty(count, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -1,5 +1,5 @@
 // copy.hip -- plain device copy used to calibrate the roofline (achievable streaming bandwidth and
-// the scale of the hardware byte counters).
+// the scale of the hardware byte counters), and the empty kernel of the launch-cost probe.
 #include "launch.hpp"
 #include "stream_kernels.hpp"
 
@@ -48,6 +48,21 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t str
         hipLaunchKernelGGL(copy_bytes_kernel, dim3((unsigned)((tail + 255) / 256)), dim3(256), 0, stream,
                            (const uint8_t*)src + done, (uint8_t*)dst + done, tail);
         return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Launch-cost probe: a kernel with no work, one 64-thread workgroup per launch, so that what is
+// timed is the cost of getting a kernel from the host call to a finished dispatch.
+// ------------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(64) empty_kernel() {}
+
+hipError_t launch_empty(int64_t count, hipStream_t stream) {
+    for (int64_t i = 0; i < count; i++) {
+        hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, stream);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }

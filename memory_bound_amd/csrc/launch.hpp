@@ -6,21 +6,9 @@
 #include <stdint.h>
 
 #include "fuse_common.hpp"
+#include "row_plan.hpp"
 
 namespace fuse {
-
-// Shape of a register-resident row kernel launch: 128-bit or per-element access, chunks per
-// lane (NV) and waves per row (WPR).
-struct RowPlan {
-    bool vec;
-    int nv;
-    int wpr;
-};
-
-// Plan for a row of n elements of elem_bytes each; `aligned` = every pointer is 16-byte aligned
-// and n * elem_bytes is a multiple of 16.  `wpr_override` > 0 forces the waves per row on the
-// 128-bit path when the resulting chunks per lane stay within the compiled set.
-RowPlan plan_row(int64_t n, int elem_bytes, bool aligned, int wpr_override);
 
 enum class EwOp : int { BiasGeluRes = 0, Add = 1, BiasAdd = 2, Gelu = 3, SiluMul = 4, Scale = 5 };
 
@@ -48,6 +36,7 @@ hipError_t launch_softmax_unfused(const void* x, void* y, int64_t rows, int cols
                                   bool vec, void* e, float* m, float* s, hipStream_t stream);
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+hipError_t launch_empty(int64_t count, hipStream_t stream);
 
 // SwiGLU dual GEMM, bf16.  unfused = true runs the scheme-A pair instead: the same product
 // kernel storing c1 and c2 (bf16, in `c1`, `c2`), then the element-wise SiLU(c1) * c2.

@@ -1,7 +1,7 @@
 // row_plan.hip -- choice of the compiled row-kernel instantiation (lane vector width, chunks per
 // lane, waves per row) for a row length.  Kept apart from the entry points so that the code which
 // decides the launch of the row kernels sits in the files those kernels are built from.
-#include "launch.hpp"
+#include "row_plan.hpp"
 
 namespace fuse {
 

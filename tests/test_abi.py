@@ -216,6 +216,12 @@ def test_copy_validation(lib):
     assert lib.fuse_copy(v(P), v(2 * P), (1 << 40) + 1, None) == SHAPE
 
 
+def test_empty_kernels_validation(lib):
+    assert lib.fuse_empty_kernels(-1, None) == SHAPE
+    assert lib.fuse_empty_kernels((1 << 20) + 1, None) == SHAPE
+    assert lib.fuse_empty_kernels(0, None) == OK  # nothing enqueued
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     from memory_bound_amd import api as libfuse

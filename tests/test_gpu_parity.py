@@ -514,6 +514,21 @@ def test_copy_kernel():
     assert torch.equal(s2, d2)
 
 
+def test_empty_kernels_eager_and_captured():
+    # the launch-cost probe runs to completion eagerly and inside a captured graph
+    announce("empty kernels")
+    api.fuse_empty_kernels(1000)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        api.fuse_empty_kernels(50)
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+    api.fuse_empty_kernels(0)
+
+
 def test_binding_reports_status_errors():
     x = torch.zeros(4, 64, dtype=torch.float16, device="cuda")
     with pytest.raises(api.FuseError):
