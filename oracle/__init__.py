@@ -65,12 +65,15 @@ def _load():
     lib.oracle_cumsum_scale_rows.argtypes = [dp, dp, i64, i64, ctypes.c_double]
     lib.oracle_matmul.argtypes = [dp, dp, dp, i64, i64, i64]
     lib.oracle_swiglu.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64]
+    lib.oracle_gemm_bias_act.argtypes = [dp, dp, dp, dp, i64, i64, i64, ctypes.c_int]
+    lib.oracle_activation.argtypes = [dp, dp, i64, ctypes.c_int]
     lib.oracle_round.argtypes = [dp, dp, i64, ctypes.c_int]
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
     for name in ("oracle_add_layernorm", "oracle_add_layernorm_ex", "oracle_bias_gelu_residual", "oracle_softmax_rows",
                  "oracle_cumsum_scale_rows",
-                 "oracle_matmul", "oracle_swiglu", "oracle_round"):
+                 "oracle_matmul", "oracle_swiglu", "oracle_gemm_bias_act", "oracle_activation",
+                 "oracle_round"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -185,6 +188,39 @@ def swiglu(a, b1, b2) -> np.ndarray:
     c2 = np.empty_like(out)
     _load().oracle_swiglu(_p(a), _p(b1), _p(b2), _p(out), _p(c1), _p(c2), M, N, K)
     return out
+
+
+ACT = {"none": 0, "relu": 1, "gelu": 2, "silu": 3}
+
+
+def gemm_bias_act(x, w, bias, act: str) -> np.ndarray:
+    """y = act(x . W + bias[col]); [P1] §二.1 (GEMM + BiasAdd + Activation)."""
+    x, w = f64(x), f64(w)
+    M, K = x.shape
+    assert w.shape[0] == K
+    N = w.shape[1]
+    b = f64(bias) if bias is not None else None
+    if b is not None:
+        assert b.shape == (N,)
+    y = np.empty((M, N), dtype=np.float64)
+    _load().oracle_gemm_bias_act(_p(x), _p(w), _p(b) if b is not None else None, _p(y), M, N, K, ACT[act])
+    return y
+
+
+def gemm_bias_act_unfused(x, w, bias, act: str, kind: str) -> np.ndarray:
+    """[P1] §二.1's unfused pipeline: the GEMM kernel stores C, the bias kernel stores C + b, the
+    activation kernel reads that; each stored intermediate rounded to the I/O type."""
+    c = round_to(gemm_bias_act(x, w, None, "none"), kind)
+    t = round_to(c + (f64(bias)[None, :] if bias is not None else 0.0), kind)
+    return activation(t, act)
+
+
+def activation(t, act: str) -> np.ndarray:
+    """The activation alone, element-wise (none, ReLU, GELU erf form, SiLU)."""
+    t = f64(t)
+    y = np.empty_like(t)
+    _load().oracle_activation(_p(t), _p(y), t.size, ACT[act])
+    return y
 
 
 _KIND = {"f32": 0, "fp32": 0, "f16": 1, "fp16": 1, "bf16": 2}

@@ -264,6 +264,43 @@ void oracle_swiglu(const double *a, const double *b1, const double *b2,
 }
 
 /*
+ * GEMM + BiasAdd + Activation, the first vertical fusion [P1] §二.1 lists
+ * ("线性变换组合"), with its fused_gemm_bias_relu(x, W1, b1) example:
+ * t = matmul(x, W) + bias[col], then the activation element-wise:
+ *   act 0: none, 1: ReLU (t below zero becomes 0), 2: GELU (erf form),
+ *   3: SiLU.
+ * x [M,K], W [K,N], bias [N] (may be NULL: no bias), y [M,N], row-major.
+ */
+static double activation(double t, int act)
+{
+    if (act == 1)
+        return t < 0.0 ? 0.0 : t;
+    if (act == 2)
+        return gelu_erf(t);
+    if (act == 3)
+        return silu(t);
+    return t;
+}
+
+/* The activation alone, element-wise over n values (the last kernel of the
+ * unfused chain). */
+void oracle_activation(const double *t, double *y, int64_t n, int act)
+{
+    int64_t e;
+    for (e = 0; e < n; e++)
+        y[e] = activation(t[e], act);
+}
+
+void oracle_gemm_bias_act(const double *x, const double *w, const double *bias,
+                          double *y, int64_t M, int64_t N, int64_t K, int act)
+{
+    int64_t e;
+    oracle_matmul(x, w, y, M, N, K);
+    for (e = 0; e < M * N; e++)
+        y[e] = activation(y[e] + (bias ? bias[e % N] : 0.0), act);
+}
+
+/*
  * Round-to-nearest-even of a double to the binary16 / bfloat16 grid, the
  * value returned as a double.  Used where an unfused chain stores an
  * intermediate in the I/O type ([P3] §1 accounts each intermediate at the

@@ -441,3 +441,65 @@ def test_unfused_swiglu_rounds_both_products():
     y = oracle.swiglu_unfused(a, b1, b2, "bf16")
     s1 = float(read_golden("logistic.txt")[1][1])
     assert abs(y[0, 0] - s1) < 1e-15
+
+
+# ------------------------------------------------------------------------------------------------
+# GEMM + BiasAdd + Activation ([P1] §二.1)
+# ------------------------------------------------------------------------------------------------
+
+def test_gemm_bias_act_identity_hits_table_values():
+    # x = I: y = act(W + bias) element by element; W + bias lands on the tabulated points
+    t = np.array([[1.0, -1.0, 3.0, 0.0], [-3.0, 2.5, -0.5, 7.0]])  # targets of W + bias
+    bias = np.array([0.25, -0.5, 1.0, 0.0])
+    w = t - bias[None, :]
+    x = np.eye(2)
+    phi = {float(a): float(b) for a, b in read_golden("normal_cdf.txt")}
+    silu = {float(a): float(b) for a, b in read_golden("logistic.txt")}
+    y = oracle.gemm_bias_act(x, w, bias, "gelu")
+    assert abs(y[0, 0] - 1.0 * phi[1.0]) < 1e-15
+    assert abs(y[0, 2] - 3.0 * phi[3.0]) < 1e-15
+    assert abs(y[1, 0] - (-3.0) * (1 - phi[3.0])) < 1e-15
+    y = oracle.gemm_bias_act(x, w, bias, "silu")
+    assert abs(y[0, 0] - silu[1.0]) < 1e-15 and abs(y[0, 1] - silu[-1.0]) < 1e-15
+    y = oracle.gemm_bias_act(x, w, bias, "relu")
+    np.testing.assert_array_equal(y, np.maximum(t, 0.0))
+    np.testing.assert_array_equal(oracle.gemm_bias_act(x, w, bias, "none"), t)
+
+
+def test_gemm_bias_broadcasts_over_rows_and_rank_one():
+    # M, N, K all different: a transposed operand or a bias indexed by row fails
+    rng = np.random.default_rng(12)
+    M, N, K = 5, 7, 3
+    x = np.round(rng.standard_normal((M, K)) * 8) / 8
+    w = np.round(rng.standard_normal((K, N)) * 8) / 8
+    bias = np.arange(N, dtype=np.float64)
+    y0 = oracle.gemm_bias_act(x, w, None, "none")
+    y1 = oracle.gemm_bias_act(x, w, bias, "none")
+    np.testing.assert_array_equal(y1 - y0, np.broadcast_to(bias, (M, N)))
+    # K = 1: y = act(x_i * w_j + b_j)
+    y = oracle.gemm_bias_act(x[:, :1], w[:1], bias, "relu")
+    np.testing.assert_array_equal(y, np.maximum(x[:, :1] * w[:1] + bias, 0.0))
+
+
+@pytest.mark.parametrize("act", ["none", "relu", "gelu", "silu"])
+def test_gemm_bias_act_torch(act):
+    rng = np.random.default_rng(13)
+    x, w, b = rng.standard_normal((9, 33)), rng.standard_normal((33, 17)), rng.standard_normal(17)
+    t = torch.from_numpy(x) @ torch.from_numpy(w) + torch.from_numpy(b)
+    ref = {"none": t, "relu": F.relu(t), "gelu": F.gelu(t, approximate="none"), "silu": F.silu(t)}[act]
+    np.testing.assert_allclose(oracle.gemm_bias_act(x, w, b, act), ref.numpy(), rtol=1e-13, atol=1e-13)
+
+
+def test_gemm_bias_act_unfused_exact_when_intermediates_fit():
+    # small integers: C and C + b are exact in bf16, so the unfused chain equals the fused result
+    rng = np.random.default_rng(14)
+    x = rng.integers(-3, 4, (6, 5)).astype(np.float64)
+    w = rng.integers(-3, 4, (5, 8)).astype(np.float64)
+    b = rng.integers(-4, 5, 8).astype(np.float64)
+    for act in ("relu", "gelu", "silu"):
+        np.testing.assert_array_equal(oracle.gemm_bias_act_unfused(x, w, b, act, "bf16"),
+                                      oracle.gemm_bias_act(x, w, b, act))
+    # and differs once C needs more than bf16's 8 significant bits
+    w2 = w + 1.0 / 512
+    assert not np.array_equal(oracle.gemm_bias_act_unfused(x, w2, b, "none", "bf16"),
+                              oracle.gemm_bias_act(x, w2, b, "none"))
