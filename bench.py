@@ -159,7 +159,7 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
         work = roofline.workload_work(op, shape, dtype, fused)
         us = ev_ms * 1e3 / n
         r = {"avg_launch_us": round(us, 3), "algorithmic_bytes": work["bytes"]}
-        if op == "swiglu":
+        if "flops" in work:
             tf = work["flops"] / (us * 1e-6) / 1e12
             r.update({"achieved_tflops": round(tf, 1), "peak_tflops": roofline.MFMA_PEAK_TFLOPS["bf16"],
                       "frac": round(tf / roofline.MFMA_PEAK_TFLOPS["bf16"], 4), "bound": "mfma"})
@@ -312,6 +312,31 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
         record("swiglu_unfused_bf16_2048x8960x1536", w.op, w.shape, w.dtype, False, ev, n_launch // 2)
         del ws
 
+        w = synth.WORKLOADS["gemm_relu_bf16_2048x8960x1536"]
+        d = w.inputs()
+        x, wt, bias = d["x"].cuda(), d["w"].cuda(), d["bias"].cuda()
+        y = torch.empty(w.shape[0], w.shape[1], dtype=torch.bfloat16, device="cuda")
+        ws = api._workspace(api.FUSE_OP_GEMM_BIAS_ACT, *w.shape, api.FUSE_BF16, "cuda")
+
+        def gm(i):
+            api.fuse_gemm_bias_act(x, wt, bias, "relu", y=y)
+
+        def gm_unf(i):
+            api.fuse_unfused_gemm_bias_act(x, wt, bias, "relu", y=y, workspace=ws)
+
+        def gm_vendor(i):  # reference only: torch's library GEMM, not part of the path
+            torch.matmul(x, wt, out=y)
+        _, ev = time_launches(torch, stream, gm, n_launch // 2)
+        record("gemm_bias_relu_bf16_2048x8960x1536", w.op, w.shape, w.dtype, True, ev, n_launch // 2)
+        _, ev = time_launches(torch, stream, gm_unf, n_launch // 2)
+        record("gemm_bias_relu_unfused_bf16_2048x8960x1536", w.op, w.shape, w.dtype, False, ev, n_launch // 2,
+               {"note": "GEMM kernel, bias kernel, ReLU kernel"})
+        _, ev = time_launches(torch, stream, gm_vendor, n_launch // 2)
+        record("reference_vendor_gemm_bf16_2048x8960x1536", w.op, w.shape, w.dtype, True, ev, n_launch // 2,
+               {"note": "torch.matmul (hipBLASLt) without bias or activation: context for the MFMA ceiling, "
+                        "not part of the path"})
+        del ws
+
         # copy of the headline's byte count (read 32 MiB + write 16 MiB would not be a copy;
         # copy 24 MiB -> 24 MiB moves the same 48 MiB)
         nbytes = 24 << 20
@@ -435,6 +460,47 @@ def launch_study(torch, api, synth, n_empty=4000, n_graph=1000, n_steps=200):
     return out
 
 
+def selection_study(torch, api, synth, K=1536, n=20):
+    """Fused (scheme B) against unfused (scheme A) SwiGLU over shapes ([P4] 不同场景下的选型建议
+    derives its thresholds from block counts against SM counts): this library's own scheme A
+    (the product kernel storing c1 and c2, then SiLU * product), and for context the library-GEMM
+    form of scheme A (two torch matmuls, then SiLU and product as torch kernels).  Same buffers
+    every launch (the weights stay cache-resident, as they would across a model's layers)."""
+    import torch.nn.functional as F
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.Stream()
+    out = {"cus": cus, "K": K, "shapes": []}
+    with torch.cuda.stream(stream):
+        for M in (256, 1024, 2048):
+            for N in (256, 512, 1024, 2048, 4096, 8960):
+                d = synth.swiglu_inputs(M, N, K, "bf16", seed=M + N)
+                a, b1, b2 = d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda()
+                o = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+                c1, c2 = torch.empty_like(o), torch.empty_like(o)
+                ws = api._workspace(api.FUSE_OP_SWIGLU, M, N, K, api.FUSE_BF16, "cuda")
+
+                def fused(i):
+                    api.fuse_swiglu_dualgemm(a, b1, b2, out=o)
+
+                def ours_a(i):
+                    api.fuse_unfused_swiglu(a, b1, b2, out=o, workspace=ws)
+
+                def lib_a(i):
+                    torch.matmul(a, b1, out=c1)
+                    torch.matmul(a, b2, out=c2)
+                    torch.mul(F.silu(c1), c2, out=o)
+                r = {"M": M, "N": N, "tiles_fused": -(-M // 256) * -(-N // 128)}
+                for name, f in (("fused_us", fused), ("unfused_us", ours_a), ("library_gemm_scheme_a_us", lib_a)):
+                    _, ev = time_launches(torch, stream, f, n)
+                    r[name] = round(ev * 1e3 / n, 2)
+                r["fused_speedup_vs_unfused"] = round(r["unfused_us"] / r["fused_us"], 3)
+                out["shapes"].append(r)
+                log(f"selection M={M} N={N}: fused {r['fused_us']} us, unfused {r['unfused_us']} us, "
+                    f"library-GEMM scheme A {r['library_gemm_scheme_a_us']} us")
+                del ws
+    return out
+
+
 def cpu_baseline(synth, roofline, budget_s=10.0):
     import numpy as np
 
@@ -489,6 +555,7 @@ def main():
     log(f"headline: {h['avg_launch_us']:.2f} us/launch, value {h['value_gbps']:.0f} GB/s")
     rows = {} if a.no_rows else other_rows(torch, api, synth, roofline)
     study = None if a.no_rows else launch_study(torch, api, synth)
+    selection = None if a.no_rows else selection_study(torch, api, synth)
     cpu = None if a.no_cpu else cpu_baseline(synth, roofline)
 
     traffic = read_counters()
@@ -518,6 +585,7 @@ def main():
         "cpu_baseline": cpu,
         "rows": rows,
         "launch_study": study,
+        "selection_study": selection,
     }
     print(json.dumps(line), flush=True)
 

@@ -166,12 +166,32 @@ fuse_status_t fuse_swiglu_dualgemm(const void *a, const void *b1, const void *b2
                                    void *stream);
 
 /*
+ * Fused GEMM + BiasAdd + Activation, the first vertical fusion of [P1] §二.1 ("线性变换组合":
+ * GEMM + BiasAdd + Activation; its example fused_gemm_bias_relu(x, W1, b1) replaces the three
+ * kernels gemm, bias_add, relu):
+ *   y = act(x . w + bias[col]).
+ * Runs on the SwiGLU kernel's matrix-core main loop: each 256 x 256 tile of y is two adjacent
+ * 128-column halves sharing the x tile; the bias and the activation are applied to the fp32
+ * accumulators before the single store.
+ *
+ *   x : [M, K];  w : [K, N];  bias : [N] or NULL (no bias);  y : [M, N], must not overlap the
+ *   others.  dtype FUSE_BF16 (bf16 in and out, fp32 accumulation).
+ *   act : FUSE_ACT_NONE, FUSE_ACT_RELU (a NaN stays NaN), FUSE_ACT_GELU (erf form, as the GELU
+ *   chain) or FUSE_ACT_SILU; another value is FUSE_ERR_BAD_VALUE.
+ * M >= 0, N >= 1, K >= 1, each below 2^31; K or N above 2^21 is FUSE_ERR_UNSUPPORTED.
+ */
+typedef enum { FUSE_ACT_NONE = 0, FUSE_ACT_RELU = 1, FUSE_ACT_GELU = 2, FUSE_ACT_SILU = 3 } fuse_act_t;
+fuse_status_t fuse_gemm_bias_act(const void *x, const void *w, const void *bias, void *y, int64_t M,
+                                 int64_t N, int64_t K, fuse_act_t act, fuse_dtype_t dtype,
+                                 void *stream);
+
+/*
  * Unfused baselines (measurement companions).  Each runs the same computation as separate
  * kernels that store every intermediate in HBM in the I/O type, as the pages' "before
  * fusion" pictures do ([P3] §1: Add kernel writes A, LayerNorm kernel reads it; [P3] intro
  * diagram: BiasAdd, GELU, Residual; [P2] §4.3: row max, exp and sum, divide; [P4] scheme A:
  * one kernel for both products, one for SiLU and the product; [P2] §4.4: the scan kernel
- * storing the prefix sums, then the scale).  They exist so that the
+ * storing the prefix sums, then the scale; [P1] §二.1: gemm, bias_add and activation kernels).  They exist so that the
  * traffic and time fusion saves can be measured, and they are the semantic reference the
  * pages recommend keeping ([P4] 迁移与使用注意事项 §3).
  *
@@ -183,11 +203,12 @@ typedef enum {
     FUSE_OP_BIAS_GELU_RESIDUAL = 1,
     FUSE_OP_SOFTMAX_ROWS = 2,
     FUSE_OP_SWIGLU = 3,
-    FUSE_OP_CUMSUM_SCALE = 4
+    FUSE_OP_CUMSUM_SCALE = 4,
+    FUSE_OP_GEMM_BIAS_ACT = 5
 } fuse_op_t;
 
 /* Workspace bytes for an unfused baseline: (rows, hidden, -) for the row operations,
- * (M, N, K) for SwiGLU.  Returns 0 for invalid arguments. */
+ * (M, N, K) for SwiGLU and GEMM + bias + activation.  Returns 0 for invalid arguments. */
 size_t fuse_unfused_workspace_bytes(fuse_op_t op, int64_t d0, int64_t d1, int64_t d2,
                                     fuse_dtype_t dtype);
 
@@ -213,6 +234,11 @@ fuse_status_t fuse_unfused_swiglu(const void *a, const void *b1, const void *b2,
 fuse_status_t fuse_unfused_cumsum_scale_rows(const void *x, void *y, int64_t rows, int64_t cols,
                                              float scale, fuse_dtype_t dtype, void *workspace,
                                              size_t workspace_bytes, void *stream);
+
+fuse_status_t fuse_unfused_gemm_bias_act(const void *x, const void *w, const void *bias, void *y,
+                                         int64_t M, int64_t N, int64_t K, fuse_act_t act,
+                                         fuse_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                                         void *stream);
 
 /*
  * Plain device-to-device copy of `bytes` bytes, the calibration kernel of the roofline: its

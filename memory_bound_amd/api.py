@@ -21,7 +21,9 @@ _DTYPE_CODE = {torch.float32: FUSE_F32, torch.float16: FUSE_F16, torch.bfloat16:
 
 FUSE_LN_RELU = 1
 
-FUSE_OP_ADD_LAYERNORM, FUSE_OP_BIAS_GELU_RESIDUAL, FUSE_OP_SOFTMAX_ROWS, FUSE_OP_SWIGLU, FUSE_OP_CUMSUM_SCALE = 0, 1, 2, 3, 4
+FUSE_OP_ADD_LAYERNORM, FUSE_OP_BIAS_GELU_RESIDUAL, FUSE_OP_SOFTMAX_ROWS, FUSE_OP_SWIGLU = 0, 1, 2, 3
+FUSE_OP_CUMSUM_SCALE, FUSE_OP_GEMM_BIAS_ACT = 4, 5
+FUSE_ACT = {"none": 0, "relu": 1, "gelu": 2, "silu": 3}
 
 STATUS = {0: "FUSE_OK", 1: "FUSE_ERR_NULL_PTR", 2: "FUSE_ERR_BAD_SHAPE", 3: "FUSE_ERR_BAD_DTYPE",
           4: "FUSE_ERR_BAD_VALUE", 5: "FUSE_ERR_ALIAS", 6: "FUSE_ERR_UNSUPPORTED",
@@ -30,7 +32,7 @@ STATUS = {0: "FUSE_OK", 1: "FUSE_ERR_NULL_PTR", 2: "FUSE_ERR_BAD_SHAPE", 3: "FUS
 # Every symbol include/libfuse.h declares.
 EXPORTS = [
     "fuse_add_layernorm", "fuse_add_layernorm_ex", "fuse_bias_gelu_residual", "fuse_softmax_rows",
-    "fuse_cumsum_scale_rows", "fuse_swiglu_dualgemm",
+    "fuse_cumsum_scale_rows", "fuse_swiglu_dualgemm", "fuse_gemm_bias_act", "fuse_unfused_gemm_bias_act",
     "fuse_unfused_workspace_bytes", "fuse_unfused_add_layernorm", "fuse_unfused_bias_gelu_residual",
     "fuse_unfused_softmax_rows", "fuse_unfused_cumsum_scale_rows", "fuse_unfused_swiglu", "fuse_copy", "fuse_empty_kernels",
     "fuse_status_string", "fuse_last_hip_error", "fuse_version",
@@ -68,6 +70,8 @@ def load() -> ctypes.CDLL:
         "fuse_cumsum_scale_rows": [vp, vp, i64, i64, f32, i32, vp],
         "fuse_unfused_cumsum_scale_rows": [vp, vp, i64, i64, f32, i32, vp, sz, vp],
         "fuse_swiglu_dualgemm": [vp, vp, vp, vp, i64, i64, i64, i32, vp],
+        "fuse_gemm_bias_act": [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp],
+        "fuse_unfused_gemm_bias_act": [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp],
         "fuse_unfused_add_layernorm": [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp, sz, vp],
         "fuse_unfused_bias_gelu_residual": [vp, vp, vp, vp, i64, i64, i32, vp, sz, vp],
         "fuse_unfused_softmax_rows": [vp, vp, i64, i64, f32, i32, vp, sz, vp],
@@ -243,6 +247,21 @@ def fuse_swiglu_dualgemm(a, b1, b2, out=None, stream=None):
     return out
 
 
+def fuse_gemm_bias_act(x, w, bias=None, act="relu", y=None, stream=None):
+    """y = act(x @ w + bias); x [M,K], w [K,N], bias [N] or None, bf16; act none/relu/gelu/silu."""
+    M, K = x.shape
+    N = w.shape[1]
+    _check(x, "x")
+    _check(w, "w", x.dtype, (K, N))
+    _check(bias, "bias", x.dtype, (N,))
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _check(y, "y", x.dtype, (M, N))
+    _ok(load().fuse_gemm_bias_act(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), M, N, K, FUSE_ACT[act], _dt(x),
+                                  _stream(stream)), "fuse_gemm_bias_act")
+    return y
+
+
 # ------------------------------------------------------------------------------------------------
 # unfused baselines (the workspace is allocated here unless given as (tensor, ptr, bytes))
 # ------------------------------------------------------------------------------------------------
@@ -309,6 +328,18 @@ def fuse_unfused_swiglu(a, b1, b2, out=None, workspace=None, stream=None):
 def fuse_unfused_workspace_bytes(op: int, d0: int, d1: int, d2: int, dtype) -> int:
     code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     return int(load().fuse_unfused_workspace_bytes(op, d0, d1, d2, code))
+
+
+def fuse_unfused_gemm_bias_act(x, w, bias=None, act="relu", y=None, workspace=None, stream=None):
+    M, K = x.shape
+    N = w.shape[1]
+    _check(x, "x")
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    ws = workspace or _workspace(FUSE_OP_GEMM_BIAS_ACT, M, N, K, _dt(x), x.device)
+    _ok(load().fuse_unfused_gemm_bias_act(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), M, N, K, FUSE_ACT[act], _dt(x),
+                                          ws[1], ws[2], _stream(stream)), "fuse_unfused_gemm_bias_act")
+    return y
 
 
 def fuse_copy(src, dst, stream=None):

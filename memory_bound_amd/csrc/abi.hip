@@ -322,6 +322,39 @@ fuse_status_t fuse_swiglu_dualgemm(const void* a, const void* b1, const void* b2
 }
 
 // ------------------------------------------------------------------------------------------------
+// GEMM + bias + activation
+// ------------------------------------------------------------------------------------------------
+
+static fuse_status_t check_gemm(const void* x, const void* w, const void* bias, void* y, int64_t M, int64_t N,
+                                int64_t K, fuse_act_t act, fuse_dtype_t dt) {
+    if (!valid_dtype(dt) || dt != FUSE_BF16) return FUSE_ERR_BAD_DTYPE;
+    if (act != FUSE_ACT_NONE && act != FUSE_ACT_RELU && act != FUSE_ACT_GELU && act != FUSE_ACT_SILU)
+        return FUSE_ERR_BAD_VALUE;
+    if (M < 0 || N < 1 || K < 1) return FUSE_ERR_BAD_SHAPE;
+    const int64_t lim = INT64_C(0x7fffffff);
+    if (M > lim || N > lim || K > lim) return FUSE_ERR_BAD_SHAPE;
+    if (K > (INT64_C(1) << 21) || N > (INT64_C(1) << 21)) return FUSE_ERR_UNSUPPORTED;
+    size_t xb, wb, yb;
+    if (!tensor_bytes(M, K, 2, &xb) || !tensor_bytes(K, N, 2, &wb) || !tensor_bytes(M, N, 2, &yb))
+        return FUSE_ERR_BAD_SHAPE;
+    if (M == 0) return FUSE_OK;
+    if (!x || !w || !y) return FUSE_ERR_NULL_PTR;
+    if (!elem_aligned(x, 2) || !elem_aligned(w, 2) || !elem_aligned(y, 2) || (bias && !elem_aligned(bias, 2)))
+        return FUSE_ERR_MISALIGNED;
+    if (overlaps(y, yb, x, xb) || overlaps(y, yb, w, wb) || overlaps(y, yb, bias, bias ? (size_t)N * 2 : 0))
+        return FUSE_ERR_ALIAS;
+    return FUSE_OK;
+}
+
+fuse_status_t fuse_gemm_bias_act(const void* x, const void* w, const void* bias, void* y, int64_t M, int64_t N,
+                                 int64_t K, fuse_act_t act, fuse_dtype_t dt, void* stream) {
+    fuse_status_t st = check_gemm(x, w, bias, y, M, N, K, act, dt);
+    if (st != FUSE_OK || M == 0) return st;
+    return hip_status(fuse::launch_gemm_bias_act(x, w, bias, y, (int)M, (int)N, (int)K, (int)act,
+                                                 (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------------------------------------
 // Unfused baselines
 // ------------------------------------------------------------------------------------------------
 
@@ -345,6 +378,9 @@ size_t fuse_unfused_workspace_bytes(fuse_op_t op, int64_t d0, int64_t d1, int64_
         case FUSE_OP_CUMSUM_SCALE:
             if (!tensor_bytes(d0, d1, elem_bytes(dt), &tb)) return 0;
             return round256(tb);
+        case FUSE_OP_GEMM_BIAS_ACT:
+            if (dt != FUSE_BF16 || !tensor_bytes(d0, d1, 2, &tb)) return 0;
+            return 2 * round256(tb);
     }
     return 0;
 }
@@ -459,6 +495,23 @@ fuse_status_t fuse_unfused_swiglu(const void* a, const void* b1, const void* b2,
     void* c2 = (char*)ws + round256(ob);
     return hip_status(fuse::launch_swiglu_unfused(a, b1, b2, out, (int)M, (int)N, (int)K, c1, c2,
                                                   (hipStream_t)stream));
+}
+
+fuse_status_t fuse_unfused_gemm_bias_act(const void* x, const void* w, const void* bias, void* y, int64_t M,
+                                         int64_t N, int64_t K, fuse_act_t act, fuse_dtype_t dt, void* ws,
+                                         size_t ws_bytes, void* stream) {
+    fuse_status_t st = check_gemm(x, w, bias, y, M, N, K, act, dt);
+    if (st != FUSE_OK || M == 0) return st;
+    const size_t need = fuse_unfused_workspace_bytes(FUSE_OP_GEMM_BIAS_ACT, M, N, K, dt);
+    if (!workspace_ok(ws, ws_bytes, need)) return FUSE_ERR_WORKSPACE;
+    const size_t xb = (size_t)M * K * 2, wb = (size_t)K * N * 2, yb = (size_t)M * N * 2;
+    if (overlaps(ws, need, x, xb) || overlaps(ws, need, w, wb) || overlaps(ws, need, y, yb) ||
+        overlaps(ws, need, bias, bias ? (size_t)N * 2 : 0))
+        return FUSE_ERR_WORKSPACE;
+    void* c = ws;
+    void* t = (char*)ws + round256(yb);
+    return hip_status(fuse::launch_gemm_bias_act_unfused(x, w, bias, y, (int)M, (int)N, (int)K, (int)act, c, t,
+                                                         (hipStream_t)stream));
 }
 
 // ------------------------------------------------------------------------------------------------

@@ -10,7 +10,7 @@
 
 namespace fuse {
 
-enum class EwOp : int { BiasGeluRes = 0, Add = 1, BiasAdd = 2, Gelu = 3, SiluMul = 4, Scale = 5 };
+enum class EwOp : int { BiasGeluRes = 0, Add = 1, BiasAdd = 2, Gelu = 3, SiluMul = 4, Scale = 5, Relu = 6, Silu = 7 };
 
 template <DT D>
 hipError_t launch_add_layernorm(const void* x, const void* res, const void* gamma, const void* beta,
@@ -44,5 +44,12 @@ hipError_t launch_swiglu(const void* a, const void* b1, const void* b2, void* ou
                          int K, hipStream_t stream);
 hipError_t launch_swiglu_unfused(const void* a, const void* b1, const void* b2, void* out, int M,
                                  int N, int K, void* c1, void* c2, hipStream_t stream);
+
+// GEMM + bias + activation, bf16: y = act(x . w + bias) with act 0 none, 1 ReLU, 2 GELU (erf),
+// 3 SiLU; bias may be null.  The unfused chain stores C (and T = C + bias) in `c` and `t`.
+hipError_t launch_gemm_bias_act(const void* x, const void* w, const void* bias, void* y, int M, int N, int K,
+                                int act, hipStream_t stream);
+hipError_t launch_gemm_bias_act_unfused(const void* x, const void* w, const void* bias, void* y, int M, int N,
+                                        int K, int act, void* c, void* t, hipStream_t stream);
 
 }  // namespace fuse

@@ -153,6 +153,8 @@ hipError_t launch_ew(EwOp op, bool vec, const void* a, const void* b, const void
         case EwOp::Gelu: by_vec.template operator()<OpGelu>(); break;
         case EwOp::SiluMul: by_vec.template operator()<OpSiluMul>(); break;
         case EwOp::Scale: by_vec.template operator()<OpScale>(); break;
+        case EwOp::Relu: by_vec.template operator()<OpRelu>(); break;
+        case EwOp::Silu: by_vec.template operator()<OpSilu>(); break;
     }
     return err;
 }

@@ -35,6 +35,14 @@ struct OpSiluMul {  // SiLU(c1) * c2 (second kernel of the unfused SwiGLU)
     static constexpr bool USE_B = true, USE_C = false;
     __device__ __forceinline__ float operator()(float a, float b, float) const { return silu(a) * b; }
 };
+struct OpRelu {  // activation kernel of the unfused GEMM + bias + ReLU (a NaN stays NaN)
+    static constexpr bool USE_B = false, USE_C = false;
+    __device__ __forceinline__ float operator()(float a, float, float) const { return a < 0.0f ? 0.0f : a; }
+};
+struct OpSilu {  // activation kernel of the unfused GEMM + bias + SiLU
+    static constexpr bool USE_B = false, USE_C = false;
+    __device__ __forceinline__ float operator()(float a, float, float) const { return silu(a); }
+};
 struct OpScale {  // alpha * s (second kernel of the unfused cumsum + scale)
     static constexpr bool USE_B = false, USE_C = false;
     float alpha;

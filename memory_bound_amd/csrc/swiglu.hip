@@ -82,12 +82,12 @@ struct Tile {
 };
 
 // Bijective remap of the dispatch index so that XCD x (= bid % 8) gets a contiguous tile range.
-__device__ __forceinline__ Tile tile_of(int bid, int tiles_m, int tiles_n) {
+__device__ __forceinline__ Tile tile_of(int bid, int tiles_m, int tiles_n, int bn_step) {
     const int nt = tiles_m * tiles_n;
     const int xcd = bid % NUM_XCD, slot = bid / NUM_XCD;
     const int q = nt / NUM_XCD, rem = nt % NUM_XCD;
     const int t = xcd * q + min(xcd, rem) + slot;
-    return {(t % tiles_m) * BM, (t / tiles_m) * BN};
+    return {(t % tiles_m) * BM, (t / tiles_m) * bn_step};
 }
 
 // Global -> registers for one K step.  The a resource spans the tile's valid rows and the b
@@ -95,7 +95,7 @@ __device__ __forceinline__ Tile tile_of(int bid, int tiles_m, int tiles_n) {
 // are sent to an offset outside the resource.  All loads are unconditional.
 template <bool ALIGNED>
 __device__ __forceinline__ void load_stage(const uint16_t* a, const uint16_t* b1, const uint16_t* b2,
-                                           int M, int N, int K, int m0, int n0, int k0,
+                                           int M, int N, int K, int nlim2, int m0, int n0, int k0,
                                            uint4 (&ra)[8], uint4 (&rb)[8]) {
     const int t = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -113,14 +113,16 @@ __device__ __forceinline__ void load_stage(const uint16_t* a, const uint16_t* b1
     {
         // waves 0-1 load b1, waves 2-3 load b2: the 8 x 8 block (kb, nb), kb = bt>>4, nb = bt&15
         const int krows = min(K - k0, BK);
+        // columns of b2 may end before N (when b2 is b1 shifted by 128 columns)
         const rsrc_t r = make_rsrc((wave < 2 ? b1 : b2) + (int64_t)k0 * N, (uint32_t)krows * (uint32_t)N * 2u);
+        const int nlim = wave < 2 ? N : nlim2;
         const int bt = t & 127;
         const int n = n0 + 8 * (bt & 15), kb = 8 * (bt >> 4);
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const uint32_t e0 = (uint32_t)(kb + i) * (uint32_t)N + (uint32_t)n;
-            if (ALIGNED) rb[i] = bload16(r, n < N ? e0 * 2u : OOB);
-            else rb[i] = load8_guarded(r, e0, N - n);
+            if (ALIGNED) rb[i] = bload16(r, n < nlim ? e0 * 2u : OOB);
+            else rb[i] = load8_guarded(r, e0, nlim - n);
         }
     }
 }
@@ -175,14 +177,98 @@ __device__ __forceinline__ void mfma_slice(const Frags& f, floatx16 (&acc1)[WM][
         }
 }
 
-template <bool ALIGNED, bool STORE_PRODUCTS>
+// What one launch of the dual-product kernels computes.  Both products share the a tile; b1 and
+// b2 are two [K, *] operands with row stride N: the two SwiGLU weight matrices, or one GEMM
+// weight read as two adjacent 128-column halves of each 256-column tile (b2 = b1 + 128).
+constexpr int MODE_SWIGLU = 0;    // out = SiLU(c1) * c2
+constexpr int MODE_PRODUCTS = 1;  // c1, c2 stored as they are (first kernel of the unfused SwiGLU)
+constexpr int MODE_BIAS = 2;      // MODE_BIAS + act: out = act(c + bias[col]) for both halves
+constexpr int ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_SILU = 3;
+
+struct DualArgs {
+    const uint16_t* a;
+    const uint16_t* b1;
+    const uint16_t* b2;
+    uint16_t* out;         // [M, N]
+    uint16_t* c1;          // products mode
+    uint16_t* c2;
+    const uint16_t* bias;  // bias mode: [N], or null for none
+    int M, N, K;           // N is also the row stride of b1, b2 and every output
+    int nlim2;             // columns of b2 that exist: N, or N - 128 when b2 = b1 + 128
+    int tiles_m, tiles_n, bn_step;
+};
+
+template <int ACT> __device__ __forceinline__ float activation(float t) {
+    if constexpr (ACT == ACT_RELU) return t < 0.0f ? 0.0f : t;  // a NaN stays NaN
+    else if constexpr (ACT == ACT_GELU) return gelu_erf(t);
+    else if constexpr (ACT == ACT_SILU) return silu(t);
+    else return t;
+}
+
+// Stores the tile at (m0, n0).  Block (i, j) element r of lane l sits at row 8 (r/4) + 4 (l/32) +
+// r%4, column l%32 of the block; the wave's blocks start at row 128 wm, column 64 wn of each
+// product's 128-column tile.  Rows past M and columns past N fall outside the store resources.
+template <int MODE>
+__device__ __forceinline__ void store_tile(const DualArgs& p, const floatx16 (&acc1)[WM][WN],
+                                           const floatx16 (&acc2)[WM][WN], int m0, int n0, int wm, int wn,
+                                           int lane) {
+    const int mrows = min(p.M - m0, BM);
+    const uint32_t out_bytes = (uint32_t)mrows * (uint32_t)p.N * 2u;
+    if constexpr (MODE == MODE_SWIGLU || MODE == MODE_PRODUCTS) {
+        constexpr bool PROD = MODE == MODE_PRODUCTS;
+        const rsrc_t ro = make_rsrc((PROD ? p.c1 : p.out) + (int64_t)m0 * p.N, out_bytes);
+        const rsrc_t ro2 = make_rsrc(PROD ? p.c2 + (int64_t)m0 * p.N : p.out, PROD ? out_bytes : 0u);
+#pragma unroll
+        for (int i = 0; i < WM; i++)
+#pragma unroll
+            for (int j = 0; j < WN; j++) {
+                const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    const uint32_t off = col < p.N ? ((uint32_t)row * (uint32_t)p.N + (uint32_t)col) * 2u : OOB;
+                    const float c1 = acc1[i][j][r], c2 = acc2[i][j][r];
+                    if constexpr (PROD) {
+                        bstore_b16<AUX_STREAM>(ro, off, f32_to_bf16(c1));
+                        bstore_b16<AUX_STREAM>(ro2, off, f32_to_bf16(c2));
+                    } else {
+                        bstore_b16<AUX_STREAM>(ro, off, f32_to_bf16(silu(c1) * c2));
+                    }
+                }
+            }
+    } else {
+        constexpr int ACT = MODE - MODE_BIAS;
+        const rsrc_t ro = make_rsrc(p.out + (int64_t)m0 * p.N, out_bytes);
+        const rsrc_t rbias = make_rsrc(p.bias ? p.bias : p.out, p.bias ? (uint32_t)p.N * 2u : 0u);  // none: zeros
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int j = 0; j < WN; j++) {
+                const int col = n0 + 128 * h + 64 * wn + 32 * j + (lane & 31);
+                const bool in = col < p.N;
+                const float bv = bf16_to_f32(bload_b16(rbias, in ? (uint32_t)col * 2u : OOB));
+#pragma unroll
+                for (int i = 0; i < WM; i++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                        const uint32_t off = in ? ((uint32_t)row * (uint32_t)p.N + (uint32_t)col) * 2u : OOB;
+                        const float c = h == 0 ? acc1[i][j][r] : acc2[i][j][r];
+                        bstore_b16<AUX_STREAM>(ro, off, f32_to_bf16(activation<ACT>(c + bv)));
+                    }
+            }
+    }
+}
+
+template <bool ALIGNED, int MODE>
 __global__ void __launch_bounds__(THREADS, 1)
-swiglu_kernel(const uint16_t* a, const uint16_t* b1, const uint16_t* b2, uint16_t* out,
-              uint16_t* c1_out, uint16_t* c2_out, int M, int N, int K, int tiles_m, int tiles_n) {
+swiglu_kernel(DualArgs p) {
+    const uint16_t *a = p.a, *b1 = p.b1, *b2 = p.b2;
+    const int M = p.M, N = p.N, K = p.K;
     constexpr int STAGE = (BM + 2 * BN) * BK;  // bf16 elements per LDS stage (64 KiB)
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
 
-    const Tile tile = tile_of(blockIdx.x, tiles_m, tiles_n);
+    const Tile tile = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, p.bn_step);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -197,9 +283,9 @@ swiglu_kernel(const uint16_t* a, const uint16_t* b1, const uint16_t* b2, uint16_
 
     const int kt_n = (K + BK - 1) / BK;
     uint4 ra[8], rb[8];
-    load_stage<ALIGNED>(a, b1, b2, M, N, K, tile.m0, tile.n0, 0, ra, rb);
+    load_stage<ALIGNED>(a, b1, b2, M, N, K, p.nlim2, tile.m0, tile.n0, 0, ra, rb);
     store_stage(lds, lds + BM * BK, lds + (BM + BN) * BK, ra, rb);
-    if (kt_n > 1) load_stage<ALIGNED>(a, b1, b2, M, N, K, tile.m0, tile.n0, BK, ra, rb);
+    if (kt_n > 1) load_stage<ALIGNED>(a, b1, b2, M, N, K, p.nlim2, tile.m0, tile.n0, BK, ra, rb);
     __syncthreads();
 
     Frags f[2];
@@ -219,7 +305,7 @@ swiglu_kernel(const uint16_t* a, const uint16_t* b1, const uint16_t* b2, uint16_
                 uint16_t* na = lds + ((kt + 1) & 1) * STAGE;
                 store_stage(na, na + BM * BK, na + (BM + BN) * BK, ra, rb);
                 if (kt + 2 < kt_n)
-                    load_stage<ALIGNED>(a, b1, b2, M, N, K, tile.m0, tile.n0, (kt + 2) * BK, ra, rb);
+                    load_stage<ALIGNED>(a, b1, b2, M, N, K, p.nlim2, tile.m0, tile.n0, (kt + 2) * BK, ra, rb);
             }
         }
         __syncthreads();
@@ -229,31 +315,7 @@ swiglu_kernel(const uint16_t* a, const uint16_t* b1, const uint16_t* b2, uint16_
         }
     }
 
-    // Epilogue.  Block (i, j) element r of lane l sits at row 8 (r/4) + 4 (l/32) + r%4, column l%32
-    // of the block.  Stores go through a resource spanning the tile's valid rows; columns past N
-    // are sent out of range, so there is no branch per element.
-    const int mrows = min(M - tile.m0, BM);
-    const uint32_t out_bytes = (uint32_t)mrows * (uint32_t)N * 2u;
-    const rsrc_t ro = make_rsrc(STORE_PRODUCTS ? c1_out + (int64_t)tile.m0 * N : out + (int64_t)tile.m0 * N, out_bytes);
-    const rsrc_t ro2 = make_rsrc(STORE_PRODUCTS ? c2_out + (int64_t)tile.m0 * N : out, STORE_PRODUCTS ? out_bytes : 0u);
-#pragma unroll
-    for (int i = 0; i < WM; i++)
-#pragma unroll
-        for (int j = 0; j < WN; j++) {
-            const int col = tile.n0 + 64 * wn + 32 * j + (lane & 31);
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const uint32_t off = col < N ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u : OOB;
-                const float c1 = acc1[i][j][r], c2 = acc2[i][j][r];
-                if constexpr (STORE_PRODUCTS) {
-                    bstore_b16<AUX_STREAM>(ro, off, f32_to_bf16(c1));
-                    bstore_b16<AUX_STREAM>(ro2, off, f32_to_bf16(c2));
-                } else {
-                    bstore_b16<AUX_STREAM>(ro, off, f32_to_bf16(silu(c1) * c2));
-                }
-            }
-        }
+    store_tile<MODE>(p, acc1, acc2, tile.m0, tile.n0, wm, wn, lane);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -404,16 +466,17 @@ __device__ __forceinline__ void slice_step(const Frags& f, Frags& nx, const char
     }
 }
 
-template <int S, bool STORE_PRODUCTS>
+template <int S, int MODE>
 __global__ void __launch_bounds__(THREADS, 1)
-swiglu_direct_kernel(const uint16_t* a, const uint16_t* b1, const uint16_t* b2, uint16_t* out,
-                     uint16_t* c1_out, uint16_t* c2_out, int M, int N, int K, int tiles_m, int tiles_n) {
+swiglu_direct_kernel(DualArgs p) {
+    const uint16_t *a = p.a, *b1 = p.b1, *b2 = p.b2;
+    const int N = p.N, K = p.K;
     using C = DirectCfg;
     constexpr int LPS = C::LOADS_PER_STAGE;
     static_assert(S >= 3 && S * C::STAGE_BYTES <= 160 * 1024, "ring of 3 to 5 stages of 32 KiB");
     __shared__ __attribute__((aligned(1024))) char lds[S * C::STAGE_BYTES];
 
-    const Tile tile = tile_of(blockIdx.x, tiles_m, tiles_n);
+    const Tile tile = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, p.bn_step);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -462,86 +525,109 @@ swiglu_direct_kernel(const uint16_t* a, const uint16_t* b1, const uint16_t* b2, 
     }
     wait_vmcnt<0>();  // no load may still be writing this workgroup's LDS when it ends
 
-    // Epilogue.  Block (i, j) element r of lane l sits at row 8 (r/4) + 4 (l/32) + r%4, column l%32
-    // of the block.
-    const uint32_t out_bytes = (uint32_t)BM * (uint32_t)N * 2u;
-    const rsrc_t ro = make_rsrc(STORE_PRODUCTS ? c1_out + (int64_t)tile.m0 * N : out + (int64_t)tile.m0 * N, out_bytes);
-    const rsrc_t ro2 = make_rsrc(STORE_PRODUCTS ? c2_out + (int64_t)tile.m0 * N : out, STORE_PRODUCTS ? out_bytes : 0u);
-#pragma unroll
-    for (int i = 0; i < WM; i++)
-#pragma unroll
-        for (int j = 0; j < WN; j++) {
-            const int col = tile.n0 + 64 * wn + 32 * j + (lane & 31);
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const uint32_t off = ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u;
-                const float c1 = acc1[i][j][r], c2 = acc2[i][j][r];
-                if constexpr (STORE_PRODUCTS) {
-                    bstore_b16<AUX_STREAM>(ro, off, f32_to_bf16(c1));
-                    bstore_b16<AUX_STREAM>(ro2, off, f32_to_bf16(c2));
-                } else {
-                    bstore_b16<AUX_STREAM>(ro, off, f32_to_bf16(silu(c1) * c2));
-                }
-            }
-        }
+    store_tile<MODE>(p, acc1, acc2, tile.m0, tile.n0, wm, wn, lane);
 }
 
 // Ring depth of the full-tile kernel (FUSE_SWIGLU_STAGES, 3 to 5, overrides the default for tuning
 // sweeps; five stages take all 160 KiB of LDS).  0: no full-tile kernel for this shape.
-int direct_stages(int M, int N, int K, bool aligned) {
-    if (!aligned || M % BM != 0 || N % BN != 0 || K % DirectCfg::BKD != 0) return 0;
+int direct_stages(int M, int N, int K, bool aligned, int tile_cols) {
+    if (!aligned || M % BM != 0 || N % tile_cols != 0 || K % DirectCfg::BKD != 0) return 0;
     if (getenv("FUSE_SWIGLU_GENERAL") != nullptr) return 0;
     const char* s = getenv("FUSE_SWIGLU_STAGES");
     const int st = s ? atoi(s) : 4;
     return (st >= 3 && st <= 5) ? st : 4;
 }
 
-template <bool STORE_PRODUCTS>
-hipError_t launch(const void* a, const void* b1, const void* b2, void* out, void* c1, void* c2, int M,
-                  int N, int K, hipStream_t stream) {
-    const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-    const bool aligned = (K % 8 == 0) && (N % 8 == 0) && (((uintptr_t)a | (uintptr_t)b1 | (uintptr_t)b2) & 15u) == 0;
-    const dim3 grid((unsigned)(tm * tn)), block(THREADS);
-    const int st = direct_stages(M, N, K, aligned);
-    if (st != 0) {
-#define FUSE_DIRECT(SV)                                                                               \
-    hipLaunchKernelGGL((swiglu_direct_kernel<SV, STORE_PRODUCTS>), grid, block, 0, stream,              \
-                       (const uint16_t*)a, (const uint16_t*)b1, (const uint16_t*)b2, (uint16_t*)out,     \
-                       (uint16_t*)c1, (uint16_t*)c2, M, N, K, tm, tn)
-        if (st == 3) FUSE_DIRECT(3);
-        else if (st == 5) FUSE_DIRECT(5);
-        else FUSE_DIRECT(4);
-#undef FUSE_DIRECT
-        return hipGetLastError();
-    }
-    if (aligned)
-        hipLaunchKernelGGL((swiglu_kernel<true, STORE_PRODUCTS>), grid, block, 0, stream, (const uint16_t*)a,
-                           (const uint16_t*)b1, (const uint16_t*)b2, (uint16_t*)out, (uint16_t*)c1,
-                           (uint16_t*)c2, M, N, K, tm, tn);
-    else
-        hipLaunchKernelGGL((swiglu_kernel<false, STORE_PRODUCTS>), grid, block, 0, stream, (const uint16_t*)a,
-                           (const uint16_t*)b1, (const uint16_t*)b2, (uint16_t*)out, (uint16_t*)c1,
-                           (uint16_t*)c2, M, N, K, tm, tn);
+// Launch of the dual-product kernels: `tile_cols` output columns per tile (128 for SwiGLU, whose
+// two products cover the same 128 columns; 256 for a GEMM, whose two halves are adjacent).
+template <int MODE>
+hipError_t launch(DualArgs p, int tile_cols, hipStream_t stream) {
+    p.tiles_m = (p.M + BM - 1) / BM;
+    p.tiles_n = (p.N + tile_cols - 1) / tile_cols;
+    p.bn_step = tile_cols;
+    if ((int64_t)p.tiles_m * p.tiles_n > 0x7fffffff) return hipErrorInvalidValue;
+    const bool aligned = (p.K % 8 == 0) && (p.N % 8 == 0) &&
+                         (((uintptr_t)p.a | (uintptr_t)p.b1 | (uintptr_t)p.b2) & 15u) == 0;
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(THREADS);
+    const int st = direct_stages(p.M, p.N, p.K, aligned, tile_cols);
+    if (st == 3) hipLaunchKernelGGL((swiglu_direct_kernel<3, MODE>), grid, block, 0, stream, p);
+    else if (st == 4) hipLaunchKernelGGL((swiglu_direct_kernel<4, MODE>), grid, block, 0, stream, p);
+    else if (st == 5) hipLaunchKernelGGL((swiglu_direct_kernel<5, MODE>), grid, block, 0, stream, p);
+    else if (aligned) hipLaunchKernelGGL((swiglu_kernel<true, MODE>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((swiglu_kernel<false, MODE>), grid, block, 0, stream, p);
     return hipGetLastError();
+}
+
+DualArgs dual_args(const void* a, const void* b1, const void* b2, int M, int N, int K) {
+    DualArgs p{};
+    p.a = (const uint16_t*)a;
+    p.b1 = (const uint16_t*)b1;
+    p.b2 = (const uint16_t*)b2;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.nlim2 = N;
+    return p;
 }
 
 }  // namespace
 
 hipError_t launch_swiglu(const void* a, const void* b1, const void* b2, void* out, int M, int N, int K,
                          hipStream_t stream) {
-    if ((int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN) > 0x7fffffff) return hipErrorInvalidValue;
-    return launch<false>(a, b1, b2, out, nullptr, nullptr, M, N, K, stream);
+    DualArgs p = dual_args(a, b1, b2, M, N, K);
+    p.out = (uint16_t*)out;
+    return launch<MODE_SWIGLU>(p, BN, stream);
 }
 
 hipError_t launch_swiglu_unfused(const void* a, const void* b1, const void* b2, void* out, int M, int N,
                                  int K, void* c1, void* c2, hipStream_t stream) {
-    if ((int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN) > 0x7fffffff) return hipErrorInvalidValue;
-    hipError_t e = launch<true>(a, b1, b2, nullptr, c1, c2, M, N, K, stream);
+    DualArgs p = dual_args(a, b1, b2, M, N, K);
+    p.c1 = (uint16_t*)c1;
+    p.c2 = (uint16_t*)c2;
+    hipError_t e = launch<MODE_PRODUCTS>(p, BN, stream);
     if (e != hipSuccess) return e;
     // second kernel of scheme A: out = SiLU(c1) * c2, element-wise over M*N
     const bool vec = (N % 8 == 0) && (((uintptr_t)out | (uintptr_t)c1 | (uintptr_t)c2) & 15u) == 0;
     return launch_ew<DT::BF16>(EwOp::SiluMul, vec, c1, c2, nullptr, out, (int64_t)M * N, N, 4, stream);
+}
+
+// GEMM + bias + activation on the same kernels: each 256 x 256 output tile is computed as two
+// 128-column halves, the second product reading the weight shifted by 128 columns.
+hipError_t launch_gemm_bias_act(const void* x, const void* w, const void* bias, void* y, int M, int N, int K,
+                                int act, hipStream_t stream) {
+    DualArgs p = dual_args(x, w, (const uint16_t*)w + 128, M, N, K);
+    p.out = (uint16_t*)y;
+    p.bias = (const uint16_t*)bias;
+    p.nlim2 = N > 128 ? N - 128 : 0;
+    switch (act) {
+        case ACT_NONE: return launch<MODE_BIAS + ACT_NONE>(p, 2 * BN, stream);
+        case ACT_RELU: return launch<MODE_BIAS + ACT_RELU>(p, 2 * BN, stream);
+        case ACT_GELU: return launch<MODE_BIAS + ACT_GELU>(p, 2 * BN, stream);
+        case ACT_SILU: return launch<MODE_BIAS + ACT_SILU>(p, 2 * BN, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Unfused chain of [P1] §二.1's example: the GEMM kernel stores C, a bias kernel stores T = C + b,
+// an activation kernel writes y (stored intermediates in bf16; no bias skips the bias kernel, no
+// activation the activation kernel).
+hipError_t launch_gemm_bias_act_unfused(const void* x, const void* w, const void* bias, void* y, int M, int N,
+                                        int K, int act, void* c, void* t, hipStream_t stream) {
+    const bool last_gemm = !bias && act == ACT_NONE;
+    hipError_t e = launch_gemm_bias_act(x, w, nullptr, last_gemm ? y : c, M, N, K, ACT_NONE, stream);
+    if (e != hipSuccess || last_gemm) return e;
+    const int64_t n = (int64_t)M * N;
+    const void* src = c;
+    if (bias) {
+        void* dst = act == ACT_NONE ? y : t;
+        const bool vec = (N % 8 == 0) && (((uintptr_t)src | (uintptr_t)bias | (uintptr_t)dst) & 15u) == 0;
+        e = launch_ew<DT::BF16>(EwOp::BiasAdd, vec, src, nullptr, bias, dst, n, N, 4, stream);
+        if (e != hipSuccess || act == ACT_NONE) return e;
+        src = t;
+    }
+    const bool vec = (N % 8 == 0) && (((uintptr_t)src | (uintptr_t)y) & 15u) == 0;
+    const EwOp op = act == ACT_RELU ? EwOp::Relu : act == ACT_GELU ? EwOp::Gelu : EwOp::Silu;
+    return launch_ew<DT::BF16>(op, vec, src, nullptr, nullptr, y, n, N, 4, stream);
 }
 
 }  // namespace fuse

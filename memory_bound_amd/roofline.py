@@ -74,6 +74,19 @@ def swiglu_bytes(M: int, N: int, K: int, dtype: str, fused: bool = True) -> dict
     return _t("unfused", base + 4 * M * N * e)
 
 
+def gemm_bias_act_bytes(M: int, N: int, K: int, dtype: str, fused: bool = True) -> dict:
+    """Minimum traffic: read x, w and bias once, write y once.  Unfused ([P1] §二.1's three
+    kernels): C written and re-read, C + bias written and re-read."""
+    e = ELEM_BYTES[dtype]
+    base = (M * K + K * N + N + M * N) * e
+    return _t("fused", base) if fused else _t("unfused", base + 4 * M * N * e)
+
+
+def gemm_flops(M: int, N: int, K: int) -> int:
+    """One M x N x K product at 2 flops per multiply-add (bias and activation not counted)."""
+    return 2 * M * N * K
+
+
 def swiglu_flops(M: int, N: int, K: int) -> int:
     """Two M x N x K products at 2 flops per multiply-add (the activation is not counted)."""
     return 4 * M * N * K
@@ -90,6 +103,10 @@ def workload_work(op: str, shape: tuple, dtype: str, fused: bool = True) -> dict
         return softmax_rows_bytes(*shape, dtype, fused)
     if op == "cumsum_scale_rows":
         return cumsum_scale_rows_bytes(*shape, dtype, fused)
+    if op == "gemm_bias_act":
+        d = gemm_bias_act_bytes(*shape, dtype, fused)
+        d["flops"] = gemm_flops(*shape)
+        return d
     if op == "swiglu":
         d = swiglu_bytes(*shape, dtype, fused)
         d["flops"] = swiglu_flops(*shape)

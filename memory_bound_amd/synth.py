@@ -73,6 +73,16 @@ def cumsum_inputs(rows: int, cols: int, dtype: str, seed: int) -> dict:
     return {"x": x, "scale": 1.0 / math.sqrt(cols)}
 
 
+def gemm_inputs(M: int, N: int, K: int, dtype: str, seed: int) -> dict:
+    """x ~ N(0,1); w ~ N(0, 1/sqrt(K)) (standard deviation); bias ~ N(0, 0.02)."""
+    g = _gen(seed)
+    t = DTYPES[dtype]
+    x = _randn(g, M, K).to(t)
+    w = (_randn(g, K, N) / math.sqrt(K)).to(t)
+    bias = (_randn(g, N) * 0.02).to(t)
+    return {"x": x, "w": w, "bias": bias}
+
+
 def swiglu_inputs(M: int, N: int, K: int, dtype: str, seed: int) -> dict:
     g = _gen(seed)
     t = DTYPES[dtype]
@@ -105,6 +115,8 @@ class Workload:
             return swiglu_inputs(*self.shape, self.dtype, self.seed)
         if self.op == "cumsum_scale_rows":
             return cumsum_inputs(*self.shape, self.dtype, self.seed)
+        if self.op == "gemm_bias_act":
+            return gemm_inputs(*self.shape, self.dtype, self.seed)
         raise ValueError(self.op)
 
 
@@ -126,5 +138,7 @@ WORKLOADS = {
                  "SwiGLU dual GEMM bf16, M=2048 N=8960 K=1536"),
         Workload("cumsum_f16_2048x4096", "cumsum_scale_rows", (2048, 4096), "f16", 1007,
                  "row cumsum + scale fp16, [B,S,H]=[1,2048,4096], scale 1/64"),
+        Workload("gemm_relu_bf16_2048x8960x1536", "gemm_bias_act", (2048, 8960, 1536), "bf16", 1008,
+                 "GEMM + bias + ReLU bf16, x [2048,1536], W [1536,8960] (the SwiGLU layer's shapes)"),
     ]
 }

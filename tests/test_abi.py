@@ -182,6 +182,33 @@ def test_swiglu_validation(lib):
     assert call(M=0) == OK
 
 
+def test_gemm_bias_act_validation(lib):
+    def call(x=P, w=2 * P, b=3 * P, y=4 * P, M=256, N=256, K=64, act=1, dt=BF16):
+        return lib.fuse_gemm_bias_act(v(x), v(w), v(b), v(y), M, N, K, act, dt, None)
+    assert call(x=0) == NULL
+    assert call(w=0) == NULL
+    assert call(y=0) == NULL
+    assert call(b=0, M=0) == OK         # no bias is allowed (M = 0: nothing launched)
+    assert call(b=0, dt=F16) == DTYPE
+    assert call(dt=F16) == DTYPE
+    assert call(act=4) == VALUE
+    assert call(act=-1) == VALUE
+    assert call(N=0) == SHAPE
+    assert call(M=-1) == SHAPE
+    assert call(K=(1 << 21) + 1) == UNSUP
+    assert call(y=2 * P + 64) == ALIAS      # y over w
+    assert call(y=3 * P) == ALIAS           # y over bias
+    assert call(b=3 * P + 1) == MISAL
+    assert call(M=0) == OK
+    n = lib.fuse_unfused_workspace_bytes(5, 256, 256, 64, BF16)
+    assert n == 2 * 256 * 256 * 2
+    assert lib.fuse_unfused_workspace_bytes(5, 256, 256, 64, F16) == 0
+    assert lib.fuse_unfused_gemm_bias_act(v(P), v(2 * P), v(3 * P), v(4 * P), 256, 256, 64, 1, BF16, v(0), n,
+                                          None) == WS
+    assert lib.fuse_unfused_gemm_bias_act(v(P), v(2 * P), v(3 * P), v(4 * P), 256, 256, 64, 1, BF16, v(5 * P),
+                                          n - 256, None) == WS
+
+
 def test_unfused_workspace_bytes(lib):
     f = lib.fuse_unfused_workspace_bytes
     t = 2048 * 4096 * 2

@@ -450,6 +450,58 @@ def test_swiglu_workload_sampled_rows(monkeypatch, stages):
 
 
 # ------------------------------------------------------------------------------------------------
+# GEMM + bias + activation
+# ------------------------------------------------------------------------------------------------
+
+GEMM_SHAPES = [
+    (256, 256, 64),     # one full 256 x 256 tile, two K steps
+    (512, 768, 320),    # several full tiles (direct path)
+    (300, 384, 96),     # ragged M; N not a multiple of 256: the second half of the last tile empty
+    (130, 200, 136),    # ragged M, N, K
+    (64, 100, 40),      # N below 128: the shifted second half has no columns at all
+    (33, 136, 37),      # K not a multiple of 8: per-element loads
+    (256, 512, 1536),   # long K
+]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+@pytest.mark.parametrize("act", ["none", "relu", "gelu", "silu"])
+def test_gemm_bias_act_parity(M, N, K, act):
+    announce(f"gemm_bias_act {M}x{N}x{K} {act}")
+    d = synth.gemm_inputs(M, N, K, "bf16", seed=M + N + K)
+    y = api.fuse_gemm_bias_act(d["x"].cuda(), d["w"].cuda(), d["bias"].cuda(), act)
+    assert_close(y, oracle.gemm_bias_act(d["x"], d["w"], d["bias"], act), "bf16", f"gemm {M}x{N}x{K} {act}")
+
+
+def test_gemm_no_bias_and_stages(monkeypatch):
+    announce("gemm without bias, every ring depth, general kernel forced")
+    d = synth.gemm_inputs(512, 512, 160, "bf16", seed=3)
+    ref = oracle.gemm_bias_act(d["x"], d["w"], None, "relu")
+    x, w = d["x"].cuda(), d["w"].cuda()
+    assert_close(api.fuse_gemm_bias_act(x, w, None, "relu"), ref, "bf16", "no bias")
+    for env in ({"FUSE_SWIGLU_STAGES": "3"}, {"FUSE_SWIGLU_STAGES": "5"}, {"FUSE_SWIGLU_GENERAL": "1"}):
+        with monkeypatch.context() as m:
+            for k, v in env.items():
+                m.setenv(k, v)
+            assert_close(api.fuse_gemm_bias_act(x, w, None, "relu"), ref, "bf16", f"no bias {env}")
+
+
+def test_gemm_workload_sampled_rows():
+    w_ = synth.WORKLOADS["gemm_relu_bf16_2048x8960x1536"]
+    announce("gemm + bias + relu workload 2048x8960x1536")
+    d = w_.inputs()
+    y = api.fuse_gemm_bias_act(d["x"].cuda(), d["w"].cuda(), d["bias"].cuda(), "relu").cpu()
+    rng = np.random.default_rng(1008)
+    rows = torch.from_numpy(np.sort(rng.choice(w_.shape[0], 48, replace=False)))
+    ref = oracle.gemm_bias_act(d["x"][rows], d["w"], d["bias"], "relu")
+    r = assert_close(y[rows], ref, "bf16", "gemm sampled rows")
+    print(f"  max_abs={r['max_abs']:.3e}", flush=True)
+    assert (y >= 0).all()
+    y2 = api.fuse_gemm_bias_act(d["x"].cuda(), d["w"].cuda(), d["bias"].cuda(), "relu").cpu()
+    assert torch.equal(y, y2)
+
+
+# ------------------------------------------------------------------------------------------------
 # Unfused baselines against the oracle with rounded intermediates (twice the fp16 / bf16 rule:
 # an intermediate that sits on a rounding boundary may round the other way in fp32)
 # ------------------------------------------------------------------------------------------------
@@ -500,6 +552,16 @@ def test_unfused_swiglu():
     out = api.fuse_unfused_swiglu(d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda())
     ref = oracle.swiglu_unfused(d["a"], d["b1"], d["b2"], "bf16")
     _loose(out, ref, "bf16", "unfused swiglu")
+
+
+@pytest.mark.parametrize("act", ["none", "relu", "gelu"])
+def test_unfused_gemm_bias_act(act):
+    announce(f"unfused gemm + bias + {act}")
+    d = synth.gemm_inputs(300, 384, 192, "bf16", seed=15)
+    y = api.fuse_unfused_gemm_bias_act(d["x"].cuda(), d["w"].cuda(), d["bias"].cuda(), act)
+    _loose(y, oracle.gemm_bias_act_unfused(d["x"], d["w"], d["bias"], act, "bf16"), "bf16", f"unfused gemm {act}")
+    y = api.fuse_unfused_gemm_bias_act(d["x"].cuda(), d["w"].cuda(), None, act)
+    _loose(y, oracle.gemm_bias_act_unfused(d["x"], d["w"], None, act, "bf16"), "bf16", f"unfused gemm {act} no bias")
 
 
 def test_copy_kernel():

@@ -110,3 +110,5 @@ def test_other_algorithmic_work():
     # cumsum + scale: read x, write y; unfused adds the stored prefix sums and their reload
     assert roofline.cumsum_scale_rows_bytes(2048, 4096, "f16")["bytes"] == 33_554_432
     assert roofline.cumsum_scale_rows_bytes(2048, 4096, "f16", fused=False)["bytes"] == 67_108_864
+    assert roofline.gemm_flops(2048, 8960, 1536) == 56_371_445_760
+    assert roofline.gemm_bias_act_bytes(2048, 8960, 1536, "bf16")["bytes"] == 2 * (2048 * 1536 + 1536 * 8960 + 8960 + 2048 * 8960)
