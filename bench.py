@@ -489,15 +489,22 @@ def selection_study(torch, api, synth, K=1536, n=20):
                     torch.matmul(a, b1, out=c1)
                     torch.matmul(a, b2, out=c2)
                     torch.mul(F.silu(c1), c2, out=o)
-                r = {"M": M, "N": N, "tiles_fused": -(-M // 256) * -(-N // 128)}
-                for name, f in (("fused_us", fused), ("unfused_us", ours_a), ("library_gemm_scheme_a_us", lib_a)):
+                wsa = api._auto_workspace(api.FUSE_OP_SWIGLU, M, N, K, "cuda")
+
+                def auto(i):
+                    api.fuse_swiglu_auto(a, b1, b2, out=o, workspace=wsa)
+                r = {"M": M, "N": N, "tiles_fused": -(-M // 256) * -(-N // 128),
+                     "auto_splits": api.fuse_auto_splits(api.FUSE_OP_SWIGLU, M, N, K)}
+                for name, f in (("fused_us", fused), ("unfused_us", ours_a), ("auto_us", auto),
+                                ("library_gemm_scheme_a_us", lib_a)):
                     _, ev = time_launches(torch, stream, f, n)
                     r[name] = round(ev * 1e3 / n, 2)
                 r["fused_speedup_vs_unfused"] = round(r["unfused_us"] / r["fused_us"], 3)
                 out["shapes"].append(r)
                 log(f"selection M={M} N={N}: fused {r['fused_us']} us, unfused {r['unfused_us']} us, "
+                    f"auto ({r['auto_splits']} splits) {r['auto_us']} us, "
                     f"library-GEMM scheme A {r['library_gemm_scheme_a_us']} us")
-                del ws
+                del ws, wsa
     return out
 
 

@@ -241,6 +241,34 @@ fuse_status_t fuse_unfused_gemm_bias_act(const void *x, const void *w, const voi
                                          void *stream);
 
 /*
+ * Shape-dependent selection between the fused single kernel and a split form ([P4]
+ * 不同场景下的选型建议 and 迁移与使用注意事项 §4: whether fusing pays depends on whether the fused
+ * kernel's blocks fill the GPU, so the choice is made per shape from the device's attributes).
+ * The fused kernel's time has a floor: one workgroup walks all of K for its output tile.  When the
+ * tiles cover less than a quarter of the device's CUs (the CU count is read from the device), K is
+ * split over several workgroups per tile, each storing fp32 partial products in the workspace,
+ * and a second kernel sums them in a fixed order and applies the same epilogue.  Full-tile,
+ * 16-byte aligned shapes only; anything else runs the single fused kernel.
+ *
+ * fuse_auto_splits: the number of K splits the plan uses for (op, M, N, K) on the current device
+ *   (1 = the single fused kernel; 0 for an invalid shape).  op is FUSE_OP_SWIGLU or
+ *   FUSE_OP_GEMM_BIAS_ACT.
+ * fuse_auto_workspace_bytes: the workspace that plan needs (0 when it is the single kernel).
+ * fuse_swiglu_auto / fuse_gemm_bias_act_auto: as fuse_swiglu_dualgemm / fuse_gemm_bias_act,
+ *   following the plan; workspace as for the unfused baselines (256-byte aligned, not
+ *   overlapping any argument; may be NULL when the plan needs none).
+ */
+int fuse_auto_splits(fuse_op_t op, int64_t M, int64_t N, int64_t K);
+size_t fuse_auto_workspace_bytes(fuse_op_t op, int64_t M, int64_t N, int64_t K, fuse_dtype_t dtype);
+fuse_status_t fuse_swiglu_auto(const void *a, const void *b1, const void *b2, void *out, int64_t M,
+                               int64_t N, int64_t K, fuse_dtype_t dtype, void *workspace,
+                               size_t workspace_bytes, void *stream);
+fuse_status_t fuse_gemm_bias_act_auto(const void *x, const void *w, const void *bias, void *y,
+                                      int64_t M, int64_t N, int64_t K, fuse_act_t act,
+                                      fuse_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                                      void *stream);
+
+/*
  * Plain device-to-device copy of `bytes` bytes, the calibration kernel of the roofline: its
  * achieved bandwidth is the practical ceiling a streaming kernel can reach, and its hardware
  * byte counters give the scale between counter readings and bytes moved.  src and dst must

@@ -33,6 +33,7 @@ STATUS = {0: "FUSE_OK", 1: "FUSE_ERR_NULL_PTR", 2: "FUSE_ERR_BAD_SHAPE", 3: "FUS
 EXPORTS = [
     "fuse_add_layernorm", "fuse_add_layernorm_ex", "fuse_bias_gelu_residual", "fuse_softmax_rows",
     "fuse_cumsum_scale_rows", "fuse_swiglu_dualgemm", "fuse_gemm_bias_act", "fuse_unfused_gemm_bias_act",
+    "fuse_auto_splits", "fuse_auto_workspace_bytes", "fuse_swiglu_auto", "fuse_gemm_bias_act_auto",
     "fuse_unfused_workspace_bytes", "fuse_unfused_add_layernorm", "fuse_unfused_bias_gelu_residual",
     "fuse_unfused_softmax_rows", "fuse_unfused_cumsum_scale_rows", "fuse_unfused_swiglu", "fuse_copy", "fuse_empty_kernels",
     "fuse_status_string", "fuse_last_hip_error", "fuse_version",
@@ -71,6 +72,9 @@ def load() -> ctypes.CDLL:
         "fuse_unfused_cumsum_scale_rows": [vp, vp, i64, i64, f32, i32, vp, sz, vp],
         "fuse_swiglu_dualgemm": [vp, vp, vp, vp, i64, i64, i64, i32, vp],
         "fuse_gemm_bias_act": [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp],
+        "fuse_swiglu_auto": [vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp],
+        "fuse_gemm_bias_act_auto": [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp],
+        "fuse_auto_splits": [i32, i64, i64, i64],
         "fuse_unfused_gemm_bias_act": [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp],
         "fuse_unfused_add_layernorm": [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp, sz, vp],
         "fuse_unfused_bias_gelu_residual": [vp, vp, vp, vp, i64, i64, i32, vp, sz, vp],
@@ -85,6 +89,8 @@ def load() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.fuse_unfused_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
     lib.fuse_unfused_workspace_bytes.restype = sz
+    lib.fuse_auto_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
+    lib.fuse_auto_workspace_bytes.restype = sz
     lib.fuse_status_string.argtypes = [i32]
     lib.fuse_status_string.restype = ctypes.c_char_p
     lib.fuse_last_hip_error.argtypes = []
@@ -259,6 +265,52 @@ def fuse_gemm_bias_act(x, w, bias=None, act="relu", y=None, stream=None):
     _check(y, "y", x.dtype, (M, N))
     _ok(load().fuse_gemm_bias_act(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), M, N, K, FUSE_ACT[act], _dt(x),
                                   _stream(stream)), "fuse_gemm_bias_act")
+    return y
+
+
+def _auto_workspace(op, M, N, K, device):
+    n = load().fuse_auto_workspace_bytes(op, M, N, K, FUSE_BF16)
+    if n == 0:
+        return None, None, 0
+    buf = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf, ctypes.c_void_p(buf.data_ptr() + off), n
+
+
+def fuse_auto_splits(op, M, N, K) -> int:
+    """K splits the shape-dependent plan uses on the current device (1 = single fused kernel)."""
+    return load().fuse_auto_splits(op, M, N, K)
+
+
+def fuse_swiglu_auto(a, b1, b2, out=None, workspace=None, stream=None):
+    """fuse_swiglu_dualgemm, or its split-K form when the tiles cannot fill the GPU."""
+    M, K = a.shape
+    N = b1.shape[1]
+    _check(a, "a")
+    _check(b1, "b1", a.dtype, (K, N))
+    _check(b2, "b2", a.dtype, (K, N))
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    _check(out, "out", a.dtype, (M, N))
+    ws = workspace or _auto_workspace(FUSE_OP_SWIGLU, M, N, K, a.device)
+    _ok(load().fuse_swiglu_auto(_ptr(a), _ptr(b1), _ptr(b2), _ptr(out), M, N, K, _dt(a), ws[1], ws[2],
+                                _stream(stream)), "fuse_swiglu_auto")
+    return out
+
+
+def fuse_gemm_bias_act_auto(x, w, bias=None, act="relu", y=None, workspace=None, stream=None):
+    """fuse_gemm_bias_act, or its split-K form when the tiles cannot fill the GPU."""
+    M, K = x.shape
+    N = w.shape[1]
+    _check(x, "x")
+    _check(w, "w", x.dtype, (K, N))
+    _check(bias, "bias", x.dtype, (N,))
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _check(y, "y", x.dtype, (M, N))
+    ws = workspace or _auto_workspace(FUSE_OP_GEMM_BIAS_ACT, M, N, K, x.device)
+    _ok(load().fuse_gemm_bias_act_auto(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), M, N, K, FUSE_ACT[act], _dt(x),
+                                       ws[1], ws[2], _stream(stream)), "fuse_gemm_bias_act_auto")
     return y
 
 

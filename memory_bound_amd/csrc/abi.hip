@@ -61,6 +61,10 @@ int env_int(const char* name) {
 
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+bool workspace_ok(const void* ws, size_t have, size_t need) {
+    return ws && have >= need && ((uintptr_t)ws & 255u) == 0;
+}
+
 template <class F> hipError_t by_dtype(fuse_dtype_t d, F&& f) {
     switch (d) {
         case FUSE_F32: return f.template operator()<fuse::DT::F32>();
@@ -355,6 +359,66 @@ fuse_status_t fuse_gemm_bias_act(const void* x, const void* w, const void* bias,
 }
 
 // ------------------------------------------------------------------------------------------------
+// Shape-dependent plans (split K when the tiles cannot fill the CUs)
+// ------------------------------------------------------------------------------------------------
+
+int fuse_auto_splits(fuse_op_t op, int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || N < 1 || K < 1 || M > INT64_C(0x7fffffff) || N > (INT64_C(1) << 21) || K > (INT64_C(1) << 21))
+        return 0;
+    if (op == FUSE_OP_SWIGLU)
+        return fuse::swiglu_auto_splits((int)M, (int)N, (int)K, nullptr, nullptr, nullptr, nullptr, nullptr);
+    if (op == FUSE_OP_GEMM_BIAS_ACT)
+        return fuse::gemm_auto_splits((int)M, (int)N, (int)K, nullptr, nullptr, nullptr, nullptr);
+    return 0;
+}
+
+size_t fuse_auto_workspace_bytes(fuse_op_t op, int64_t M, int64_t N, int64_t K, fuse_dtype_t dt) {
+    if (dt != FUSE_BF16 || M < 1 || N < 1 || K < 1 || M > INT64_C(0x7fffffff) || N > (INT64_C(1) << 21) ||
+        K > (INT64_C(1) << 21))
+        return 0;
+    size_t b = 0;
+    if (op == FUSE_OP_SWIGLU)
+        fuse::swiglu_auto_splits((int)M, (int)N, (int)K, nullptr, nullptr, nullptr, nullptr, &b);
+    else if (op == FUSE_OP_GEMM_BIAS_ACT)
+        fuse::gemm_auto_splits((int)M, (int)N, (int)K, nullptr, nullptr, nullptr, &b);
+    return b;
+}
+
+fuse_status_t fuse_swiglu_auto(const void* a, const void* b1, const void* b2, void* out, int64_t M, int64_t N,
+                               int64_t K, fuse_dtype_t dt, void* ws, size_t ws_bytes, void* stream) {
+    fuse_status_t st = check_swiglu(a, b1, b2, out, M, N, K, dt);
+    if (st != FUSE_OK || M == 0) return st;
+    size_t need = 0;
+    fuse::swiglu_auto_splits((int)M, (int)N, (int)K, a, b1, b2, out, &need);
+    if (need) {
+        if (!workspace_ok(ws, ws_bytes, need)) return FUSE_ERR_WORKSPACE;
+        const size_t ab = (size_t)M * K * 2, bb = (size_t)K * N * 2, ob = (size_t)M * N * 2;
+        if (overlaps(ws, need, a, ab) || overlaps(ws, need, b1, bb) || overlaps(ws, need, b2, bb) ||
+            overlaps(ws, need, out, ob))
+            return FUSE_ERR_WORKSPACE;
+    }
+    return hip_status(fuse::launch_swiglu_auto(a, b1, b2, out, (int)M, (int)N, (int)K, ws, (hipStream_t)stream));
+}
+
+fuse_status_t fuse_gemm_bias_act_auto(const void* x, const void* w, const void* bias, void* y, int64_t M, int64_t N,
+                                      int64_t K, fuse_act_t act, fuse_dtype_t dt, void* ws, size_t ws_bytes,
+                                      void* stream) {
+    fuse_status_t st = check_gemm(x, w, bias, y, M, N, K, act, dt);
+    if (st != FUSE_OK || M == 0) return st;
+    size_t need = 0;
+    fuse::gemm_auto_splits((int)M, (int)N, (int)K, x, w, y, &need);
+    if (need) {
+        if (!workspace_ok(ws, ws_bytes, need)) return FUSE_ERR_WORKSPACE;
+        const size_t xb = (size_t)M * K * 2, wb = (size_t)K * N * 2, yb = (size_t)M * N * 2;
+        if (overlaps(ws, need, x, xb) || overlaps(ws, need, w, wb) || overlaps(ws, need, y, yb) ||
+            overlaps(ws, need, bias, bias ? (size_t)N * 2 : 0))
+            return FUSE_ERR_WORKSPACE;
+    }
+    return hip_status(fuse::launch_gemm_bias_act_auto(x, w, bias, y, (int)M, (int)N, (int)K, (int)act, ws,
+                                                      (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------------------------------------
 // Unfused baselines
 // ------------------------------------------------------------------------------------------------
 
@@ -385,9 +449,6 @@ size_t fuse_unfused_workspace_bytes(fuse_op_t op, int64_t d0, int64_t d1, int64_
     return 0;
 }
 
-static bool workspace_ok(const void* ws, size_t have, size_t need) {
-    return ws && have >= need && ((uintptr_t)ws & 255u) == 0;
-}
 
 fuse_status_t fuse_unfused_add_layernorm(const void* x, const void* residual, const void* gamma,
                                          const void* beta, void* y, int64_t rows, int64_t hidden,

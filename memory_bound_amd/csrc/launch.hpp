@@ -49,6 +49,16 @@ hipError_t launch_swiglu_unfused(const void* a, const void* b1, const void* b2, 
 // 3 SiLU; bias may be null.  The unfused chain stores C (and T = C + bias) in `c` and `t`.
 hipError_t launch_gemm_bias_act(const void* x, const void* w, const void* bias, void* y, int M, int N, int K,
                                 int act, hipStream_t stream);
+// Shape-dependent plans: K split over several workgroups per tile when the tiles alone cannot
+// fill the CUs (splits > 1 needs *ws_bytes of fp32 workspace).  The *_auto launchers follow the
+// plan: the single fused kernel, or the split kernel and its reduction.
+int swiglu_auto_splits(int M, int N, int K, const void* a, const void* b1, const void* b2, const void* out,
+                       size_t* ws_bytes);
+int gemm_auto_splits(int M, int N, int K, const void* x, const void* w, const void* y, size_t* ws_bytes);
+hipError_t launch_swiglu_auto(const void* a, const void* b1, const void* b2, void* out, int M, int N, int K,
+                              void* ws, hipStream_t stream);
+hipError_t launch_gemm_bias_act_auto(const void* x, const void* w, const void* bias, void* y, int M, int N, int K,
+                                     int act, void* ws, hipStream_t stream);
 hipError_t launch_gemm_bias_act_unfused(const void* x, const void* w, const void* bias, void* y, int M, int N,
                                         int K, int act, void* c, void* t, hipStream_t stream);
 

@@ -27,6 +27,8 @@
 // resident on one XCD share their b1/b2 column tiles in that XCD's L2.
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "launch.hpp"
 #include "stream_kernels.hpp"
 
@@ -183,6 +185,8 @@ __device__ __forceinline__ void mfma_slice(const Frags& f, floatx16 (&acc1)[WM][
 constexpr int MODE_SWIGLU = 0;    // out = SiLU(c1) * c2
 constexpr int MODE_PRODUCTS = 1;  // c1, c2 stored as they are (first kernel of the unfused SwiGLU)
 constexpr int MODE_BIAS = 2;      // MODE_BIAS + act: out = act(c + bias[col]) for both halves
+constexpr int MODE_PART_DUAL = 8;  // split K: fp32 partial c1, c2 of this workgroup's K range
+constexpr int MODE_PART_GEMM = 9;  // split K: fp32 partial of a GEMM tile (both halves, one plane)
 constexpr int ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_SILU = 3;
 
 struct DualArgs {
@@ -196,6 +200,8 @@ struct DualArgs {
     int M, N, K;           // N is also the row stride of b1, b2 and every output
     int nlim2;             // columns of b2 that exist: N, or N - 128 when b2 = b1 + 128
     int tiles_m, tiles_n, bn_step;
+    int ksteps;            // 32-deep K steps per workgroup (all of K unless split)
+    float* part;           // split K: [splits][planes][M][N] fp32 partial products
 };
 
 template <int ACT> __device__ __forceinline__ float activation(float t) {
@@ -211,10 +217,34 @@ template <int ACT> __device__ __forceinline__ float activation(float t) {
 template <int MODE>
 __device__ __forceinline__ void store_tile(const DualArgs& p, const floatx16 (&acc1)[WM][WN],
                                            const floatx16 (&acc2)[WM][WN], int m0, int n0, int wm, int wn,
-                                           int lane) {
+                                           int lane, int split) {
     const int mrows = min(p.M - m0, BM);
     const uint32_t out_bytes = (uint32_t)mrows * (uint32_t)p.N * 2u;
-    if constexpr (MODE == MODE_SWIGLU || MODE == MODE_PRODUCTS) {
+    if constexpr (MODE == MODE_PART_DUAL || MODE == MODE_PART_GEMM) {
+        // fp32 partials of this K range (full tiles only): plane h of a dual product is c_h; a GEMM
+        // keeps one plane, its halves at their own columns
+        constexpr int PLANES = MODE == MODE_PART_DUAL ? 2 : 1;
+        const int64_t plane = (int64_t)p.M * p.N;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            float* base = p.part + ((int64_t)split * PLANES + (PLANES == 2 ? h : 0)) * plane + (int64_t)m0 * p.N;
+            const rsrc_t rp = make_rsrc(base, (uint32_t)BM * (uint32_t)p.N * 4u);
+#pragma unroll
+            for (int j = 0; j < WN; j++) {
+                const int col = n0 + (PLANES == 2 ? 0 : 128 * h) + 64 * wn + 32 * j + (lane & 31);
+#pragma unroll
+                for (int i = 0; i < WM; i++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                        const float c = h == 0 ? acc1[i][j][r] : acc2[i][j][r];
+                        // default cache policy: the reduction kernel reads these right back
+                        bstore_b32(rp, ((uint32_t)row * (uint32_t)p.N + (uint32_t)col) * 4u,
+                                   __builtin_bit_cast(uint32_t, c));
+                    }
+            }
+        }
+    } else if constexpr (MODE == MODE_SWIGLU || MODE == MODE_PRODUCTS) {
         constexpr bool PROD = MODE == MODE_PRODUCTS;
         const rsrc_t ro = make_rsrc((PROD ? p.c1 : p.out) + (int64_t)m0 * p.N, out_bytes);
         const rsrc_t ro2 = make_rsrc(PROD ? p.c2 + (int64_t)m0 * p.N : p.out, PROD ? out_bytes : 0u);
@@ -315,7 +345,7 @@ swiglu_kernel(DualArgs p) {
         }
     }
 
-    store_tile<MODE>(p, acc1, acc2, tile.m0, tile.n0, wm, wn, lane);
+    store_tile<MODE>(p, acc1, acc2, tile.m0, tile.n0, wm, wn, lane, 0);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -476,7 +506,11 @@ swiglu_direct_kernel(DualArgs p) {
     static_assert(S >= 3 && S * C::STAGE_BYTES <= 160 * 1024, "ring of 3 to 5 stages of 32 KiB");
     __shared__ __attribute__((aligned(1024))) char lds[S * C::STAGE_BYTES];
 
-    const Tile tile = tile_of(blockIdx.x, p.tiles_m, p.tiles_n, p.bn_step);
+    // With K split, workgroup (split, tile) = (bid / tiles, bid % tiles) covers K steps
+    // [split * ksteps, split * ksteps + ksteps) of its tile.
+    const int ntiles = p.tiles_m * p.tiles_n;
+    const int split = blockIdx.x / ntiles;
+    const Tile tile = tile_of(blockIdx.x - split * ntiles, p.tiles_m, p.tiles_n, p.bn_step);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -489,14 +523,15 @@ swiglu_direct_kernel(DualArgs p) {
 #pragma unroll
             for (int r = 0; r < 16; r++) acc1[i][j][r] = acc2[i][j][r] = 0.0f;
 
-    const int kt_n = K / C::BKD;
+    const int kt0 = split * p.ksteps;
+    const int kt_n = min(p.ksteps, K / C::BKD - kt0);
     // Prologue: stages 0 .. S-2.  Every step issues the loads of one stage; past the last K step
     // they reload the last stage into a buffer nobody reads again, which keeps the vmcnt
     // bookkeeping the same on every step.
 #pragma unroll
     for (int s = 0; s < S - 1; s++) {
         const uint32_t base = lds_addr(lds + s * C::STAGE_BYTES);
-        const int k0 = min(s, kt_n - 1) * C::BKD;
+        const int k0 = (kt0 + min(s, kt_n - 1)) * C::BKD;
 #pragma unroll
         for (int l = 0; l < LPS; l++) dma_slot(l, a, b1, b2, N, K, tile.m0, tile.n0, k0, base, wave, lane);
     }
@@ -517,7 +552,7 @@ swiglu_direct_kernel(DualArgs p) {
         const char* st = lds + (kt % S) * C::STAGE_BYTES;
         const char* sn = lds + ((kt + 1) % S) * C::STAGE_BYTES;
         const uint32_t nbase = lds_addr(lds + ((kt + S - 1) % S) * C::STAGE_BYTES);
-        const int nk0 = min(kt + S - 1, kt_n - 1) * C::BKD;
+        const int nk0 = (kt0 + min(kt + S - 1, kt_n - 1)) * C::BKD;
         slice_step(f0, f1, st, 1, acc1, acc2, 0, a, b1, b2, N, K, tile.m0, tile.n0, nk0, nbase, wm, wn, wave, lane);
         slice_step(f1, f0, sn, 0, acc1, acc2, 4, a, b1, b2, N, K, tile.m0, tile.n0, nk0, nbase, wm, wn, wave, lane);
         wait_vmcnt<LPS * (S - 3)>();
@@ -525,7 +560,53 @@ swiglu_direct_kernel(DualArgs p) {
     }
     wait_vmcnt<0>();  // no load may still be writing this workgroup's LDS when it ends
 
-    store_tile<MODE>(p, acc1, acc2, tile.m0, tile.n0, wm, wn, lane);
+    store_tile<MODE>(p, acc1, acc2, tile.m0, tile.n0, wm, wn, lane, split);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Split-K form.  The fused kernel's time has a floor: one workgroup walks all of K for its tile, so
+// a shape with few tiles leaves most CUs idle for that whole walk.  Below a tile count set from
+// the CU count, K is divided among several workgroups per tile; each stores its fp32 partial
+// products and a second kernel sums them (in split order, so results are reproducible) and
+// applies the epilogue.  This is the pages' trade between one kernel with fewer blocks and more
+// blocks with an intermediate in memory, decided per shape on the device at hand.
+// ------------------------------------------------------------------------------------------------
+template <int MODE, int ACT>
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float* part, const uint16_t* bias, uint16_t* out, int64_t mn, int N, int splits) {
+    constexpr int PLANES = MODE == MODE_PART_DUAL ? 2 : 1;
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;  // mn is a multiple of 4
+    if (e >= mn) return;
+    float s1[4] = {0.0f, 0.0f, 0.0f, 0.0f}, s2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < splits; s++) {
+        const float* q = part + (int64_t)s * PLANES * mn + e;
+        const float4 v = *reinterpret_cast<const float4*>(q);
+        s1[0] += v.x, s1[1] += v.y, s1[2] += v.z, s1[3] += v.w;
+        if constexpr (PLANES == 2) {
+            const float4 w = *reinterpret_cast<const float4*>(q + mn);
+            s2[0] += w.x, s2[1] += w.y, s2[2] += w.z, s2[3] += w.w;
+        }
+    }
+    uint32_t o[4];
+    const int col = (int)(e % N);
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        if constexpr (MODE == MODE_PART_DUAL) o[k] = f32_to_bf16(silu(s1[k]) * s2[k]);
+        else o[k] = f32_to_bf16(activation<ACT>(s1[k] + (bias ? bf16_to_f32(bias[col + k]) : 0.0f)));
+    }
+    *reinterpret_cast<uint2*>(out + e) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+}
+
+int cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 // Ring depth of the full-tile kernel (FUSE_SWIGLU_STAGES, 3 to 5, overrides the default for tuning
@@ -545,6 +626,7 @@ hipError_t launch(DualArgs p, int tile_cols, hipStream_t stream) {
     p.tiles_m = (p.M + BM - 1) / BM;
     p.tiles_n = (p.N + tile_cols - 1) / tile_cols;
     p.bn_step = tile_cols;
+    p.ksteps = p.K / DirectCfg::BKD;
     if ((int64_t)p.tiles_m * p.tiles_n > 0x7fffffff) return hipErrorInvalidValue;
     const bool aligned = (p.K % 8 == 0) && (p.N % 8 == 0) &&
                          (((uintptr_t)p.a | (uintptr_t)p.b1 | (uintptr_t)p.b2) & 15u) == 0;
@@ -570,7 +652,108 @@ DualArgs dual_args(const void* a, const void* b1, const void* b2, int M, int N, 
     return p;
 }
 
+// Split of K for a shape (1 = the single fused kernel).  Full tiles only.  When the tiles cover
+// fewer than SPLIT_BELOW_CU_FRACTION of the CUs, K is divided so that tiles x splits is about one
+// workgroup per CU, each split keeping at least MIN_SPLIT_STEPS steps of 32.  Measured on 256
+// CUs at K = 1536: 2 to 32 tiles gain 1.1-2.2x from the split, 64 tiles split 4 ways gain
+// nothing.  FUSE_SPLITK forces a split count (1 = never split) for tuning sweeps.
+constexpr double SPLIT_BELOW_CU_FRACTION = 0.25;
+constexpr int MIN_SPLIT_STEPS = 4;
+
+struct SplitPlan {
+    int splits, ksteps;
+};
+
+SplitPlan split_plan(int M, int N, int K, int tile_cols, bool aligned) {
+    const int kt = K / DirectCfg::BKD;
+    if (direct_stages(M, N, K, aligned, tile_cols) == 0) return {1, kt};
+    const int tiles = (M / BM) * (N / tile_cols);
+    const char* f = getenv("FUSE_SPLITK");
+    int sp;
+    if (f && atoi(f) >= 1) {
+        sp = atoi(f);
+    } else {
+        const int cus = cu_count();
+        if (tiles >= SPLIT_BELOW_CU_FRACTION * cus) return {1, kt};
+        sp = min(cus / tiles, kt / MIN_SPLIT_STEPS);
+    }
+    sp = max(1, min(sp, kt));
+    if (sp < 2) return {1, kt};
+    const int ksteps = (kt + sp - 1) / sp;
+    return {(kt + ksteps - 1) / ksteps, ksteps};  // no empty split
+}
+
+size_t split_bytes(const SplitPlan& sp, int M, int N, int planes) {
+    return sp.splits < 2 ? 0 : (size_t)sp.splits * planes * (size_t)M * (size_t)N * 4u;
+}
+
+bool aligned_args(const void* a, const void* b, int N, int K) {
+    return (K % 8 == 0) && (N % 8 == 0) && ((((uintptr_t)a | (uintptr_t)b) & 15u) == 0);
+}
+
+template <int PMODE, int ACT>
+hipError_t launch_split(DualArgs p, int tile_cols, const SplitPlan& sp, float* part, hipStream_t stream) {
+    p.tiles_m = p.M / BM;
+    p.tiles_n = p.N / tile_cols;
+    p.bn_step = tile_cols;
+    p.ksteps = sp.ksteps;
+    p.part = part;
+    const int st = direct_stages(p.M, p.N, p.K, true, tile_cols);
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n * sp.splits)), block(THREADS);
+    if (st == 3) hipLaunchKernelGGL((swiglu_direct_kernel<3, PMODE>), grid, block, 0, stream, p);
+    else if (st == 5) hipLaunchKernelGGL((swiglu_direct_kernel<5, PMODE>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((swiglu_direct_kernel<4, PMODE>), grid, block, 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t mn = (int64_t)p.M * p.N;
+    hipLaunchKernelGGL((splitk_reduce_kernel<PMODE, ACT>), dim3((unsigned)((mn / 4 + 255) / 256)), dim3(256), 0,
+                       stream, (const float*)part, p.bias, p.out, mn, p.N, sp.splits);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+// The split form also needs a 16-byte aligned output (the reduction stores 8 bytes per thread).
+int swiglu_auto_splits(int M, int N, int K, const void* a, const void* b1, const void* b2, const void* out,
+                       size_t* ws_bytes) {
+    const SplitPlan sp =
+        split_plan(M, N, K, BN, aligned_args(a, b1, N, K) && ((((uintptr_t)b2) | (uintptr_t)out) & 15u) == 0);
+    if (ws_bytes) *ws_bytes = split_bytes(sp, M, N, 2);
+    return sp.splits;
+}
+
+int gemm_auto_splits(int M, int N, int K, const void* x, const void* w, const void* y, size_t* ws_bytes) {
+    const SplitPlan sp = split_plan(M, N, K, 2 * BN, aligned_args(x, w, N, K) && ((uintptr_t)y & 15u) == 0);
+    if (ws_bytes) *ws_bytes = split_bytes(sp, M, N, 1);
+    return sp.splits;
+}
+
+hipError_t launch_swiglu_auto(const void* a, const void* b1, const void* b2, void* out, int M, int N, int K,
+                              void* ws, hipStream_t stream) {
+    const SplitPlan sp =
+        split_plan(M, N, K, BN, aligned_args(a, b1, N, K) && ((((uintptr_t)b2) | (uintptr_t)out) & 15u) == 0);
+    if (sp.splits < 2) return launch_swiglu(a, b1, b2, out, M, N, K, stream);
+    DualArgs p = dual_args(a, b1, b2, M, N, K);
+    p.out = (uint16_t*)out;
+    return launch_split<MODE_PART_DUAL, ACT_NONE>(p, BN, sp, (float*)ws, stream);
+}
+
+hipError_t launch_gemm_bias_act_auto(const void* x, const void* w, const void* bias, void* y, int M, int N, int K,
+                                     int act, void* ws, hipStream_t stream) {
+    const SplitPlan sp = split_plan(M, N, K, 2 * BN, aligned_args(x, w, N, K) && ((uintptr_t)y & 15u) == 0);
+    if (sp.splits < 2) return launch_gemm_bias_act(x, w, bias, y, M, N, K, act, stream);
+    DualArgs p = dual_args(x, w, (const uint16_t*)w + 128, M, N, K);
+    p.out = (uint16_t*)y;
+    p.bias = (const uint16_t*)bias;
+    p.nlim2 = N - 128;
+    switch (act) {
+        case ACT_NONE: return launch_split<MODE_PART_GEMM, ACT_NONE>(p, 2 * BN, sp, (float*)ws, stream);
+        case ACT_RELU: return launch_split<MODE_PART_GEMM, ACT_RELU>(p, 2 * BN, sp, (float*)ws, stream);
+        case ACT_GELU: return launch_split<MODE_PART_GEMM, ACT_GELU>(p, 2 * BN, sp, (float*)ws, stream);
+        case ACT_SILU: return launch_split<MODE_PART_GEMM, ACT_SILU>(p, 2 * BN, sp, (float*)ws, stream);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_swiglu(const void* a, const void* b1, const void* b2, void* out, int M, int N, int K,
                          hipStream_t stream) {

@@ -209,6 +209,39 @@ def test_gemm_bias_act_validation(lib):
                                           n - 256, None) == WS
 
 
+def test_auto_plan_and_validation(lib):
+    # Plans depend only on the shape and the CU count (256 here when no device answers, as on the
+    # MI355X): the split form is taken while the tiles cover less than a quarter of the CUs.
+    SW, GM = 3, 5
+    cus = 256
+    assert lib.fuse_auto_splits(SW, 2048, 8960, 1536) == 1               # 560 tiles: single kernel
+    assert lib.fuse_auto_splits(SW, 300, 512, 1536) == 1                 # ragged M: single kernel
+    assert lib.fuse_auto_splits(SW, 256, 512, 1536) == min(cus // 4, 48 // 4)  # 4 tiles
+    assert lib.fuse_auto_splits(SW, 256, 512, 96) == 1                   # 3 K steps: too short to split
+    assert lib.fuse_auto_splits(SW, 512, 2048, 1536) == 8                # 32 tiles
+    assert lib.fuse_auto_splits(SW, 1024, 2048, 1536) == 1               # 64 tiles: single kernel
+    assert lib.fuse_auto_splits(GM, 256, 512, 1536) == 12                # 2 tiles of 256 x 256
+    assert lib.fuse_auto_splits(SW, 0, 512, 1536) == 0
+    assert lib.fuse_auto_workspace_bytes(SW, 256, 512, 1536, BF16) == 12 * 2 * 256 * 512 * 4
+    assert lib.fuse_auto_workspace_bytes(GM, 256, 512, 1536, BF16) == 12 * 256 * 512 * 4
+    assert lib.fuse_auto_workspace_bytes(SW, 2048, 8960, 1536, BF16) == 0
+    assert lib.fuse_auto_workspace_bytes(SW, 256, 512, 1536, F16) == 0
+    Q = 16 * P  # 16 MiB apart: the operands of these shapes do not overlap each other
+    sw = lambda ws, n, **k: lib.fuse_swiglu_auto(v(Q), v(2 * Q), v(3 * Q), v(4 * Q), k.get("M", 256), 512, 1536,
+                                                 k.get("dt", BF16), v(ws), n, None)
+    assert sw(0, 0) == WS                       # split plan needs a workspace
+    assert sw(5 * Q, 1000) == WS                # too small
+    assert sw(5 * Q + 16, 1 << 24) == WS        # not 256-byte aligned
+    assert sw(Q, 1 << 24) == WS                 # overlaps a
+    assert sw(0, 0, dt=F16) == DTYPE
+    assert sw(0, 0, M=0) == OK
+    gm = lambda ws, n, act=1: lib.fuse_gemm_bias_act_auto(v(Q), v(2 * Q), v(3 * Q), v(4 * Q), 256, 512, 1536, act,
+                                                          BF16, v(ws), n, None)
+    assert gm(0, 0) == WS
+    assert gm(0, 0, act=9) == VALUE
+    assert gm(4 * Q, 1 << 24) == WS             # overlaps y
+
+
 def test_unfused_workspace_bytes(lib):
     f = lib.fuse_unfused_workspace_bytes
     t = 2048 * 4096 * 2

@@ -502,6 +502,48 @@ def test_gemm_workload_sampled_rows():
 
 
 # ------------------------------------------------------------------------------------------------
+# Shape-dependent plans: split K for shapes whose tiles cannot fill the GPU
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,force", [
+    (256, 512, 1536, None),   # 4 tiles: split by the plan
+    (1024, 1024, 1536, None), # 32 tiles
+    (512, 256, 320, None),    # short K
+    (256, 512, 1536, "2"), (256, 512, 1536, "5"), (256, 512, 1536, "48"),  # uneven and one step per split
+    (2048, 1024, 64, None),   # 64 tiles, two K steps: no split
+])
+def test_swiglu_auto_parity(monkeypatch, M, N, K, force):
+    if force:
+        monkeypatch.setenv("FUSE_SPLITK", force)
+    splits = api.fuse_auto_splits(api.FUSE_OP_SWIGLU, M, N, K)
+    announce(f"swiglu auto {M}x{N}x{K} splits={splits}")
+    d = synth.swiglu_inputs(M, N, K, "bf16", seed=M + 3 * N + K)
+    a, b1, b2 = d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda()
+    out = api.fuse_swiglu_auto(a, b1, b2)
+    rows = torch.arange(0, M, max(1, M // 64))
+    assert_close(out[rows.cuda()], oracle.swiglu(d["a"][rows], d["b1"], d["b2"]), "bf16", f"auto {M}x{N}x{K} s={splits}")
+    assert torch.equal(out, api.fuse_swiglu_auto(a, b1, b2))  # fixed summation order
+    if force is None and M * N <= 256 * 512:
+        assert splits > 1
+
+
+@pytest.mark.parametrize("act", ["none", "relu", "gelu", "silu"])
+def test_gemm_auto_parity(monkeypatch, act):
+    for M, N, K, force in ((256, 512, 1536, None), (512, 768, 640, "3"), (256, 256, 64, "2")):
+        with monkeypatch.context() as m:
+            if force:
+                m.setenv("FUSE_SPLITK", force)
+            splits = api.fuse_auto_splits(api.FUSE_OP_GEMM_BIAS_ACT, M, N, K)
+            announce(f"gemm auto {M}x{N}x{K} {act} splits={splits}")
+            assert splits > 1
+            d = synth.gemm_inputs(M, N, K, "bf16", seed=M + N + K + 1)
+            y = api.fuse_gemm_bias_act_auto(d["x"].cuda(), d["w"].cuda(), d["bias"].cuda(), act)
+            assert_close(y, oracle.gemm_bias_act(d["x"], d["w"], d["bias"], act), "bf16", f"gemm auto {M}x{N}x{K} {act}")
+            y = api.fuse_gemm_bias_act_auto(d["x"].cuda(), d["w"].cuda(), None, act)
+            assert_close(y, oracle.gemm_bias_act(d["x"], d["w"], None, act), "bf16", f"gemm auto no bias {act}")
+
+
+# ------------------------------------------------------------------------------------------------
 # Unfused baselines against the oracle with rounded intermediates (twice the fp16 / bf16 rule:
 # an intermediate that sits on a rounding boundary may round the other way in fp32)
 # ------------------------------------------------------------------------------------------------
