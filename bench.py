@@ -393,6 +393,66 @@ def counters_pass(torch, api, synth, n=8):
     log(f"counters: {n} x copy of {nbytes} bytes")
 
 
+def counters_rows(torch, api, synth, n=4):
+    """Like counters_pass for the other rows of the path: a few cold dispatches (1 GiB rotation)
+    of each fused kernel and its unfused chain, then the 24 MiB copy calibration."""
+    def run(name, inputs, outputs, fn):
+        sets = rotation_sets(torch, inputs, outputs, ROTATE_BYTES)
+        for i in range(n):
+            fn(sets[i % len(sets)])
+            torch.cuda.synchronize()
+        log(f"counters: {n} x {name}")
+        del sets
+
+    w = synth.WORKLOADS[HEADLINE]
+    d = w.inputs()
+    gamma, beta = d["gamma"].cuda(), d["beta"].cuda()
+    stats = (torch.empty(w.shape[0], device="cuda"), torch.empty(w.shape[0], device="cuda"))
+    run("add_layernorm_ex", {"x": d["x"], "r": d["residual"]}, {"y": d["x"], "s": d["x"]},
+        lambda s: api.fuse_add_layernorm_ex(s["x"], s["r"], gamma, beta, 1e-5, relu=True, y=s["y"], sum_out=s["s"],
+                                            mean_out=stats[0], var_out=stats[1]))
+    w = synth.WORKLOADS["cumsum_f16_2048x4096"]
+    d = w.inputs()
+    ws = api._workspace(api.FUSE_OP_CUMSUM_SCALE, *w.shape, 0, api.FUSE_F16, "cuda")
+    run("cumsum_scale", {"x": d["x"]}, {"y": d["x"]}, lambda s: api.fuse_cumsum_scale_rows(s["x"], d["scale"], y=s["y"]))
+    run("cumsum_scale_unfused", {"x": d["x"]}, {"y": d["x"]},
+        lambda s: api.fuse_unfused_cumsum_scale_rows(s["x"], d["scale"], y=s["y"], workspace=ws))
+    del ws
+    w = synth.WORKLOADS["softmax_f16_65536x2048"]
+    d = w.inputs()
+    ws = api._workspace(api.FUSE_OP_SOFTMAX_ROWS, *w.shape, 0, api.FUSE_F16, "cuda")
+    run("softmax", {"x": d["x"]}, {"y": d["x"]}, lambda s: api.fuse_softmax_rows(s["x"], d["scale"], y=s["y"]))
+    run("softmax_unfused", {"x": d["x"]}, {"y": d["x"]},
+        lambda s: api.fuse_unfused_softmax_rows(s["x"], d["scale"], y=s["y"], workspace=ws))
+    del ws, d
+    w = synth.WORKLOADS["swiglu_bf16_2048x8960x1536"]
+    d = w.inputs()
+    M, N, K = w.shape
+    o = torch.empty(M, N, dtype=torch.bfloat16)
+    ws = api._workspace(api.FUSE_OP_SWIGLU, M, N, K, api.FUSE_BF16, "cuda")
+    io = {"a": d["a"], "b1": d["b1"], "b2": d["b2"]}
+    run("swiglu", io, {"o": o}, lambda s: api.fuse_swiglu_dualgemm(s["a"], s["b1"], s["b2"], out=s["o"]))
+    run("swiglu_unfused", io, {"o": o},
+        lambda s: api.fuse_unfused_swiglu(s["a"], s["b1"], s["b2"], out=s["o"], workspace=ws))
+    del ws, d
+    w = synth.WORKLOADS["gemm_relu_bf16_2048x8960x1536"]
+    d = w.inputs()
+    ws = api._workspace(api.FUSE_OP_GEMM_BIAS_ACT, M, N, K, api.FUSE_BF16, "cuda")
+    io = {"x": d["x"], "w": d["w"], "b": d["bias"]}
+    run("gemm_bias_relu", io, {"y": o}, lambda s: api.fuse_gemm_bias_act(s["x"], s["w"], s["b"], "relu", y=s["y"]))
+    run("gemm_bias_relu_unfused", io, {"y": o},
+        lambda s: api.fuse_unfused_gemm_bias_act(s["x"], s["w"], s["b"], "relu", y=s["y"], workspace=ws))
+    del ws, d
+    nbytes = 24 << 20
+    bufs = [(torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1),
+             torch.empty(nbytes, dtype=torch.uint8, device="cuda")) for _ in range(22)]
+    for i in range(8):
+        s, t = bufs[(i + 7) % len(bufs)]
+        api.fuse_copy(s, t)
+        torch.cuda.synchronize()
+    log(f"counters: 8 x copy of {nbytes} bytes")
+
+
 def launch_study(torch, api, synth, n_empty=4000, n_graph=1000, n_steps=200):
     """Launch cost on this GPU ([P2] §4.5, [P3] §2): an empty kernel enqueued from a loop inside
     the library (host cost per call, back-to-back interval on the GPU, cost per kernel inside a
@@ -542,6 +602,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--counters", action="store_true",
                     help="only run the short dispatch sequence read by rocprofv3 --pmc, no timing")
+    ap.add_argument("--counters-rows", action="store_true",
+                    help="the same for the other rows of the path (their fused and unfused kernels)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): the fused row kernels are "
@@ -557,6 +619,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if a.counters:
         counters_pass(torch, api, synth)
+        return
+    if a.counters_rows:
+        counters_rows(torch, api, synth)
         return
     h = headline(torch, api, synth, roofline, a.steps, a.warmup)
     log(f"headline: {h['avg_launch_us']:.2f} us/launch, value {h['value_gbps']:.0f} GB/s")
