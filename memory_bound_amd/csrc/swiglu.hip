@@ -202,6 +202,7 @@ struct DualArgs {
     int tiles_m, tiles_n, bn_step;
     int ksteps;            // 32-deep K steps per workgroup (all of K unless split)
     float* part;           // split K: [splits][planes][M][N] fp32 partial products
+    int tail;              // full-tile kernel: the last `tail` tiles run as two 128-row halves each
 };
 
 template <int ACT> __device__ __forceinline__ float activation(float t) {
@@ -211,14 +212,15 @@ template <int ACT> __device__ __forceinline__ float activation(float t) {
     else return t;
 }
 
-// Stores the tile at (m0, n0).  Block (i, j) element r of lane l sits at row 8 (r/4) + 4 (l/32) +
-// r%4, column l%32 of the block; the wave's blocks start at row 128 wm, column 64 wn of each
-// product's 128-column tile.  Rows past M and columns past N fall outside the store resources.
-template <int MODE>
-__device__ __forceinline__ void store_tile(const DualArgs& p, const floatx16 (&acc1)[WM][WN],
-                                           const floatx16 (&acc2)[WM][WN], int m0, int n0, int wm, int wn,
+// Stores the tile at (m0, n0) (64 WMT rows).  Block (i, j) element r of lane l sits at row
+// 8 (r/4) + 4 (l/32) + r%4, column l%32 of the block; the wave's blocks start at row 32 WMT wm,
+// column 64 wn of each product's 128-column tile.  Rows past M and columns past N fall outside the store resources.
+template <int MODE, int WMT = WM>
+__device__ __forceinline__ void store_tile(const DualArgs& p, const floatx16 (&acc1)[WMT][WN],
+                                           const floatx16 (&acc2)[WMT][WN], int m0, int n0, int wm, int wn,
                                            int lane, int split) {
-    const int mrows = min(p.M - m0, BM);
+    constexpr int TM = 64 * WMT;  // tile rows: two waves of 32 * WMT rows
+    const int mrows = min(p.M - m0, TM);
     const uint32_t out_bytes = (uint32_t)mrows * (uint32_t)p.N * 2u;
     if constexpr (MODE == MODE_PART_DUAL || MODE == MODE_PART_GEMM) {
         // fp32 partials of this K range (full tiles only): plane h of a dual product is c_h; a GEMM
@@ -228,15 +230,15 @@ __device__ __forceinline__ void store_tile(const DualArgs& p, const floatx16 (&a
 #pragma unroll
         for (int h = 0; h < 2; h++) {
             float* base = p.part + ((int64_t)split * PLANES + (PLANES == 2 ? h : 0)) * plane + (int64_t)m0 * p.N;
-            const rsrc_t rp = make_rsrc(base, (uint32_t)BM * (uint32_t)p.N * 4u);
+            const rsrc_t rp = make_rsrc(base, (uint32_t)TM * (uint32_t)p.N * 4u);
 #pragma unroll
             for (int j = 0; j < WN; j++) {
                 const int col = n0 + (PLANES == 2 ? 0 : 128 * h) + 64 * wn + 32 * j + (lane & 31);
 #pragma unroll
-                for (int i = 0; i < WM; i++)
+                for (int i = 0; i < WMT; i++)
 #pragma unroll
                     for (int r = 0; r < 16; r++) {
-                        const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                        const int row = 32 * WMT * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                         const float c = h == 0 ? acc1[i][j][r] : acc2[i][j][r];
                         // default cache policy: the reduction kernel reads these right back
                         bstore_b32(rp, ((uint32_t)row * (uint32_t)p.N + (uint32_t)col) * 4u,
@@ -249,13 +251,13 @@ __device__ __forceinline__ void store_tile(const DualArgs& p, const floatx16 (&a
         const rsrc_t ro = make_rsrc((PROD ? p.c1 : p.out) + (int64_t)m0 * p.N, out_bytes);
         const rsrc_t ro2 = make_rsrc(PROD ? p.c2 + (int64_t)m0 * p.N : p.out, PROD ? out_bytes : 0u);
 #pragma unroll
-        for (int i = 0; i < WM; i++)
+        for (int i = 0; i < WMT; i++)
 #pragma unroll
             for (int j = 0; j < WN; j++) {
                 const int col = n0 + 64 * wn + 32 * j + (lane & 31);
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    const int row = 32 * WMT * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                     const uint32_t off = col < p.N ? ((uint32_t)row * (uint32_t)p.N + (uint32_t)col) * 2u : OOB;
                     const float c1 = acc1[i][j][r], c2 = acc2[i][j][r];
                     if constexpr (PROD) {
@@ -278,10 +280,10 @@ __device__ __forceinline__ void store_tile(const DualArgs& p, const floatx16 (&a
                 const bool in = col < p.N;
                 const float bv = bf16_to_f32(bload_b16(rbias, in ? (uint32_t)col * 2u : OOB));
 #pragma unroll
-                for (int i = 0; i < WM; i++)
+                for (int i = 0; i < WMT; i++)
 #pragma unroll
                     for (int r = 0; r < 16; r++) {
-                        const int row = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                        const int row = 32 * WMT * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                         const uint32_t off = in ? ((uint32_t)row * (uint32_t)p.N + (uint32_t)col) * 2u : OOB;
                         const float c = h == 0 ? acc1[i][j][r] : acc2[i][j][r];
                         bstore_b16<AUX_STREAM>(ro, off, f32_to_bf16(activation<ACT>(c + bv)));
@@ -378,17 +380,21 @@ swiglu_kernel(DualArgs p) {
 // step kt+1 overwrite.
 // ------------------------------------------------------------------------------------------------
 
-struct DirectCfg {
+// TM = 256 (the tile) or 128 (half of a tile of the last round, see the kernel).
+template <int TM> struct DirectCfgT {
     static constexpr int BKD = 32;
     static constexpr int A_ROW_BYTES = 64, A_CHUNKS = 4;
-    static constexpr int A_BYTES = BM * A_ROW_BYTES;  // 16 KiB
+    static constexpr int A_BYTES = TM * A_ROW_BYTES;  // 16 or 8 KiB
     static constexpr int B_BYTES = BKD * BN * 2;      // 8 KiB per matrix
     static constexpr int STAGE_BYTES = A_BYTES + 2 * B_BYTES;
-    // asynchronous load instructions per wave per stage: 4 of a rows, 2 each of b1 and b2 rows
-    static constexpr int A_LOADS = 4;
-    static constexpr int LOADS_PER_STAGE = 8;
+    static constexpr int WMT = TM / 64;               // 32-row blocks per wave (wave tile TM/2 x 64)
+    // asynchronous load instructions per wave per stage: TM/64 of a rows (TM/4 rows per wave),
+    // 2 each of b1 and b2 rows
+    static constexpr int A_LOADS = TM / 64;
+    static constexpr int LOADS_PER_STAGE = A_LOADS + 4;
     __device__ static int a_phys(int r, int q) { return q ^ ((r >> 2) & 3); }
 };
+using DirectCfg = DirectCfgT<BM>;
 
 __device__ __forceinline__ int b_phys(int k, int q) { return q ^ (4 * (k & 3)); }
 
@@ -415,15 +421,16 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
 }
 
-// Load slot `slot` (0 .. 7) of K step k0 into the stage at LDS address `base`: slots 0-3 fill a rows
-// [64 w, 64 w + 64) of wave w (16 rows of 64 bytes per instruction), slots 4-7 four rows each of
-// the b1 and b2 tiles, wave w taking rows [8 w, 8 w + 8).  Called with compile-time slot numbers
-// from unrolled loops, so the branch folds away.
+// Load slot `slot` of K step k0 into the stage at LDS address `base`: the first A_LOADS slots fill
+// a rows [TM/4 w, TM/4 w + TM/4) of wave w (16 rows of 64 bytes per instruction), the last four
+// four rows each of the b1 and b2 tiles, wave w taking rows [8 w, 8 w + 8).  Called with
+// compile-time slot numbers from unrolled loops, so the branch folds away.
+template <int TM>
 __device__ __forceinline__ void dma_slot(int slot, const uint16_t* a, const uint16_t* b1, const uint16_t* b2,
                                          int N, int K, int m0, int n0, int k0, uint32_t base, int wave, int lane) {
-    using C = DirectCfg;
+    using C = DirectCfgT<TM>;
     if (slot < C::A_LOADS) {
-        const int r0 = 64 * wave + 16 * slot;
+        const int r0 = (TM / 4) * wave + 16 * slot;
         const int r = r0 + lane / C::A_CHUNKS, p = lane % C::A_CHUNKS;
         dma16(a + (int64_t)(m0 + r) * K + k0 + 8 * C::a_phys(r, p), base + r0 * C::A_ROW_BYTES);
     } else {
@@ -449,82 +456,95 @@ __device__ __forceinline__ bf16x8 join(v4i16 lo, v4i16 hi) {
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+template <int TM>
 __device__ __forceinline__ bf16x8 a_frag(const char* st, int wm, int lane, int kk, int i) {
-    using C = DirectCfg;
-    const int r = 128 * wm + 32 * i + (lane & 31), qa = 2 * kk + (lane >> 5);
+    using C = DirectCfgT<TM>;
+    const int r = (TM / 2) * wm + 32 * i + (lane & 31), qa = 2 * kk + (lane >> 5);
     return *reinterpret_cast<const bf16x8*>(st + r * C::A_ROW_BYTES + C::a_phys(r, qa) * 16);
 }
 
-// The 16 MFMAs of one k slice on fragments `f`, interleaved with the LDS reads of the fragments `nx`
-// of slice rk of stage `rs` (one read after each of the first MFMAs, in the order the next slice
-// uses them) and with load slots slot0 .. slot0 + 3 of the stage at LDS address `base` (after
-// MFMAs 9, 11, 13 and 15).
-__device__ __forceinline__ void slice_step(const Frags& f, Frags& nx, const char* rs, int rk,
-                                           floatx16 (&acc1)[WM][WN], floatx16 (&acc2)[WM][WN], int slot0,
-                                           const uint16_t* a, const uint16_t* b1, const uint16_t* b2, int N,
-                                           int K, int m0, int n0, int k0, uint32_t base, int wm, int wn,
+template <int WMT> struct FragsD {
+    bf16x8 a[WMT], b1[WN], b2[WN];
+};
+
+// The 4 WMT MFMAs of one k slice on fragments `f`, interleaved with the LDS reads of the fragments
+// `nx` of slice rk of stage `rs`, issued after the first MFMAs in the order the next slice uses
+// them (a0, b1[0], b2[0], b1[1], b2[1], then the other a rows; each b fragment is two transposed
+// reads), and with this slice's share of the next stage's load slots (from slot0) after the later
+// MFMAs.
+template <int TM>
+__device__ __forceinline__ void slice_step(const FragsD<TM / 64>& f, FragsD<TM / 64>& nx, const char* rs, int rk,
+                                           floatx16 (&acc1)[TM / 64][WN], floatx16 (&acc2)[TM / 64][WN],
+                                           int slot0, const uint16_t* a, const uint16_t* b1, const uint16_t* b2,
+                                           int N, int K, int m0, int n0, int k0, uint32_t base, int wm, int wn,
                                            int wave, int lane) {
-    using C = DirectCfg;
+    using C = DirectCfgT<TM>;
+    constexpr int WMT = C::WMT, NM = 4 * WMT, HALF = C::LOADS_PER_STAGE / 2;
     const char* bt1 = rs + C::A_BYTES;
     const char* bt2 = rs + C::A_BYTES + C::B_BYTES;
+    // read unit u: 0 = a0; 1..8 = the transposed halves of b1[0], b2[0], b1[1], b2[1]; 9.. = a1, a2, ...
+    auto read_unit = [&](int u, v4i16 (&h)[8]) {
+        if (u == 0) {
+            nx.a[0] = a_frag<TM>(rs, wm, lane, rk, 0);
+        } else if (u <= 8) {
+            const int q = u - 1, frag = q >> 1, t = q & 1;  // frag: b1[0], b2[0], b1[1], b2[1]
+            h[q] = b_frag_half((frag & 1) ? bt2 : bt1, 64 * wn + 32 * (frag >> 1), 16 * rk, lane, t);
+            if (t == 1) {
+                const bf16x8 v = join(h[q - 1], h[q]);
+                if (frag == 0) nx.b1[0] = v;
+                else if (frag == 1) nx.b2[0] = v;
+                else if (frag == 2) nx.b1[1] = v;
+                else nx.b2[1] = v;
+            }
+        } else {
+            nx.a[u - 8] = a_frag<TM>(rs, wm, lane, rk, u - 8);
+        }
+    };
+    constexpr int NU = 8 + WMT;                     // read units per slice
+    constexpr int UPM = (NU + NM - 1 - HALF) / (NM - HALF) > 1 ? 2 : 1;  // units after each early MFMA
     v4i16 h[8];
 #pragma unroll
-    for (int m = 0; m < 16; m++) {
+    for (int m = 0; m < NM; m++) {
         const int i = m >> 2, j = (m >> 1) & 1;
         if (m & 1) acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b2[j], acc2[i][j], 0, 0, 0);
         else acc1[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b1[j], acc1[i][j], 0, 0, 0);
-        // reads, in the order slice rk's MFMAs need them: a0, b1[0], b2[0], b1[1], b2[1], a1, a2, a3
-        switch (m) {
-            case 0: nx.a[0] = a_frag(rs, wm, lane, rk, 0); break;
-            case 1: h[0] = b_frag_half(bt1, 64 * wn, 16 * rk, lane, 0); break;
-            case 2: h[1] = b_frag_half(bt1, 64 * wn, 16 * rk, lane, 1); nx.b1[0] = join(h[0], h[1]); break;
-            case 3: h[2] = b_frag_half(bt2, 64 * wn, 16 * rk, lane, 0); break;
-            case 4: h[3] = b_frag_half(bt2, 64 * wn, 16 * rk, lane, 1); nx.b2[0] = join(h[2], h[3]); break;
-            case 5: h[4] = b_frag_half(bt1, 64 * wn + 32, 16 * rk, lane, 0); break;
-            case 6: h[5] = b_frag_half(bt1, 64 * wn + 32, 16 * rk, lane, 1); nx.b1[1] = join(h[4], h[5]); break;
-            case 7: h[6] = b_frag_half(bt2, 64 * wn + 32, 16 * rk, lane, 0); break;
-            case 8: h[7] = b_frag_half(bt2, 64 * wn + 32, 16 * rk, lane, 1); nx.b2[1] = join(h[6], h[7]); break;
-            case 9: nx.a[1] = a_frag(rs, wm, lane, rk, 1); break;
-            case 10: nx.a[2] = a_frag(rs, wm, lane, rk, 2); break;
-            case 11: nx.a[3] = a_frag(rs, wm, lane, rk, 3); break;
-            default: break;
+#pragma unroll
+        for (int u = m * UPM; u < (m + 1) * UPM; u++)
+            if (u < NU) read_unit(u, h);
+        // the last HALF MFMAs (every other one for the full tile) carry the load slots
+        if constexpr (WMT == 4) {
+            if (m >= 9 && (m & 1))
+                dma_slot<TM>(slot0 + (m - 9) / 2, a, b1, b2, N, K, m0, n0, k0, base, wave, lane);
+        } else {
+            if (m >= NM - HALF)
+                dma_slot<TM>(slot0 + m - (NM - HALF), a, b1, b2, N, K, m0, n0, k0, base, wave, lane);
         }
-        if (m >= 9 && (m & 1))
-            dma_slot(slot0 + (m - 9) / 2, a, b1, b2, N, K, m0, n0, k0, base, wave, lane);
         // keep this order: the scheduler would otherwise bunch the reads and the MFMAs
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-template <int S, int MODE>
-__global__ void __launch_bounds__(THREADS, 1)
-swiglu_direct_kernel(DualArgs p) {
+// One workgroup's tile (TM rows from m0, 128-column products from n0) over K steps
+// [kt0, kt0 + kt_n), ring of S stages in `lds`.
+template <int TM, int S, int MODE>
+__device__ __forceinline__ void direct_tile(const DualArgs& p, char* lds, int m0, int n0, int kt0, int kt_n,
+                                            int split) {
     const uint16_t *a = p.a, *b1 = p.b1, *b2 = p.b2;
     const int N = p.N, K = p.K;
-    using C = DirectCfg;
-    constexpr int LPS = C::LOADS_PER_STAGE;
-    static_assert(S >= 3 && S * C::STAGE_BYTES <= 160 * 1024, "ring of 3 to 5 stages of 32 KiB");
-    __shared__ __attribute__((aligned(1024))) char lds[S * C::STAGE_BYTES];
-
-    // With K split, workgroup (split, tile) = (bid / tiles, bid % tiles) covers K steps
-    // [split * ksteps, split * ksteps + ksteps) of its tile.
-    const int ntiles = p.tiles_m * p.tiles_n;
-    const int split = blockIdx.x / ntiles;
-    const Tile tile = tile_of(blockIdx.x - split * ntiles, p.tiles_m, p.tiles_n, p.bn_step);
+    using C = DirectCfgT<TM>;
+    constexpr int LPS = C::LOADS_PER_STAGE, WMT = C::WMT;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
-    floatx16 acc1[WM][WN], acc2[WM][WN];
+    floatx16 acc1[WMT][WN], acc2[WMT][WN];
 #pragma unroll
-    for (int i = 0; i < WM; i++)
+    for (int i = 0; i < WMT; i++)
 #pragma unroll
         for (int j = 0; j < WN; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc1[i][j][r] = acc2[i][j][r] = 0.0f;
 
-    const int kt0 = split * p.ksteps;
-    const int kt_n = min(p.ksteps, K / C::BKD - kt0);
     // Prologue: stages 0 .. S-2.  Every step issues the loads of one stage; past the last K step
     // they reload the last stage into a buffer nobody reads again, which keeps the vmcnt
     // bookkeeping the same on every step.
@@ -533,13 +553,13 @@ swiglu_direct_kernel(DualArgs p) {
         const uint32_t base = lds_addr(lds + s * C::STAGE_BYTES);
         const int k0 = (kt0 + min(s, kt_n - 1)) * C::BKD;
 #pragma unroll
-        for (int l = 0; l < LPS; l++) dma_slot(l, a, b1, b2, N, K, tile.m0, tile.n0, k0, base, wave, lane);
+        for (int l = 0; l < LPS; l++) dma_slot<TM>(l, a, b1, b2, N, K, m0, n0, k0, base, wave, lane);
     }
     wait_vmcnt<LPS * (S - 3)>();  // stages 0 and 1 are in
     __syncthreads();
-    Frags f0, f1;
+    FragsD<WMT> f0, f1;
 #pragma unroll
-    for (int i = 0; i < WM; i++) f0.a[i] = a_frag(lds, wm, lane, 0, i);
+    for (int i = 0; i < WMT; i++) f0.a[i] = a_frag<TM>(lds, wm, lane, 0, i);
 #pragma unroll
     for (int j = 0; j < WN; j++) {
         f0.b1[j] = join(b_frag_half(lds + C::A_BYTES, 64 * wn + 32 * j, 0, lane, 0),
@@ -553,14 +573,41 @@ swiglu_direct_kernel(DualArgs p) {
         const char* sn = lds + ((kt + 1) % S) * C::STAGE_BYTES;
         const uint32_t nbase = lds_addr(lds + ((kt + S - 1) % S) * C::STAGE_BYTES);
         const int nk0 = (kt0 + min(kt + S - 1, kt_n - 1)) * C::BKD;
-        slice_step(f0, f1, st, 1, acc1, acc2, 0, a, b1, b2, N, K, tile.m0, tile.n0, nk0, nbase, wm, wn, wave, lane);
-        slice_step(f1, f0, sn, 0, acc1, acc2, 4, a, b1, b2, N, K, tile.m0, tile.n0, nk0, nbase, wm, wn, wave, lane);
+        slice_step<TM>(f0, f1, st, 1, acc1, acc2, 0, a, b1, b2, N, K, m0, n0, nk0, nbase, wm, wn, wave, lane);
+        slice_step<TM>(f1, f0, sn, 0, acc1, acc2, LPS / 2, a, b1, b2, N, K, m0, n0, nk0, nbase, wm, wn, wave,
+                       lane);
         wait_vmcnt<LPS * (S - 3)>();
         __syncthreads();
     }
     wait_vmcnt<0>();  // no load may still be writing this workgroup's LDS when it ends
 
-    store_tile<MODE>(p, acc1, acc2, tile.m0, tile.n0, wm, wn, lane, split);
+    store_tile<MODE, WMT>(p, acc1, acc2, m0, n0, wm, wn, lane, split);
+}
+
+// Workgroup roles.  Split K (p.tail = 0): workgroup (split, tile) = (bid / tiles, bid % tiles)
+// covers K steps [split * ksteps, split * ksteps + ksteps) of its tile.  Otherwise the first
+// tiles - tail workgroups take a whole tile each, and the last 2 tail workgroups take the
+// remaining tiles as 128-row halves: when the tiles leave a last round of at most half the CUs,
+// that round then takes about half as long.
+template <int S, int MODE>
+__global__ void __launch_bounds__(THREADS, 1)
+swiglu_direct_kernel(DualArgs p) {
+    static_assert(S >= 3 && S * DirectCfg::STAGE_BYTES <= 160 * 1024, "ring of 3 to 5 stages of 32 KiB");
+    __shared__ __attribute__((aligned(1024))) char lds[S * DirectCfg::STAGE_BYTES];
+    const int ntiles = p.tiles_m * p.tiles_n;
+    const int kt_all = p.K / DirectCfg::BKD;
+    const int bid = blockIdx.x;
+    const int head = ntiles - p.tail;
+    if (p.tail == 0 || bid < head) {
+        const int split = bid / ntiles;
+        const Tile tile = tile_of(bid - split * ntiles, p.tiles_m, p.tiles_n, p.bn_step);
+        const int kt0 = split * p.ksteps;
+        direct_tile<BM, S, MODE>(p, lds, tile.m0, tile.n0, kt0, min(p.ksteps, kt_all - kt0), split);
+    } else {
+        const int q = bid - head;
+        const Tile tile = tile_of(head + (q >> 1), p.tiles_m, p.tiles_n, p.bn_step);
+        direct_tile<BM / 2, S, MODE>(p, lds, tile.m0 + (BM / 2) * (q & 1), tile.n0, 0, kt_all, 0);
+    }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -619,6 +666,18 @@ int direct_stages(int M, int N, int K, bool aligned, int tile_cols) {
     return (st >= 3 && st <= 5) ? st : 4;
 }
 
+// Tiles of the last round that the full-tile kernel runs as 128-row halves: when the tiles take
+// two or more rounds over the CUs and the last round fills at most half of them (560 tiles on
+// 256 CUs: 48).  FUSE_SWIGLU_TAIL=0 turns it off for measurement.
+int tail_tiles(int ntiles) {
+    const char* e = getenv("FUSE_SWIGLU_TAIL");
+    if (e && atoi(e) == 0) return 0;
+    const int cus = cu_count();
+    const int rounds = (ntiles + cus - 1) / cus;
+    const int last = ntiles - (rounds - 1) * cus;
+    return (rounds >= 2 && 2 * last <= cus) ? last : 0;
+}
+
 // Launch of the dual-product kernels: `tile_cols` output columns per tile (128 for SwiGLU, whose
 // two products cover the same 128 columns; 256 for a GEMM, whose two halves are adjacent).
 template <int MODE>
@@ -630,8 +689,9 @@ hipError_t launch(DualArgs p, int tile_cols, hipStream_t stream) {
     if ((int64_t)p.tiles_m * p.tiles_n > 0x7fffffff) return hipErrorInvalidValue;
     const bool aligned = (p.K % 8 == 0) && (p.N % 8 == 0) &&
                          (((uintptr_t)p.a | (uintptr_t)p.b1 | (uintptr_t)p.b2) & 15u) == 0;
-    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(THREADS);
     const int st = direct_stages(p.M, p.N, p.K, aligned, tile_cols);
+    p.tail = st != 0 ? tail_tiles(p.tiles_m * p.tiles_n) : 0;
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n + p.tail)), block(THREADS);
     if (st == 3) hipLaunchKernelGGL((swiglu_direct_kernel<3, MODE>), grid, block, 0, stream, p);
     else if (st == 4) hipLaunchKernelGGL((swiglu_direct_kernel<4, MODE>), grid, block, 0, stream, p);
     else if (st == 5) hipLaunchKernelGGL((swiglu_direct_kernel<5, MODE>), grid, block, 0, stream, p);
