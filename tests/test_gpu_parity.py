@@ -655,6 +655,41 @@ def test_empty_kernels_eager_and_captured():
     api.fuse_empty_kernels(0)
 
 
+def test_empty_inputs_launch_nothing():
+    # rows == 0 / M == 0 are valid no-ops for every entry point (nothing is enqueued)
+    announce("empty inputs")
+    e16 = torch.empty(0, 4096, dtype=torch.float16, device="cuda")
+    p16 = torch.zeros(4096, dtype=torch.float16, device="cuda")
+    assert api.fuse_add_layernorm(e16, e16, p16, p16).shape == (0, 4096)
+    y, s, m, v = api.fuse_add_layernorm_ex(e16, None, p16, p16, relu=True, want_sum=True, want_stats=True)
+    assert y.numel() == 0 and s.numel() == 0 and m.numel() == 0 and v.numel() == 0
+    assert api.fuse_bias_gelu_residual(e16, p16, e16).numel() == 0
+    assert api.fuse_softmax_rows(e16, 0.5).numel() == 0
+    assert api.fuse_cumsum_scale_rows(e16, 0.5).numel() == 0
+    a = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros(64, 128, dtype=torch.bfloat16, device="cuda")
+    assert api.fuse_swiglu_dualgemm(a, b, b).shape == (0, 128)
+    assert api.fuse_gemm_bias_act(a, b, None, "relu").shape == (0, 128)
+    assert api.fuse_swiglu_auto(a, b, b).shape == (0, 128)
+    torch.cuda.synchronize()
+
+
+def test_swiglu_gemm_largest_k_and_n():
+    # K and N at their limit (2^21): the 32-bit offsets inside a tile and a K step stay in range
+    announce("swiglu K = 2^21")
+    K = 1 << 21
+    d = synth.swiglu_inputs(256, 128, K, "bf16", seed=31)
+    out = api.fuse_swiglu_dualgemm(d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda())
+    rows = torch.tensor([0, 77, 128, 255])
+    assert_close(out[rows.cuda()], oracle.swiglu(d["a"][rows], d["b1"], d["b2"]), "bf16", "K = 2^21")
+    announce("gemm N = 2^21")
+    N = 1 << 21
+    d = synth.gemm_inputs(256, N, 32, "bf16", seed=32)
+    y = api.fuse_gemm_bias_act(d["x"].cuda(), d["w"].cuda(), d["bias"].cuda(), "relu")
+    rows = torch.tensor([3, 200])
+    assert_close(y[rows.cuda()], oracle.gemm_bias_act(d["x"][rows], d["w"], d["bias"], "relu"), "bf16", "N = 2^21")
+
+
 def test_binding_reports_status_errors():
     x = torch.zeros(4, 64, dtype=torch.float16, device="cuda")
     with pytest.raises(api.FuseError):
