@@ -354,6 +354,24 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
                              "frac": round(gb / peak_bw, 4), "bound": "hbm",
                              "note": "plain copy of 24 MiB (48 MiB moved): the achievable streaming ceiling"}
         log(f"copy: {us:.2f} us {gb:.0f} GB/s")
+        del bufs
+
+        # the same ceiling at the softmax's size (256 MiB read, 256 MiB written)
+        nbytes = 256 << 20
+        bufs = [(torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1),
+                 torch.empty(nbytes, dtype=torch.uint8, device="cuda")) for _ in range(3)]
+
+        def cp_big(i):
+            s, t = bufs[i % len(bufs)]
+            api.fuse_copy(s, t)
+        _, ev = time_launches(torch, stream, cp_big, n_launch // 2)
+        us = ev * 1e3 / (n_launch // 2)
+        gb = 2 * nbytes / (us * 1e-6) / 1e9
+        out["copy_512MiB"] = {"avg_launch_us": round(us, 3), "achieved_gbps": round(gb, 1),
+                              "frac": round(gb / peak_bw, 4), "bound": "hbm",
+                              "note": "plain copy of 256 MiB (512 MiB moved): the ceiling at the softmax's size"}
+        log(f"copy 512 MiB: {us:.2f} us {gb:.0f} GB/s")
+        del bufs
     return out
 
 
