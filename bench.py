@@ -471,6 +471,28 @@ def counters_rows(torch, api, synth, n=4):
     log(f"counters: 8 x copy of {nbytes} bytes")
 
 
+def dispatch_only(torch, api, synth, name, count):
+    """`count` eager dispatches of one fused row at its workload (for a profiler run), no timing."""
+    w = synth.WORKLOADS[name]
+    d = {k: (v.cuda() if hasattr(v, "cuda") else v) for k, v in w.inputs().items()}
+    if w.op == "swiglu":
+        call = lambda: api.fuse_swiglu_dualgemm(d["a"], d["b1"], d["b2"])
+    elif w.op == "gemm_bias_act":
+        call = lambda: api.fuse_gemm_bias_act(d["x"], d["w"], d["bias"], "relu")
+    elif w.op == "softmax_rows":
+        call = lambda: api.fuse_softmax_rows(d["x"], d["scale"])
+    elif w.op == "cumsum_scale_rows":
+        call = lambda: api.fuse_cumsum_scale_rows(d["x"], d["scale"])
+    elif w.op == "bias_gelu_residual":
+        call = lambda: api.fuse_bias_gelu_residual(d["x"], d["bias"], d["residual"])
+    else:
+        call = lambda: api.fuse_add_layernorm(d["x"], d["residual"], d["gamma"], d["beta"], d["eps"])
+    for _ in range(count):
+        call()
+        torch.cuda.synchronize()
+    log(f"dispatched {count} x {name}")
+
+
 def launch_study(torch, api, synth, n_empty=4000, n_graph=1000, n_steps=200):
     """Launch cost on this GPU ([P2] §4.5, [P3] §2): an empty kernel enqueued from a loop inside
     the library (host cost per call, back-to-back interval on the GPU, cost per kernel inside a
@@ -620,6 +642,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--counters", action="store_true",
                     help="only run the short dispatch sequence read by rocprofv3 --pmc, no timing")
+    ap.add_argument("--dispatch", metavar="WORKLOAD",
+                    help="only dispatch the fused kernel of one workload --dispatch-count times (profiling)")
+    ap.add_argument("--dispatch-count", type=int, default=3)
     ap.add_argument("--counters-rows", action="store_true",
                     help="the same for the other rows of the path (their fused and unfused kernels)")
     a = ap.parse_args()
@@ -640,6 +665,9 @@ def main():
         return
     if a.counters_rows:
         counters_rows(torch, api, synth)
+        return
+    if a.dispatch:
+        dispatch_only(torch, api, synth, a.dispatch, a.dispatch_count)
         return
     h = headline(torch, api, synth, roofline, a.steps, a.warmup)
     log(f"headline: {h['avg_launch_us']:.2f} us/launch, value {h['value_gbps']:.0f} GB/s")
