@@ -1,26 +1,33 @@
-// swiglu.hip -- fused SwiGLU dual GEMM on the gfx950 matrix cores:
-//   out[M,N] = SiLU(a[M,K] . b1[K,N]) * (a[M,K] . b2[K,N]), bf16 in and out, fp32 accumulation.
+// swiglu.hip -- dual-product MFMA kernels on the gfx950 matrix cores, bf16 in and out, fp32
+// accumulation:
+//   SwiGLU            out = SiLU(a . b1) * (a . b2)          (a [M,K], b1 and b2 [K,N])
+//   GEMM + bias + act y = act(x . W + bias)                  (each 256-column tile as two halves)
+// and the split-K form and the unfused baselines built on the same kernels.
 //
-// Tiling.  A 256-thread workgroup (4 waves, 2 x 2) owns a 256 x 128 tile of out and keeps two
-// fp32 accumulator sets, one per product: each wave holds 4 x 2 blocks of 32 x 32 for C1 and the
-// same for C2 (v_mfma_f32_32x32x16_bf16, 16 fp32 per lane per block, 256 accumulators per lane,
-// held in AGPRs).  Per 16-deep k slice a wave reads 8 fragments from LDS (4 of a, 2 of b1, 2 of
-// b2) for 16 MFMAs: every a fragment feeds one MFMA against b1 and one against b2, so the a tile
-// is loaded from memory once for both products.
+// Tiling.  A 256-thread workgroup (4 waves, 2 x 2) owns a 256 x 128 tile and keeps two fp32
+// accumulator sets, one per product: each wave holds 4 x 2 blocks of 32 x 32 for C1 and the same
+// for C2 (v_mfma_f32_32x32x16_bf16, 16 fp32 per lane per block, 256 accumulators per lane, held
+// in AGPRs).  Per 16-deep k slice a wave reads 8 fragments from LDS (4 of a, 2 of b1, 2 of b2)
+// for 16 MFMAs: every a fragment feeds one MFMA against b1 and one against b2, so the a tile is
+// loaded from memory once for both products.
 //
-// Layouts.  The matrix cores want both operands with 8 consecutive k values per lane.  a is
-// row-major [M,K] (k contiguous) and is copied to LDS as is.  b1 and b2 are row-major [K,N]
-// (n contiguous); each thread loads an 8 (k) x 8 (n) block with eight 128-bit loads, transposes
-// it in registers and writes eight 128-bit rows of the k-contiguous LDS tile Bt[n][k].  LDS rows
-// are 64 bf16 (eight 16-byte chunks); chunk q of row r lives at chunk q ^ ((r ^ r>>3) & 7), which
-// keeps the fragment reads (16 consecutive rows per 16 lanes, 64 banks) and the transposed writes
-// (rows 8 apart) free of bank conflicts.
+// Two kernels.  Full tiles (the workloads) take the direct kernel further down: operands go
+// straight from memory into a ring of LDS stages and b is transposed at fragment-read time.
+// Any other shape takes the general kernel below, which stages through registers:
 //
-// Pipeline (general kernel).  LDS holds two stages of 64 KiB.  While the MFMAs consume one stage, the registers
-// loaded during the previous step are written to the other stage and the global loads of the
-// step after are issued; fragments are double-buffered in registers so the LDS reads of the next
-// k slice are in flight during the current slice's MFMAs.  One barrier per K step of 64; one
-// workgroup per CU (one wave per SIMD, up to 512 registers per lane).
+// General kernel layouts.  The matrix cores want both operands with 8 consecutive k values per
+// lane.  a is row-major [M,K] (k contiguous) and is copied to LDS as is.  b1 and b2 are
+// row-major [K,N] (n contiguous); each thread loads an 8 (k) x 8 (n) block with eight 128-bit
+// loads, transposes it in registers and writes eight 128-bit rows of the k-contiguous LDS tile
+// Bt[n][k].  LDS rows are 64 bf16 (eight 16-byte chunks); chunk q of row r lives at chunk
+// q ^ ((r ^ r>>3) & 7), which keeps the fragment reads (16 consecutive rows per 16 lanes, 64
+// banks) and the transposed writes (rows 8 apart) free of bank conflicts.
+//
+// General kernel pipeline.  LDS holds two stages of 64 KiB.  While the MFMAs consume one stage,
+// the registers loaded during the previous step are written to the other stage and the global
+// loads of the step after are issued; fragments are double-buffered in registers so the LDS
+// reads of the next k slice are in flight during the current slice's MFMAs.  One barrier per K
+// step of 64; one workgroup per CU (one wave per SIMD, up to 512 registers per lane).
 //
 // Scheduling.  Workgroups are dispatched round-robin over the 8 XCDs; the tile index is remapped
 // so that each XCD owns a contiguous range of tiles, walked with M fastest, so that workgroups
@@ -45,8 +52,6 @@ constexpr int NUM_XCD = 8;
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 // Element offset of 16-byte chunk q (0..7) of LDS row r.
 __device__ __forceinline__ int lds_off(int r, int q) { return r * BK + ((q ^ swz(r)) << 3); }
-
-__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
 // 8 bf16 at element offset e0 of resource r; elements at index >= avail are zero (per-element
 // path for operands whose rows are not 16-byte aligned).
