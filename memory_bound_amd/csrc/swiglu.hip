@@ -207,7 +207,8 @@ struct DualArgs {
     int tiles_m, tiles_n, bn_step;
     int ksteps;            // 32-deep K steps per workgroup (all of K unless split)
     float* part;           // split K: [splits][planes][M][N] fp32 partial products
-    int tail;              // full-tile kernel: the last `tail` tiles run as two 128-row halves each
+    int tail;              // full-tile kernel: the last `tail` tiles run as `parts` row slices each
+    int parts;             // 2 (128-row halves) or 4 (64-row quarters)
 };
 
 template <int ACT> __device__ __forceinline__ float activation(float t) {
@@ -480,11 +481,12 @@ template <int WMT> struct FragsD {
 template <int TM>
 __device__ __forceinline__ void slice_step(const FragsD<TM / 64>& f, FragsD<TM / 64>& nx, const char* rs, int rk,
                                            floatx16 (&acc1)[TM / 64][WN], floatx16 (&acc2)[TM / 64][WN],
-                                           int slot0, const uint16_t* a, const uint16_t* b1, const uint16_t* b2,
+                                           int slot0, int nslots, const uint16_t* a, const uint16_t* b1,
+                                           const uint16_t* b2,
                                            int N, int K, int m0, int n0, int k0, uint32_t base, int wm, int wn,
                                            int wave, int lane) {
     using C = DirectCfgT<TM>;
-    constexpr int WMT = C::WMT, NM = 4 * WMT, HALF = C::LOADS_PER_STAGE / 2;
+    constexpr int WMT = C::WMT, NM = 4 * WMT;
     const char* bt1 = rs + C::A_BYTES;
     const char* bt2 = rs + C::A_BYTES + C::B_BYTES;
     // read unit u: 0 = a0; 1..8 = the transposed halves of b1[0], b2[0], b1[1], b2[1]; 9.. = a1, a2, ...
@@ -505,8 +507,8 @@ __device__ __forceinline__ void slice_step(const FragsD<TM / 64>& f, FragsD<TM /
             nx.a[u - 8] = a_frag<TM>(rs, wm, lane, rk, u - 8);
         }
     };
-    constexpr int NU = 8 + WMT;                     // read units per slice
-    constexpr int UPM = (NU + NM - 1 - HALF) / (NM - HALF) > 1 ? 2 : 1;  // units after each early MFMA
+    constexpr int NU = 8 + WMT;                  // read units per slice
+    constexpr int UPM = (NU + NM - 1) / NM;      // read units after each of the first MFMAs
     v4i16 h[8];
 #pragma unroll
     for (int m = 0; m < NM; m++) {
@@ -516,13 +518,14 @@ __device__ __forceinline__ void slice_step(const FragsD<TM / 64>& f, FragsD<TM /
 #pragma unroll
         for (int u = m * UPM; u < (m + 1) * UPM; u++)
             if (u < NU) read_unit(u, h);
-        // the last HALF MFMAs (every other one for the full tile) carry the load slots
+        // the load slots: for the full tile after MFMAs 9, 11, 13, 15; otherwise one after each of
+        // the last nslots MFMAs (nslots <= NM)
         if constexpr (WMT == 4) {
-            if (m >= 9 && (m & 1))
+            if (m >= 9 && (m & 1) && (m - 9) / 2 < nslots)
                 dma_slot<TM>(slot0 + (m - 9) / 2, a, b1, b2, N, K, m0, n0, k0, base, wave, lane);
         } else {
-            if (m >= NM - HALF)
-                dma_slot<TM>(slot0 + m - (NM - HALF), a, b1, b2, N, K, m0, n0, k0, base, wave, lane);
+            if (m >= NM - nslots)
+                dma_slot<TM>(slot0 + m - (NM - nslots), a, b1, b2, N, K, m0, n0, k0, base, wave, lane);
         }
         // keep this order: the scheduler would otherwise bunch the reads and the MFMAs
         __builtin_amdgcn_sched_barrier(0);
@@ -578,8 +581,9 @@ __device__ __forceinline__ void direct_tile(const DualArgs& p, char* lds, int m0
         const char* sn = lds + ((kt + 1) % S) * C::STAGE_BYTES;
         const uint32_t nbase = lds_addr(lds + ((kt + S - 1) % S) * C::STAGE_BYTES);
         const int nk0 = (kt0 + min(kt + S - 1, kt_n - 1)) * C::BKD;
-        slice_step<TM>(f0, f1, st, 1, acc1, acc2, 0, a, b1, b2, N, K, m0, n0, nk0, nbase, wm, wn, wave, lane);
-        slice_step<TM>(f1, f0, sn, 0, acc1, acc2, LPS / 2, a, b1, b2, N, K, m0, n0, nk0, nbase, wm, wn, wave,
+        slice_step<TM>(f0, f1, st, 1, acc1, acc2, 0, LPS / 2, a, b1, b2, N, K, m0, n0, nk0, nbase, wm, wn, wave,
+                       lane);
+        slice_step<TM>(f1, f0, sn, 0, acc1, acc2, LPS / 2, LPS - LPS / 2, a, b1, b2, N, K, m0, n0, nk0, nbase, wm, wn, wave,
                        lane);
         wait_vmcnt<LPS * (S - 3)>();
         __syncthreads();
@@ -591,9 +595,9 @@ __device__ __forceinline__ void direct_tile(const DualArgs& p, char* lds, int m0
 
 // Workgroup roles.  Split K (p.tail = 0): workgroup (split, tile) = (bid / tiles, bid % tiles)
 // covers K steps [split * ksteps, split * ksteps + ksteps) of its tile.  Otherwise the first
-// tiles - tail workgroups take a whole tile each, and the last 2 tail workgroups take the
-// remaining tiles as 128-row halves: when the tiles leave a last round of at most half the CUs,
-// that round then takes about half as long.
+// tiles - tail workgroups take a whole tile each, and the last parts * tail workgroups take the
+// remaining tiles as 128-row halves or 64-row quarters: when the tiles leave a last round that
+// fills few CUs, that round is spread over more of them.
 template <int S, int MODE>
 __global__ void __launch_bounds__(THREADS, 1)
 swiglu_direct_kernel(DualArgs p) {
@@ -608,10 +612,14 @@ swiglu_direct_kernel(DualArgs p) {
         const Tile tile = tile_of(bid - split * ntiles, p.tiles_m, p.tiles_n, p.bn_step);
         const int kt0 = split * p.ksteps;
         direct_tile<BM, S, MODE>(p, lds, tile.m0, tile.n0, kt0, min(p.ksteps, kt_all - kt0), split);
-    } else {
+    } else if (p.parts == 2) {
         const int q = bid - head;
         const Tile tile = tile_of(head + (q >> 1), p.tiles_m, p.tiles_n, p.bn_step);
         direct_tile<BM / 2, S, MODE>(p, lds, tile.m0 + (BM / 2) * (q & 1), tile.n0, 0, kt_all, 0);
+    } else {
+        const int q = bid - head;
+        const Tile tile = tile_of(head + (q >> 2), p.tiles_m, p.tiles_n, p.bn_step);
+        direct_tile<BM / 4, S, MODE>(p, lds, tile.m0 + (BM / 4) * (q & 3), tile.n0, 0, kt_all, 0);
     }
 }
 
@@ -671,16 +679,24 @@ int direct_stages(int M, int N, int K, bool aligned, int tile_cols) {
     return (st >= 3 && st <= 5) ? st : 4;
 }
 
-// Tiles of the last round that the full-tile kernel runs as 128-row halves: when the tiles take
-// two or more rounds over the CUs and the last round fills at most half of them (560 tiles on
-// 256 CUs: 48).  FUSE_SWIGLU_TAIL=0 turns it off for measurement.
-int tail_tiles(int ntiles) {
+// Tiles of the last round that the full-tile kernel runs in row slices, and how many slices:
+// when the tiles take two or more rounds over the CUs and the last round fills at most half of
+// them, its tiles run as halves, or as quarters when even those fill at most a quarter (560
+// tiles on 256 CUs: 48 tiles as 192 quarters).  FUSE_SWIGLU_TAIL=0 turns it off and =2 limits it
+// to halves, for measurement.
+struct TailPlan {
+    int tail, parts;
+};
+TailPlan tail_plan(int ntiles) {
     const char* e = getenv("FUSE_SWIGLU_TAIL");
-    if (e && atoi(e) == 0) return 0;
+    const int lim = e ? atoi(e) : 4;
     const int cus = cu_count();
     const int rounds = (ntiles + cus - 1) / cus;
     const int last = ntiles - (rounds - 1) * cus;
-    return (rounds >= 2 && 2 * last <= cus) ? last : 0;
+    if (rounds < 2 || lim < 2) return {0, 0};
+    if (lim >= 4 && 4 * last <= cus) return {last, 4};
+    if (2 * last <= cus) return {last, 2};
+    return {0, 0};
 }
 
 // Launch of the dual-product kernels: `tile_cols` output columns per tile (128 for SwiGLU, whose
@@ -695,8 +711,10 @@ hipError_t launch(DualArgs p, int tile_cols, hipStream_t stream) {
     const bool aligned = (p.K % 8 == 0) && (p.N % 8 == 0) &&
                          (((uintptr_t)p.a | (uintptr_t)p.b1 | (uintptr_t)p.b2) & 15u) == 0;
     const int st = direct_stages(p.M, p.N, p.K, aligned, tile_cols);
-    p.tail = st != 0 ? tail_tiles(p.tiles_m * p.tiles_n) : 0;
-    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n + p.tail)), block(THREADS);
+    const TailPlan tp = st != 0 ? tail_plan(p.tiles_m * p.tiles_n) : TailPlan{0, 0};
+    p.tail = tp.tail;
+    p.parts = tp.parts;
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n + (tp.parts - 1) * tp.tail)), block(THREADS);
     if (st == 3) hipLaunchKernelGGL((swiglu_direct_kernel<3, MODE>), grid, block, 0, stream, p);
     else if (st == 4) hipLaunchKernelGGL((swiglu_direct_kernel<4, MODE>), grid, block, 0, stream, p);
     else if (st == 5) hipLaunchKernelGGL((swiglu_direct_kernel<5, MODE>), grid, block, 0, stream, p);

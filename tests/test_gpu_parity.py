@@ -429,26 +429,29 @@ def test_swiglu_full_tile_paths(monkeypatch, env):
             assert_close(out, oracle.swiglu(d["a"], d["b1"], d["b2"]), "bf16", f"swiglu N={N} K={K} {env}")
 
 
-def test_swiglu_last_round_halves(monkeypatch):
-    # 5 x 53 = 265 tiles on 256 CUs: the last 9 tiles run as 128-row halves.  Same k order per
-    # element either way, so the result is bit-identical to whole tiles; checked against the
-    # oracle on every fourth row.
+def test_swiglu_last_round_slices(monkeypatch):
+    # 5 x 53 = 265 tiles on 256 CUs: the last 9 tiles run as 64-row quarters by default, as 128-row
+    # halves with FUSE_SWIGLU_TAIL=2, whole with =0.  Same k order per element every way, so the
+    # results are bit-identical; checked against the oracle on every fourth row.
     M, N, K = 1280, 6784, 256
-    announce(f"swiglu {M}x{N}x{K} last-round halves")
+    announce(f"swiglu {M}x{N}x{K} last-round slices")
     d = synth.swiglu_inputs(M, N, K, "bf16", seed=29)
     a, b1, b2 = d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda()
     out = api.fuse_swiglu_dualgemm(a, b1, b2)
     rows = torch.arange(0, M, 4)
-    assert_close(out[rows.cuda()], oracle.swiglu(d["a"][rows], d["b1"], d["b2"]), "bf16", "halves")
-    monkeypatch.setenv("FUSE_SWIGLU_TAIL", "0")
-    assert torch.equal(out, api.fuse_swiglu_dualgemm(a, b1, b2))
+    assert_close(out[rows.cuda()], oracle.swiglu(d["a"][rows], d["b1"], d["b2"]), "bf16", "quarters")
+    for tail in ("2", "0"):
+        monkeypatch.setenv("FUSE_SWIGLU_TAIL", tail)
+        assert torch.equal(out, api.fuse_swiglu_dualgemm(a, b1, b2)), f"tail {tail}"
     d = synth.gemm_inputs(M, 2 * N, K, "bf16", seed=30)  # the same tile grid for the GEMM
     x, w, bias = d["x"].cuda(), d["w"].cuda(), d["bias"].cuda()
     y0 = api.fuse_gemm_bias_act(x, w, bias, "gelu")
+    monkeypatch.setenv("FUSE_SWIGLU_TAIL", "2")
+    assert torch.equal(y0, api.fuse_gemm_bias_act(x, w, bias, "gelu")), "gemm halves"
     monkeypatch.delenv("FUSE_SWIGLU_TAIL")
     y1 = api.fuse_gemm_bias_act(x, w, bias, "gelu")
-    assert torch.equal(y0, y1)
-    assert_close(y1[rows.cuda()], oracle.gemm_bias_act(d["x"][rows], d["w"], d["bias"], "gelu"), "bf16", "gemm halves")
+    assert torch.equal(y0, y1), "gemm quarters"
+    assert_close(y1[rows.cuda()], oracle.gemm_bias_act(d["x"][rows], d["w"], d["bias"], "gelu"), "bf16", "gemm quarters")
 
 
 @pytest.mark.parametrize("stages", [None, "3", "5"])
