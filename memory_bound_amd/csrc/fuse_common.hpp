@@ -57,6 +57,11 @@ template <DT D> __device__ __forceinline__ void unpack(const uint4& w, float* ou
     }
 }
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+// VEC fp32 values -> one 128-bit word.  16-bit types convert in pairs (v_cvt_pk_f16_f32,
+// v_cvt_pk_bf16_f32: one instruction per two elements, round to nearest even).
 template <DT D> __device__ __forceinline__ uint4 pack(const float* v) {
     uint32_t u[4];
     if constexpr (D == DT::F32) {
@@ -64,12 +69,37 @@ template <DT D> __device__ __forceinline__ uint4 pack(const float* v) {
         for (int i = 0; i < 4; i++) u[i] = __builtin_bit_cast(uint32_t, v[i]);
     } else if constexpr (D == DT::F16) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) u[i] = f32_to_f16(v[2 * i]) | (f32_to_f16(v[2 * i + 1]) << 16);
+        for (int i = 0; i < 4; i++) {
+            const half2_t h = {(_Float16)v[2 * i], (_Float16)v[2 * i + 1]};
+            u[i] = __builtin_bit_cast(uint32_t, h);
+        }
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; i++) u[i] = f32_to_bf16(v[2 * i]) | (f32_to_bf16(v[2 * i + 1]) << 16);
+        for (int i = 0; i < 4; i++) {
+            const bf162_t h = {(__bf16)v[2 * i], (__bf16)v[2 * i + 1]};
+            u[i] = __builtin_bit_cast(uint32_t, h);
+        }
     }
     return make_uint4(u[0], u[1], u[2], u[3]);
+}
+
+// round_f16(a0 * g.lo + b.lo) | round_f16(a1 * g.hi + b.hi) << 16, with g and b packed f16 pairs:
+// v_fma_mixlo_f16 / v_fma_mixhi_f16 widen g and b, fuse the multiply-add and round once, from the
+// exact result, to f16 (fp32 fmaf then a conversion would round twice).
+__device__ __forceinline__ uint32_t fma_mix_f16x2(float a0, float a1, uint32_t g, uint32_t b) {
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[0,1,1]" : "=v"(r) : "v"(a0), "v"(g), "v"(b));
+    asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[0,1,1] op_sel_hi:[0,1,1]" : "+v"(r) : "v"(a1), "v"(g), "v"(b));
+    return r;
+}
+
+// 1.0f that the compiler cannot fold away: fmaf(a, one, b) is exactly a + b (a * 1 is exact, one
+// rounding), but left as a fused multiply-add it merges with the f16 -> fp32 widening of a and b
+// into one mixed-precision instruction (v_fma_mix_f32) instead of two conversions and an add.
+__device__ __forceinline__ float opaque_one() {
+    float one;
+    asm("s_mov_b32 %0, 1.0" : "=s"(one));
+    return one;
 }
 
 // ------------------------------------------------------------------------------------------------

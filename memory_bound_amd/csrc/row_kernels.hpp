@@ -86,6 +86,9 @@ template <DT D, bool VECP, int NV, int WPR> struct RowSlice {
         if constexpr (VECP) unpack<D>(bload16<AUX>(r, (uint32_t)chunk(j) * 16u), out);
         else out[0] = bload_elem<D, AUX>(r, (uint32_t)chunk(j));
     }
+    template <int AUX = AUX_DEFAULT> __device__ __forceinline__ void store_raw(rsrc_t r, int j, const uint4& w) const {
+        bstore16<AUX>(r, (uint32_t)chunk(j) * 16u, w);
+    }
     template <int AUX = AUX_DEFAULT> __device__ __forceinline__ void store(rsrc_t r, int j, const float* v) const {
         if constexpr (VECP) bstore16<AUX>(r, (uint32_t)chunk(j) * 16u, pack<D>(v));
         else bstore_elem<D, AUX>(r, (uint32_t)chunk(j), v[0]);
@@ -152,6 +155,9 @@ __device__ __forceinline__ void add_layernorm_row(const typename Elem<D>::T* x, 
     }
     __builtin_amdgcn_sched_barrier(0);  // issue all of the above before anything below
 
+    // 1 / hidden, correctly rounded; computed while the loads are in flight
+    const float inv_h = 1.0f / (float)hidden;
+    const float one = opaque_one();
     float v[NV][V], g[NV][V], b[NV][V];
     float sum = 0.0f;
 #pragma unroll
@@ -161,7 +167,7 @@ __device__ __forceinline__ void add_layernorm_row(const typename Elem<D>::T* x, 
             float rv[V];
             s.unpack_raw(wr[j], rv);
 #pragma unroll
-            for (int k = 0; k < V; k++) v[j][k] += rv[k];
+            for (int k = 0; k < V; k++) v[j][k] = fmaf(v[j][k], one, rv[k]);  // x + r
         }
 #pragma unroll
         for (int k = 0; k < V; k++) sum += v[j][k];  // zeros outside the row
@@ -174,51 +180,98 @@ __device__ __forceinline__ void add_layernorm_row(const typename Elem<D>::T* x, 
         sum += __builtin_bit_cast(float, dep & (uint32_t)(hidden >> 31));  // adds +0.0f
     }
     sum = row_allreduce<WPR>(sum, SumOp{}, lds_sum);
-    const float mean = sum / (float)hidden;
+    // mean = sum / hidden correctly rounded: the product with the correctly rounded reciprocal,
+    // then one correction by the exact remainder (Markstein's division step).  A constant row thus
+    // has its value as mean exactly, whenever its sum is exact.
+    const float hf = (float)hidden;
+    const float q0 = sum * inv_h;
+    const float mean = fmaf(fmaf(-q0, hf, sum), inv_h, q0);
 
-    // branch-free (a select per chunk) so that the kernel stays one basic block and the compiler
-    // cannot sink the gamma/beta loads down to their use
+    // deviations d = v - mean, kept for the output; chunks past the end of the row (only when the
+    // row leaves some of the slice's chunks empty) are left out of the second sum with a select
     float sq = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NV; j++) {
-        const bool in_row = s.ok(j);
+    for (int j = 0; j < NV; j++)
 #pragma unroll
-        for (int k = 0; k < V; k++) {
-            const float d = in_row ? v[j][k] - mean : 0.0f;
-            sq = fmaf(d, d, sq);
+        for (int k = 0; k < V; k++) v[j][k] -= mean;
+    if (s.nchunk == NV * WPR * 64) {
+#pragma unroll
+        for (int j = 0; j < NV; j++)
+#pragma unroll
+            for (int k = 0; k < V; k++) sq = fmaf(v[j][k], v[j][k], sq);
+    } else {
+#pragma unroll
+        for (int j = 0; j < NV; j++) {
+            const bool in_row = s.ok(j);
+#pragma unroll
+            for (int k = 0; k < V; k++) {
+                const float d = in_row ? v[j][k] : 0.0f;
+                sq = fmaf(d, d, sq);
+            }
         }
     }
     sq = row_allreduce<WPR>(sq, SumOp{}, lds_sq);
-    const float rstd = 1.0f / sqrtf(sq / (float)hidden + eps);
+    const float var = sq * inv_h;
+    const float rstd = __builtin_amdgcn_rsqf(var + eps);  // v_rsq_f32, within about 1 ulp
     if constexpr (EX) {
         // one lane of the row's first wave writes the statistics
         const bool leader = (threadIdx.x & 63) == 0 && (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % WPR) == 0;
         const rsrc_t rm = make_rsrc(ex.mean ? ex.mean + row : (float*)y, ex.mean && row < rows ? 4u : 0u);
         const rsrc_t rv = make_rsrc(ex.var ? ex.var + row : (float*)y, ex.var && row < rows ? 4u : 0u);
         bstore_b32(rm, leader ? 0u : OOB, __builtin_bit_cast(uint32_t, mean));
-        bstore_b32(rv, leader ? 0u : OOB, __builtin_bit_cast(uint32_t, sq / (float)hidden));
+        bstore_b32(rv, leader ? 0u : OOB, __builtin_bit_cast(uint32_t, var));
     }
 
+    if constexpr (D == DT::F16 && VECP) {
+        // f16 out: y = round_f16(d * rstd * gamma + beta) from the packed gamma/beta words, one
+        // rounding per element, two instructions per pair
 #pragma unroll
-    for (int j = 0; j < NV; j++) {
-        if constexpr (PREFETCH_AFFINE) {
-            s.unpack_raw(wg[j], g[j]);
-            s.unpack_raw(wb[j], b[j]);
-        } else {
-            s.load(rg, j, g[j]);
-            s.load(rb, j, b[j]);
+        for (int j = 0; j < NV; j++) {
+            if constexpr (!PREFETCH_AFFINE) {
+                wg[j] = s.load_raw(rg, j);
+                wb[j] = s.load_raw(rb, j);
+            }
+            const uint32_t gw[4] = {wg[j].x, wg[j].y, wg[j].z, wg[j].w};
+            const uint32_t bw[4] = {wb[j].x, wb[j].y, wb[j].z, wb[j].w};
+            uint32_t u[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                u[i] = fma_mix_f16x2(v[j][2 * i] * rstd, v[j][2 * i + 1] * rstd, gw[i], bw[i]);
+                if constexpr (EX) {
+                    // ReLU on the rounded values: a half with its sign set that is not a NaN
+                    // (a negative number or -0) becomes +0
+                    if (ex.relu) {
+                        const uint32_t lo = u[i] & 0xffffu, hi = u[i] >> 16;
+                        const bool zlo = (lo & 0x8000u) && (lo & 0x7fffu) <= 0x7c00u;
+                        const bool zhi = (hi & 0x8000u) && (hi & 0x7fffu) <= 0x7c00u;
+                        u[i] = (zlo ? 0u : lo) | ((zhi ? 0u : hi) << 16);
+                    }
+                }
+            }
+            s.template store_raw<AUX_STREAM>(ry, j, make_uint4(u[0], u[1], u[2], u[3]));
         }
-    }
+    } else {
 #pragma unroll
-    for (int j = 0; j < NV; j++) {
-        float o[V];
-#pragma unroll
-        for (int k = 0; k < V; k++) o[k] = fmaf((v[j][k] - mean) * rstd, g[j][k], b[j][k]);
-        if constexpr (EX) {
-#pragma unroll
-            for (int k = 0; k < V; k++) o[k] = (ex.relu && o[k] < 0.0f) ? 0.0f : o[k];
+        for (int j = 0; j < NV; j++) {
+            if constexpr (PREFETCH_AFFINE) {
+                s.unpack_raw(wg[j], g[j]);
+                s.unpack_raw(wb[j], b[j]);
+            } else {
+                s.load(rg, j, g[j]);
+                s.load(rb, j, b[j]);
+            }
         }
-        s.template store<AUX_STREAM>(ry, j, o);
+#pragma unroll
+        for (int j = 0; j < NV; j++) {
+            float o[V];
+#pragma unroll
+            for (int k = 0; k < V; k++) o[k] = fmaf(v[j][k] * rstd, g[j][k], b[j][k]);
+            if constexpr (EX) {
+#pragma unroll
+                for (int k = 0; k < V; k++) o[k] = (ex.relu && o[k] < 0.0f) ? 0.0f : o[k];
+            }
+            s.template store<AUX_STREAM>(ry, j, o);
+        }
     }
 }
 
