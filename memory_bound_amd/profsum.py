@@ -30,8 +30,10 @@ def trace(db_path: str) -> list[dict]:
         g[(short_name(name), gx, wx)].append(dur / 1e3)
     out = []
     for (n, gx, wx), d in g.items():
+        q = statistics.quantiles(d, n=10, method="inclusive") if len(d) > 1 else [d[0]] * 9
         out.append({"kernel": n, "grid": gx, "wg": wx, "calls": len(d), "mean_us": statistics.mean(d),
-                    "median_us": statistics.median(d), "min_us": min(d), "max_us": max(d)})
+                    "median_us": statistics.median(d), "p10_us": q[0], "p90_us": q[8],
+                    "min_us": min(d), "max_us": max(d)})
     return out
 
 
@@ -53,10 +55,11 @@ def main(argv):
     mode, path = argv[1], argv[2]
     if mode == "trace":
         print(f"{'kernel':64s} {'grid':>9s} {'wg':>4s} {'calls':>5s} {'mean_us':>9s} {'median_us':>9s} "
-              f"{'min_us':>8s} {'max_us':>8s}")
+              f"{'p10_us':>8s} {'p90_us':>8s} {'min_us':>8s} {'max_us':>8s}")
         for r in trace(path):
             print(f"{r['kernel'][:64]:64s} {r['grid']:9d} {r['wg']:4d} {r['calls']:5d} {r['mean_us']:9.3f} "
-                  f"{r['median_us']:9.3f} {r['min_us']:8.3f} {r['max_us']:8.3f}")
+                  f"{r['median_us']:9.3f} {r['p10_us']:8.3f} {r['p90_us']:8.3f} {r['min_us']:8.3f} "
+                  f"{r['max_us']:8.3f}")
     elif mode == "pmc":
         print(f"{'kernel':64s} {'grid':>9s} {'counter':>11s} {'calls':>5s} {'mean':>12s} {'median':>12s}")
         for r in pmc(path):

@@ -70,6 +70,8 @@ def _load():
     lib.oracle_round.argtypes = [dp, dp, i64, ctypes.c_int]
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_threads.restype = None
     for name in ("oracle_add_layernorm", "oracle_add_layernorm_ex", "oracle_bias_gelu_residual", "oracle_softmax_rows",
                  "oracle_cumsum_scale_rows",
                  "oracle_matmul", "oracle_swiglu", "oracle_gemm_bias_act", "oracle_activation",
@@ -94,6 +96,11 @@ def _p(a: np.ndarray):
 def threads() -> int:
     """OpenMP threads the oracle's row loops use."""
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Sets the OpenMP threads of the oracle's row loops (for timing it on one core)."""
+    _load().oracle_set_threads(int(n))
 
 
 # ----------------------------------------------------------------------------------------------

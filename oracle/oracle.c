@@ -355,3 +355,16 @@ int oracle_threads(void)
     return 1;
 #endif
 }
+
+/* Sets the OpenMP threads of later parallel regions (n >= 1; no effect without OpenMP).  Used to
+ * time the oracle single-threaded beside the all-core figure. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
