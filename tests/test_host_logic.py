@@ -112,3 +112,21 @@ def test_other_algorithmic_work():
     assert roofline.cumsum_scale_rows_bytes(2048, 4096, "f16", fused=False)["bytes"] == 67_108_864
     assert roofline.gemm_flops(2048, 8960, 1536) == 56_371_445_760
     assert roofline.gemm_bias_act_bytes(2048, 8960, 1536, "bf16")["bytes"] == 2 * (2048 * 1536 + 1536 * 8960 + 8960 + 2048 * 8960)
+
+
+def test_oracle_thread_count_round_trip():
+    # the one-thread timing in the bench's CPU baseline sets and restores the OpenMP thread count;
+    # the result must not depend on it
+    import oracle
+
+    n = oracle.threads()
+    d = synth.add_layernorm_inputs(8, 256, "f16", seed=5)
+    x, r, g, b = (oracle.f64(d[k]) for k in ("x", "residual", "gamma", "beta"))
+    y_all = oracle.add_layernorm(x, r, g, b, 1e-5)
+    oracle.set_threads(1)
+    try:
+        assert oracle.threads() == 1
+        assert np.array_equal(oracle.add_layernorm(x, r, g, b, 1e-5), y_all)
+    finally:
+        oracle.set_threads(n)
+    assert oracle.threads() == n
