@@ -174,6 +174,23 @@ def test_add_layernorm_ex_inplace_sum_and_nan():
     _check_ln_ex(outs, dd, False, "bf16", "ln_ex no residual", residual=None)
 
 
+def test_add_layernorm_relu_f16_tiny_negatives_become_plus_zero():
+    # gamma at the smallest f16 subnormal and beta 0: every output lies within one subnormal of
+    # zero, and the negative ones round to -0 or -2^-24 before the clamp.  The clamp must store
+    # +0 for all of them (the oracle clamps first, then rounds), never the bit pattern of -0.
+    announce("add_layernorm_ex relu f16 tiny negatives")
+    d = synth.add_layernorm_inputs(16, 2048, "f16", seed=43)
+    d["gamma"] = torch.full((2048,), 2.0 ** -24, dtype=torch.float16)
+    d["beta"] = torch.zeros(2048, dtype=torch.float16)
+    g = cuda(d)
+    y = api.fuse_add_layernorm_ex(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"], relu=True)[0].cpu()
+    bits = y.view(torch.int16)
+    assert not (bits == -32768).any(), "a -0 was stored"
+    assert (y.float() >= 0).all()
+    ref = oracle.add_layernorm_ex(d["x"], d["residual"], d["gamma"], d["beta"], d["eps"], relu=True)[0]
+    assert_close(y, ref, "f16", "relu tiny")
+
+
 def test_add_layernorm_large_mean_rows():
     # mean 1e4, spread 1: the statistics must not lose the variance to cancellation
     announce("add_layernorm mean 1e4 fp32")
