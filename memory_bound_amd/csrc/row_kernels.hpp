@@ -113,184 +113,243 @@ template <class T> struct LnExtra {
     int relu;     // nonzero: y = max(y, 0) (a NaN stays NaN)
 };
 
-template <DT D, bool VECP, int NV, int WPR, bool HAS_RES, bool EX>
-__device__ __forceinline__ void add_layernorm_row(const typename Elem<D>::T* x, const typename Elem<D>::T* res,
-                                                  const typename Elem<D>::T* gamma,
-                                                  const typename Elem<D>::T* beta, typename Elem<D>::T* y,
-                                                  int64_t rows, int hidden, float eps,
-                                                  const LnExtra<typename Elem<D>::T>& ex) {
+// Raw x and r chunks of one row, as loaded.
+template <class S, int NV> struct LnRowIn {
+    typename S::Raw wx[NV], wr[NV];
+};
+
+// Workgroup steps.  With KS = 1 a workgroup owns one block of rows (ROWS_PER_BLOCK rows).  With
+// KS > 1 (launched only when the row fills every chunk of the slice) it walks KS blocks, blockIdx.x + k * gridDim.x for k < KS, keeping DEPTH of them in
+// flight: the loads of block k + DEPTH go out as soon as block k is normalised and stored, and
+// gamma/beta are loaded once for all KS blocks.  Fewer, longer-lived workgroups then spread each
+// CU's reads over the kernel and interleave them with its writes instead of issuing every read at
+// the start; the arithmetic per row is the same, so the results are bit-identical for every KS.
+template <DT D, bool VECP, int NV, int WPR, bool HAS_RES, bool EX, int KS, int DEPTH>
+__device__ __forceinline__ void add_layernorm_rows(const typename Elem<D>::T* x, const typename Elem<D>::T* res,
+                                                   const typename Elem<D>::T* gamma,
+                                                   const typename Elem<D>::T* beta, typename Elem<D>::T* y,
+                                                   int64_t rows, int hidden, float eps,
+                                                   const LnExtra<typename Elem<D>::T>& ex) {
     using S = RowSlice<D, VECP, NV, WPR>;
+    using T = typename S::T;
     constexpr int V = S::V;
+    static_assert(KS >= 1 && DEPTH >= 1 && DEPTH <= KS, "steps and depth");
     // Keep gamma/beta loads in flight with x and r when the slice is small; otherwise load
     // them after the statistics so that the register footprint stays bounded.
     constexpr bool PREFETCH_AFFINE = NV * V <= 64;
+    static_assert(KS == 1 || PREFETCH_AFFINE, "multi-step workgroups hold gamma/beta in registers");
     __shared__ float lds_sum[8], lds_sq[8];
 
     const S s(hidden);
-    const int64_t row = (int64_t)blockIdx.x * RowShape<WPR>::ROWS_PER_BLOCK +
-                        __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / WPR;
-    const uint32_t row_bytes = row < rows ? (uint32_t)hidden * (uint32_t)sizeof(typename S::T) : 0u;
-    const uint32_t par_bytes = (uint32_t)hidden * (uint32_t)sizeof(typename S::T);
-    const rsrc_t rx = make_rsrc(x + row * hidden, row_bytes);
-    const rsrc_t rr = make_rsrc(HAS_RES ? res + row * hidden : x, HAS_RES ? row_bytes : 0u);
-    const rsrc_t ry = make_rsrc(y + row * hidden, row_bytes);
+    const int row_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / WPR;
+    const uint32_t par_bytes = (uint32_t)hidden * (uint32_t)sizeof(T);
     const rsrc_t rg = make_rsrc(gamma, par_bytes);
     const rsrc_t rb = make_rsrc(beta, par_bytes);
-    const rsrc_t rsum = make_rsrc(EX && ex.sum ? ex.sum + row * hidden : y, EX && ex.sum ? row_bytes : 0u);
-
-    // All loads of the row are issued here.  gamma and beta stay raw until the normalisation.
-    // Left alone the compiler sinks their loads below the reductions, which adds a cache round
-    // trip to every row's critical path; a zero-valued data dependency of the row sum on one
-    // word of each of them (masked with hidden >> 31, zero for any valid row length but unknown
-    // at compile time) keeps them in flight together with x and r.
-    typename S::Raw wx[NV], wr[NV], wg[NV], wb[NV];
+    auto row_of = [&](int k) {
+        return ((int64_t)blockIdx.x + (int64_t)k * gridDim.x) * RowShape<WPR>::ROWS_PER_BLOCK + row_in_block;
+    };
+    // x and r of step k; a row past the end gets empty resources (loads return zeros)
+    auto issue = [&](int k, LnRowIn<S, NV>& in) {
+        const int64_t row = row_of(k);
+        const uint32_t row_bytes = row < rows ? par_bytes : 0u;
+        const rsrc_t rx = make_rsrc(x + row * hidden, row_bytes);
+        const rsrc_t rr = make_rsrc(HAS_RES ? res + row * hidden : x, HAS_RES ? row_bytes : 0u);
 #pragma unroll
-    for (int j = 0; j < NV; j++) {
-        wx[j] = s.template load_raw<AUX_STREAM>(rx, j);
-        if constexpr (HAS_RES) wr[j] = s.template load_raw<AUX_STREAM>(rr, j);
-        if constexpr (PREFETCH_AFFINE) {
-            wg[j] = s.load_raw(rg, j);
-            wb[j] = s.load_raw(rb, j);
+        for (int j = 0; j < NV; j++) {
+            in.wx[j] = s.template load_raw<AUX_STREAM>(rx, j);
+            if constexpr (HAS_RES) in.wr[j] = s.template load_raw<AUX_STREAM>(rr, j);
         }
+    };
+
+    // The first DEPTH steps' loads and gamma/beta are issued here; gamma and beta stay raw until
+    // the normalisation.  One step (KS = 1): x and r first, then gamma/beta.  Left alone the
+    // compiler sinks the gamma/beta loads below the reductions, which adds a cache round trip to
+    // the row's critical path; a zero-valued data dependency of the row sum on one word of each
+    // of them (masked with hidden >> 31, zero for any valid row length but unknown at compile
+    // time) keeps them in flight together with x and r.  Several steps: gamma/beta first, as the
+    // oldest loads they return before any row's data, and no dependency is needed.
+    LnRowIn<S, NV> in[DEPTH];
+    typename S::Raw wg[NV], wb[NV];
+    auto issue_affine = [&]() {
+        if constexpr (PREFETCH_AFFINE) {
+#pragma unroll
+            for (int j = 0; j < NV; j++) {
+                wg[j] = s.load_raw(rg, j);
+                wb[j] = s.load_raw(rb, j);
+            }
+        }
+    };
+    if constexpr (KS > 1) {
+        issue_affine();
+        issue(0, in[0]);
+    } else {
+        issue(0, in[0]);
+        issue_affine();
     }
+#pragma unroll
+    for (int d = 1; d < DEPTH; d++) issue(d, in[d]);
     __builtin_amdgcn_sched_barrier(0);  // issue all of the above before anything below
 
     // 1 / hidden, correctly rounded; computed while the loads are in flight
     const float inv_h = 1.0f / (float)hidden;
-    const float one = opaque_one();
-    float v[NV][V], g[NV][V], b[NV][V];
-    float sum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NV; j++) {
-        s.unpack_raw(wx[j], v[j]);
-        if constexpr (HAS_RES) {
-            float rv[V];
-            s.unpack_raw(wr[j], rv);
-#pragma unroll
-            for (int k = 0; k < V; k++) v[j][k] = fmaf(v[j][k], one, rv[k]);  // x + r
-        }
-#pragma unroll
-        for (int k = 0; k < V; k++) sum += v[j][k];  // zeros outside the row
-        if constexpr (EX) s.template store<AUX_STREAM>(rsum, j, v[j]);
-    }
-    if constexpr (PREFETCH_AFFINE) {
-        uint32_t dep = 0;
-#pragma unroll
-        for (int j = 0; j < NV; j++) dep |= S::word0(wg[j]) | S::word0(wb[j]);
-        sum += __builtin_bit_cast(float, dep & (uint32_t)(hidden >> 31));  // adds +0.0f
-    }
-    sum = row_allreduce<WPR>(sum, SumOp{}, lds_sum);
-    // mean = sum / hidden correctly rounded: the product with the correctly rounded reciprocal,
-    // then one correction by the exact remainder (Markstein's division step).  A constant row thus
-    // has its value as mean exactly, whenever its sum is exact.
     const float hf = (float)hidden;
-    const float q0 = sum * inv_h;
-    const float mean = fmaf(fmaf(-q0, hf, sum), inv_h, q0);
+    const float one = opaque_one();
 
-    // deviations d = v - mean, kept for the output; chunks past the end of the row (only when the
-    // row leaves some of the slice's chunks empty) are left out of the second sum with a select
-    float sq = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NV; j++)
+    for (int k = 0; k < KS; k++) {
+        const LnRowIn<S, NV>& cur = in[k % DEPTH];
+        const int64_t row = row_of(k);
+        const uint32_t row_bytes = row < rows ? par_bytes : 0u;
+        const rsrc_t ry = make_rsrc(y + row * hidden, row_bytes);
+        const rsrc_t rsum = make_rsrc(EX && ex.sum ? ex.sum + row * hidden : y, EX && ex.sum ? row_bytes : 0u);
+
+        float v[NV][V], g[NV][V], b[NV][V];
+        float sum = 0.0f;
 #pragma unroll
-        for (int k = 0; k < V; k++) v[j][k] -= mean;
-    if (s.nchunk == NV * WPR * 64) {
+        for (int j = 0; j < NV; j++) {
+            s.unpack_raw(cur.wx[j], v[j]);
+            if constexpr (HAS_RES) {
+                float rv[V];
+                s.unpack_raw(cur.wr[j], rv);
+#pragma unroll
+                for (int q = 0; q < V; q++) v[j][q] = fmaf(v[j][q], one, rv[q]);  // x + r
+            }
+#pragma unroll
+            for (int q = 0; q < V; q++) sum += v[j][q];  // zeros outside the row
+            if constexpr (EX) s.template store<AUX_STREAM>(rsum, j, v[j]);
+        }
+        if constexpr (PREFETCH_AFFINE && KS == 1) {
+            uint32_t dep = 0;
+#pragma unroll
+            for (int j = 0; j < NV; j++) dep |= S::word0(wg[j]) | S::word0(wb[j]);
+            sum += __builtin_bit_cast(float, dep & (uint32_t)(hidden >> 31));  // adds +0.0f
+        }
+        sum = row_allreduce<WPR>(sum, SumOp{}, lds_sum);
+        // mean = sum / hidden correctly rounded: the product with the correctly rounded
+        // reciprocal, then one correction by the exact remainder (Markstein's division step).  A
+        // constant row thus has its value as mean exactly, whenever its sum is exact.
+        const float q0 = sum * inv_h;
+        const float mean = fmaf(fmaf(-q0, hf, sum), inv_h, q0);
+
+        // deviations d = v - mean, kept for the output; chunks past the end of the row (only
+        // when the row leaves some of the slice's chunks empty) are left out of the second sum
+        // with a select
+        float sq = 0.0f;
 #pragma unroll
         for (int j = 0; j < NV; j++)
 #pragma unroll
-            for (int k = 0; k < V; k++) sq = fmaf(v[j][k], v[j][k], sq);
-    } else {
+            for (int q = 0; q < V; q++) v[j][q] -= mean;
+        // (several steps are launched only for rows that fill every chunk: no mask, no branch)
+        if (KS > 1 || s.nchunk == NV * WPR * 64) {
 #pragma unroll
-        for (int j = 0; j < NV; j++) {
-            const bool in_row = s.ok(j);
+            for (int j = 0; j < NV; j++)
 #pragma unroll
-            for (int k = 0; k < V; k++) {
-                const float d = in_row ? v[j][k] : 0.0f;
-                sq = fmaf(d, d, sq);
-            }
-        }
-    }
-    sq = row_allreduce<WPR>(sq, SumOp{}, lds_sq);
-    const float var = sq * inv_h;
-    const float rstd = __builtin_amdgcn_rsqf(var + eps);  // v_rsq_f32, within about 1 ulp
-    if constexpr (EX) {
-        // one lane of the row's first wave writes the statistics
-        const bool leader = (threadIdx.x & 63) == 0 && (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % WPR) == 0;
-        const rsrc_t rm = make_rsrc(ex.mean ? ex.mean + row : (float*)y, ex.mean && row < rows ? 4u : 0u);
-        const rsrc_t rv = make_rsrc(ex.var ? ex.var + row : (float*)y, ex.var && row < rows ? 4u : 0u);
-        bstore_b32(rm, leader ? 0u : OOB, __builtin_bit_cast(uint32_t, mean));
-        bstore_b32(rv, leader ? 0u : OOB, __builtin_bit_cast(uint32_t, var));
-    }
-
-    if constexpr (D == DT::F16 && VECP) {
-        // f16 out: y = round_f16(d * rstd * gamma + beta) from the packed gamma/beta words, one
-        // rounding per element, two instructions per pair
+                for (int q = 0; q < V; q++) sq = fmaf(v[j][q], v[j][q], sq);
+        } else {
 #pragma unroll
-        for (int j = 0; j < NV; j++) {
-            if constexpr (!PREFETCH_AFFINE) {
-                wg[j] = s.load_raw(rg, j);
-                wb[j] = s.load_raw(rb, j);
-            }
-            const uint32_t gw[4] = {wg[j].x, wg[j].y, wg[j].z, wg[j].w};
-            const uint32_t bw[4] = {wb[j].x, wb[j].y, wb[j].z, wb[j].w};
-            uint32_t u[4];
+            for (int j = 0; j < NV; j++) {
+                const bool in_row = s.ok(j);
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                u[i] = fma_mix_f16x2(v[j][2 * i] * rstd, v[j][2 * i + 1] * rstd, gw[i], bw[i]);
-                if constexpr (EX) {
-                    // ReLU on the rounded values: a half with its sign set that is not a NaN
-                    // (a negative number or -0) becomes +0
-                    if (ex.relu) {
-                        const uint32_t lo = u[i] & 0xffffu, hi = u[i] >> 16;
-                        const bool zlo = (lo & 0x8000u) && (lo & 0x7fffu) <= 0x7c00u;
-                        const bool zhi = (hi & 0x8000u) && (hi & 0x7fffu) <= 0x7c00u;
-                        u[i] = (zlo ? 0u : lo) | ((zhi ? 0u : hi) << 16);
-                    }
+                for (int q = 0; q < V; q++) {
+                    const float d = in_row ? v[j][q] : 0.0f;
+                    sq = fmaf(d, d, sq);
                 }
             }
-            s.template store_raw<AUX_STREAM>(ry, j, make_uint4(u[0], u[1], u[2], u[3]));
         }
-    } else {
+        sq = row_allreduce<WPR>(sq, SumOp{}, lds_sq);
+        const float var = sq * inv_h;
+        const float rstd = __builtin_amdgcn_rsqf(var + eps);  // v_rsq_f32, within about 1 ulp
+        if constexpr (EX) {
+            // one lane of the row's first wave writes the statistics
+            const bool leader =
+                (threadIdx.x & 63) == 0 && (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % WPR) == 0;
+            const rsrc_t rm = make_rsrc(ex.mean ? ex.mean + row : (float*)y, ex.mean && row < rows ? 4u : 0u);
+            const rsrc_t rv = make_rsrc(ex.var ? ex.var + row : (float*)y, ex.var && row < rows ? 4u : 0u);
+            bstore_b32(rm, leader ? 0u : OOB, __builtin_bit_cast(uint32_t, mean));
+            bstore_b32(rv, leader ? 0u : OOB, __builtin_bit_cast(uint32_t, var));
+        }
+
+        if constexpr (D == DT::F16 && VECP) {
+            // f16 out: y = round_f16(d * rstd * gamma + beta) from the packed gamma/beta words,
+            // one rounding per element, two instructions per pair
 #pragma unroll
-        for (int j = 0; j < NV; j++) {
-            if constexpr (PREFETCH_AFFINE) {
-                s.unpack_raw(wg[j], g[j]);
-                s.unpack_raw(wb[j], b[j]);
-            } else {
-                s.load(rg, j, g[j]);
-                s.load(rb, j, b[j]);
+            for (int j = 0; j < NV; j++) {
+                if constexpr (!PREFETCH_AFFINE) {
+                    wg[j] = s.load_raw(rg, j);
+                    wb[j] = s.load_raw(rb, j);
+                }
+                const uint32_t gw[4] = {wg[j].x, wg[j].y, wg[j].z, wg[j].w};
+                const uint32_t bw[4] = {wb[j].x, wb[j].y, wb[j].z, wb[j].w};
+                uint32_t u[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    u[i] = fma_mix_f16x2(v[j][2 * i] * rstd, v[j][2 * i + 1] * rstd, gw[i], bw[i]);
+                    if constexpr (EX) {
+                        // ReLU on the rounded values: a half with its sign set that is not a NaN
+                        // (a negative number or -0) becomes +0
+                        if (ex.relu) {
+                            const uint32_t lo = u[i] & 0xffffu, hi = u[i] >> 16;
+                            const bool zlo = (lo & 0x8000u) && (lo & 0x7fffu) <= 0x7c00u;
+                            const bool zhi = (hi & 0x8000u) && (hi & 0x7fffu) <= 0x7c00u;
+                            u[i] = (zlo ? 0u : lo) | ((zhi ? 0u : hi) << 16);
+                        }
+                    }
+                }
+                s.template store_raw<AUX_STREAM>(ry, j, make_uint4(u[0], u[1], u[2], u[3]));
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NV; j++) {
+                if constexpr (PREFETCH_AFFINE) {
+                    s.unpack_raw(wg[j], g[j]);
+                    s.unpack_raw(wb[j], b[j]);
+                } else {
+                    s.load(rg, j, g[j]);
+                    s.load(rb, j, b[j]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NV; j++) {
+                float o[V];
+#pragma unroll
+                for (int q = 0; q < V; q++) o[q] = fmaf(v[j][q] * rstd, g[j][q], b[j][q]);
+                if constexpr (EX) {
+#pragma unroll
+                    for (int q = 0; q < V; q++) o[q] = (ex.relu && o[q] < 0.0f) ? 0.0f : o[q];
+                }
+                s.template store<AUX_STREAM>(ry, j, o);
             }
         }
-#pragma unroll
-        for (int j = 0; j < NV; j++) {
-            float o[V];
-#pragma unroll
-            for (int k = 0; k < V; k++) o[k] = fmaf(v[j][k] * rstd, g[j][k], b[j][k]);
-            if constexpr (EX) {
-#pragma unroll
-                for (int k = 0; k < V; k++) o[k] = (ex.relu && o[k] < 0.0f) ? 0.0f : o[k];
-            }
-            s.template store<AUX_STREAM>(ry, j, o);
-        }
+        // Reuse of the exchange slots needs no extra barrier: every wave reads lds_sum of step k
+        // before it reaches the lds_sq barrier of step k, and reads lds_sq of step k before it
+        // reaches the lds_sum barrier of step k + 1.
+        if (k + DEPTH < KS) issue(k + DEPTH, in[k % DEPTH]);
     }
 }
 
-template <DT D, bool VECP, int NV, int WPR, bool HAS_RES>
+// KS row blocks per workgroup (1, 2 or 4), DEPTH = min(KS, 2) of them in flight.
+// The pointers are declared __restrict__ although y may be x or res itself (in place): a row is
+// stored only after all of its own loads have returned (its stored values depend on them), and
+// different steps touch different rows, so no load can observe a store it should not.  Without
+// it the compiler cannot tell the next rows' loads from this row's stores and waits for the
+// prefetched loads before every store.
+template <DT D, bool VECP, int NV, int WPR, bool HAS_RES, int KS>
 __global__ void __launch_bounds__(RowShape<WPR>::THREADS)
-add_layernorm_kernel(const typename Elem<D>::T* x, const typename Elem<D>::T* res,
-                     const typename Elem<D>::T* gamma, const typename Elem<D>::T* beta,
-                     typename Elem<D>::T* y, int64_t rows, int hidden, float eps) {
-    add_layernorm_row<D, VECP, NV, WPR, HAS_RES, false>(x, res, gamma, beta, y, rows, hidden, eps,
-                                                        LnExtra<typename Elem<D>::T>{nullptr, nullptr, nullptr, 0});
+add_layernorm_kernel(const typename Elem<D>::T* __restrict__ x, const typename Elem<D>::T* __restrict__ res,
+                     const typename Elem<D>::T* __restrict__ gamma, const typename Elem<D>::T* __restrict__ beta,
+                     typename Elem<D>::T* __restrict__ y, int64_t rows, int hidden, float eps) {
+    add_layernorm_rows<D, VECP, NV, WPR, HAS_RES, false, KS, (KS > 1 ? 2 : 1)>(
+        x, res, gamma, beta, y, rows, hidden, eps, LnExtra<typename Elem<D>::T>{nullptr, nullptr, nullptr, 0});
 }
 
-template <DT D, bool VECP, int NV, int WPR, bool HAS_RES>
+template <DT D, bool VECP, int NV, int WPR, bool HAS_RES, int KS>
 __global__ void __launch_bounds__(RowShape<WPR>::THREADS)
 add_layernorm_ex_kernel(const typename Elem<D>::T* x, const typename Elem<D>::T* res,
                         const typename Elem<D>::T* gamma, const typename Elem<D>::T* beta,
                         typename Elem<D>::T* y, int64_t rows, int hidden, float eps,
                         LnExtra<typename Elem<D>::T> ex) {
-    add_layernorm_row<D, VECP, NV, WPR, HAS_RES, true>(x, res, gamma, beta, y, rows, hidden, eps, ex);
+    add_layernorm_rows<D, VECP, NV, WPR, HAS_RES, true, KS, (KS > 1 ? 2 : 1)>(x, res, gamma, beta, y, rows,
+                                                                             hidden, eps, ex);
 }
 
 // ------------------------------------------------------------------------------------------------

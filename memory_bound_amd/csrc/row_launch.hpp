@@ -4,6 +4,7 @@
 
 #include "launch.hpp"
 #include "row_kernels.hpp"
+#include "row_plan.hpp"
 #include "stream_kernels.hpp"
 
 namespace fuse {
@@ -43,6 +44,21 @@ template <class F> bool with_plan(const RowPlan& p, F&& f) {
 
 }  // namespace detail
 
+// Calls run.template operator()<KS>() with the workgroup steps row_steps() picks: 1, 2 or 4 on
+// the 128-bit path with up to 4 chunks per lane when the row fills every chunk of the slice
+// (full), 1 otherwise.
+template <bool VECP, int NV, class R> void with_steps(int64_t blocks, bool full, R&& run) {
+    if constexpr (VECP && NV <= 4) {
+        switch (full ? row_steps(blocks) : 1) {
+            case 2: run.template operator()<2>(); return;
+            case 4: run.template operator()<4>(); return;
+            default: run.template operator()<1>(); return;
+        }
+    } else {
+        run.template operator()<1>();
+    }
+}
+
 template <DT D>
 hipError_t launch_add_layernorm(const void* x, const void* res, const void* gamma, const void* beta,
                                 void* y, int64_t rows, int hidden, float eps, RowPlan plan,
@@ -50,16 +66,20 @@ hipError_t launch_add_layernorm(const void* x, const void* res, const void* gamm
     using T = typename Elem<D>::T;
     hipError_t err = hipErrorInvalidValue;
     auto go = [&]<bool VECP, int NV, int WPR>() {
-        const dim3 grid((unsigned)detail::row_blocks<WPR>(rows)), block(RowShape<WPR>::THREADS);
-        if (res)
-            hipLaunchKernelGGL((add_layernorm_kernel<D, VECP, NV, WPR, true>), grid, block, 0, stream,
-                               (const T*)x, (const T*)res, (const T*)gamma, (const T*)beta, (T*)y,
-                               rows, hidden, eps);
-        else
-            hipLaunchKernelGGL((add_layernorm_kernel<D, VECP, NV, WPR, false>), grid, block, 0, stream,
-                               (const T*)x, (const T*)nullptr, (const T*)gamma, (const T*)beta, (T*)y,
-                               rows, hidden, eps);
-        err = hipGetLastError();
+        const int64_t blocks = detail::row_blocks<WPR>(rows);
+        const bool full = VECP && (int64_t)hidden == (int64_t)NV * WPR * 64 * Elem<D>::VEC;
+        with_steps<VECP, NV>(blocks, full, [&]<int KS>() {
+            const dim3 grid((unsigned)((blocks + KS - 1) / KS)), block(RowShape<WPR>::THREADS);
+            if (res)
+                hipLaunchKernelGGL((add_layernorm_kernel<D, VECP, NV, WPR, true, KS>), grid, block, 0, stream,
+                                   (const T*)x, (const T*)res, (const T*)gamma, (const T*)beta, (T*)y,
+                                   rows, hidden, eps);
+            else
+                hipLaunchKernelGGL((add_layernorm_kernel<D, VECP, NV, WPR, false, KS>), grid, block, 0, stream,
+                                   (const T*)x, (const T*)nullptr, (const T*)gamma, (const T*)beta, (T*)y,
+                                   rows, hidden, eps);
+            err = hipGetLastError();
+        });
     };
     if (!detail::with_plan(plan, go)) return hipErrorInvalidValue;
     return err;
@@ -73,16 +93,20 @@ hipError_t launch_add_layernorm_ex(const void* x, const void* res, const void* g
     hipError_t err = hipErrorInvalidValue;
     const LnExtra<T> ex{(T*)sum, mean, var, relu ? 1 : 0};
     auto go = [&]<bool VECP, int NV, int WPR>() {
-        const dim3 grid((unsigned)detail::row_blocks<WPR>(rows)), block(RowShape<WPR>::THREADS);
-        if (res)
-            hipLaunchKernelGGL((add_layernorm_ex_kernel<D, VECP, NV, WPR, true>), grid, block, 0, stream,
-                               (const T*)x, (const T*)res, (const T*)gamma, (const T*)beta, (T*)y,
-                               rows, hidden, eps, ex);
-        else
-            hipLaunchKernelGGL((add_layernorm_ex_kernel<D, VECP, NV, WPR, false>), grid, block, 0, stream,
-                               (const T*)x, (const T*)nullptr, (const T*)gamma, (const T*)beta, (T*)y,
-                               rows, hidden, eps, ex);
-        err = hipGetLastError();
+        const int64_t blocks = detail::row_blocks<WPR>(rows);
+        const bool full = VECP && (int64_t)hidden == (int64_t)NV * WPR * 64 * Elem<D>::VEC;
+        with_steps<VECP, NV>(blocks, full, [&]<int KS>() {
+            const dim3 grid((unsigned)((blocks + KS - 1) / KS)), block(RowShape<WPR>::THREADS);
+            if (res)
+                hipLaunchKernelGGL((add_layernorm_ex_kernel<D, VECP, NV, WPR, true, KS>), grid, block, 0, stream,
+                                   (const T*)x, (const T*)res, (const T*)gamma, (const T*)beta, (T*)y,
+                                   rows, hidden, eps, ex);
+            else
+                hipLaunchKernelGGL((add_layernorm_ex_kernel<D, VECP, NV, WPR, false, KS>), grid, block, 0, stream,
+                                   (const T*)x, (const T*)nullptr, (const T*)gamma, (const T*)beta, (T*)y,
+                                   rows, hidden, eps, ex);
+            err = hipGetLastError();
+        });
     };
     if (!detail::with_plan(plan, go)) return hipErrorInvalidValue;
     return err;

@@ -18,4 +18,8 @@ struct RowPlan {
 // 128-bit path when the resulting chunks per lane stay within the compiled set.
 RowPlan plan_row(int64_t n, int elem_bytes, bool aligned, int wpr_override);
 
+// Row blocks each workgroup of the LayerNorm kernels walks (1, 2 or 4) for a launch of `blocks`
+// row blocks on the current device.  FUSE_ROW_STEPS = 1, 2 or 4 overrides it (tests, tuning).
+int row_steps(int64_t blocks);
+
 }  // namespace fuse

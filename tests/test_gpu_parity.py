@@ -174,6 +174,35 @@ def test_add_layernorm_ex_inplace_sum_and_nan():
     _check_ln_ex(outs, dd, False, "bf16", "ln_ex no residual", residual=None)
 
 
+@pytest.mark.parametrize("rows,hidden,dtype", [(2048, 4096, "f16"), (2047, 4096, "f16"), (1000, 1024, "bf16"),
+                                               (4096, 2048, "f16"), (513, 1024, "f32"), (3, 4096, "bf16"),
+                                               (130, 4000, "f16"), (777, 256, "f16")])
+def test_add_layernorm_steps_bit_identical(monkeypatch, rows, hidden, dtype):
+    # workgroups that walk 1, 2 or 4 row blocks with the next block's loads in flight run the same
+    # arithmetic per row: every output of every LayerNorm entry point must be bit-identical, for
+    # ragged row counts (steps past the last row); rows that leave chunks of the slice empty
+    # (H = 4000, 256) always take one step, whatever the override
+    announce(f"add_layernorm steps 1/2/4 {rows}x{hidden} {dtype}")
+    d = synth.add_layernorm_inputs(rows, hidden, dtype, seed=47 + rows)
+    g = cuda(d)
+    outs = {}
+    for st in ("1", "2", "4"):
+        monkeypatch.setenv("FUSE_ROW_STEPS", st)
+        y = api.fuse_add_layernorm(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"])
+        yn = api.fuse_add_layernorm(g["x"], None, g["gamma"], g["beta"], d["eps"])
+        ex = api.fuse_add_layernorm_ex(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"], relu=True,
+                                       want_sum=True, want_stats=True)
+        outs[st] = (y, yn) + tuple(ex)
+    for st in ("2", "4"):
+        for a, b in zip(outs["1"], outs[st]):
+            assert torch.equal(a, b), f"steps {st}"
+    monkeypatch.delenv("FUSE_ROW_STEPS")
+    y = api.fuse_add_layernorm(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"])
+    assert torch.equal(y, outs["1"][0])
+    assert_close(y, oracle.add_layernorm(d["x"], d["residual"], d["gamma"], d["beta"], d["eps"]), dtype,
+                 f"steps default {rows}x{hidden}")
+
+
 def test_add_layernorm_relu_f16_tiny_negatives_become_plus_zero():
     # gamma at the smallest f16 subnormal and beta 0: every output lies within one subnormal of
     # zero, and the negative ones round to -0 or -2^-24 before the clamp.  The clamp must store
