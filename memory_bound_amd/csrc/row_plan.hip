@@ -56,8 +56,8 @@ int row_steps(int64_t blocks) {
         if (v == 1 || v == 2 || v == 4) return v;
     }
     // Measured on MI355X (256 CUs), [R, 4096] fp16 Add+LayerNorm: 2048 rows (8 blocks per CU)
-    // fastest with 4 steps (512 workgroups, 9.86 vs 10.4 us), 16384 rows (64 per CU) with 2
-    // (64.0 vs 66.5 us); 4 steps start once they still leave two workgroups per CU, 2 steps
+    // fastest with 4 steps (512 workgroups, 10.0 vs 10.4 us), 16384 rows (64 per CU) with 2
+    // (66.3 vs 68.3 us); 4 steps start once they still leave two workgroups per CU, 2 steps
     // once they leave four.
     const int64_t cus = device_cus();
     if (blocks > 16 * cus) return 2;
