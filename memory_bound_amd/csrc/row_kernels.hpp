@@ -119,9 +119,10 @@ template <class S, int NV> struct LnRowIn {
 };
 
 // Workgroup steps.  With KS = 1 a workgroup owns one block of rows (ROWS_PER_BLOCK rows).  With
-// KS > 1 (launched only when the row fills every chunk of the slice) it walks KS blocks, blockIdx.x + k * gridDim.x for k < KS, keeping DEPTH of them in
-// flight: the loads of block k + DEPTH go out as soon as block k is normalised and stored, and
-// gamma/beta are loaded once for all KS blocks.  Fewer, longer-lived workgroups then spread each
+// KS > 1 (launched only when the row fills every chunk of the slice) it walks KS blocks,
+// blockIdx.x + k * gridDim.x for k < KS, keeping DEPTH of them in flight: the loads of block
+// k + DEPTH go out as soon as block k is normalised and stored, and gamma/beta are loaded once
+// for all KS blocks.  Fewer, longer-lived workgroups then spread each
 // CU's reads over the kernel and interleave them with its writes instead of issuing every read at
 // the start; the arithmetic per row is the same, so the results are bit-identical for every KS.
 template <DT D, bool VECP, int NV, int WPR, bool HAS_RES, bool EX, int KS, int DEPTH>
@@ -328,16 +329,11 @@ __device__ __forceinline__ void add_layernorm_rows(const typename Elem<D>::T* x,
 }
 
 // KS row blocks per workgroup (1, 2 or 4), DEPTH = min(KS, 2) of them in flight.
-// The pointers are declared __restrict__ although y may be x or res itself (in place): a row is
-// stored only after all of its own loads have returned (its stored values depend on them), and
-// different steps touch different rows, so no load can observe a store it should not.  Without
-// it the compiler cannot tell the next rows' loads from this row's stores and waits for the
-// prefetched loads before every store.
 template <DT D, bool VECP, int NV, int WPR, bool HAS_RES, int KS>
 __global__ void __launch_bounds__(RowShape<WPR>::THREADS)
-add_layernorm_kernel(const typename Elem<D>::T* __restrict__ x, const typename Elem<D>::T* __restrict__ res,
-                     const typename Elem<D>::T* __restrict__ gamma, const typename Elem<D>::T* __restrict__ beta,
-                     typename Elem<D>::T* __restrict__ y, int64_t rows, int hidden, float eps) {
+add_layernorm_kernel(const typename Elem<D>::T* x, const typename Elem<D>::T* res,
+                     const typename Elem<D>::T* gamma, const typename Elem<D>::T* beta,
+                     typename Elem<D>::T* y, int64_t rows, int hidden, float eps) {
     add_layernorm_rows<D, VECP, NV, WPR, HAS_RES, false, KS, (KS > 1 ? 2 : 1)>(
         x, res, gamma, beta, y, rows, hidden, eps, LnExtra<typename Elem<D>::T>{nullptr, nullptr, nullptr, 0});
 }
