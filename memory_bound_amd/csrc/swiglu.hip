@@ -386,11 +386,11 @@ swiglu_kernel(DualArgs p) {
 // step kt+1 overwrite.
 // ------------------------------------------------------------------------------------------------
 
-// TM = 256 (the tile) or 128 (half of a tile of the last round, see the kernel).
+// TM = 256 (the tile), 128 or 64 (a half or a quarter of a tile of the last round, see the kernel).
 template <int TM> struct DirectCfgT {
     static constexpr int BKD = 32;
     static constexpr int A_ROW_BYTES = 64, A_CHUNKS = 4;
-    static constexpr int A_BYTES = TM * A_ROW_BYTES;  // 16 or 8 KiB
+    static constexpr int A_BYTES = TM * A_ROW_BYTES;  // 16, 8 or 4 KiB
     static constexpr int B_BYTES = BKD * BN * 2;      // 8 KiB per matrix
     static constexpr int STAGE_BYTES = A_BYTES + 2 * B_BYTES;
     static constexpr int WMT = TM / 64;               // 32-row blocks per wave (wave tile TM/2 x 64)
