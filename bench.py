@@ -137,7 +137,13 @@ def headline(torch, api, synth, roofline, steps, warmup):
         timed_graph = Timed(torch, stream, lambda i: launch(i + warmup), steps)
         warm_graph.run()
         host_s, ev_ms = timed_graph.run()
+        # the same kernel on one buffer set every launch: its 48 MiB stay in the 256 MB Infinity
+        # Cache, so this is a cache figure, reported apart and never as HBM bandwidth
+        hot = Timed(torch, stream, lambda i: launch(0), 200)
+        hot.run()
+        _, hot_ms = hot.run()
     avg_us = ev_ms * 1e3 / steps
+    hot_us = hot_ms * 1e3 / 200
     return {
         "workload": w,
         "bytes": work["bytes"],
@@ -146,6 +152,8 @@ def headline(torch, api, synth, roofline, steps, warmup):
         "value_gbps": work["bytes"] * steps / host_s / 1e9,
         "achieved_gbps": work["bytes"] / (avg_us * 1e-6) / 1e9,
         "sets": len(sets),
+        "hot": {"avg_launch_us": round(hot_us, 3), "gbps": round(work["bytes"] / (hot_us * 1e-6) / 1e9, 1),
+                "note": "same buffers every launch (Infinity Cache resident): not an HBM figure"},
     }
 
 
@@ -727,6 +735,7 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": h["bytes"],
                      "avg_launch_us": round(h["avg_launch_us"], 3)},
         "cpu_baseline": cpu,
+        "headline_hot_cache": h["hot"],
         "rows": rows,
         "launch_study": study,
         "selection_study": selection,
