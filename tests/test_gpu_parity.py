@@ -203,6 +203,28 @@ def test_add_layernorm_steps_bit_identical(monkeypatch, rows, hidden, dtype):
                  f"steps default {rows}x{hidden}")
 
 
+@pytest.mark.parametrize("steps", ["1", "2", "4"])
+def test_add_layernorm_steps_in_place(monkeypatch, steps):
+    # y over x, y over the residual, and the ReLU variant's pre-norm sum over x, on the workload
+    # shape where several row blocks per workgroup are in flight: bit-identical to out of place
+    monkeypatch.setenv("FUSE_ROW_STEPS", steps)
+    announce(f"add_layernorm in place, steps {steps}")
+    d = synth.add_layernorm_inputs(2048, 4096, "f16", seed=53)
+    g = cuda(d)
+    y = api.fuse_add_layernorm(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"])
+    x = g["x"].clone()
+    assert api.fuse_add_layernorm(x, g["residual"], g["gamma"], g["beta"], d["eps"], y=x) is x
+    assert torch.equal(x, y)
+    r = g["residual"].clone()
+    api.fuse_add_layernorm(g["x"], r, g["gamma"], g["beta"], d["eps"], y=r)
+    assert torch.equal(r, y)
+    ref = api.fuse_add_layernorm_ex(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"], relu=True, want_sum=True)
+    x = g["x"].clone()
+    got = api.fuse_add_layernorm_ex(x, g["residual"], g["gamma"], g["beta"], d["eps"], relu=True, sum_out=x)
+    assert got[1] is x
+    assert torch.equal(got[0], ref[0]) and torch.equal(x, ref[1])
+
+
 def test_add_layernorm_relu_f16_tiny_negatives_become_plus_zero():
     # gamma at the smallest f16 subnormal and beta 0: every output lies within one subnormal of
     # zero, and the negative ones round to -0 or -2^-24 before the clamp.  The clamp must store
