@@ -433,70 +433,94 @@ __device__ __forceinline__ float wave_inclusive_scan(float v) {
     return v;
 }
 
-template <DT D, bool VECP, int NV, int WPR>
+// KS row blocks per workgroup (1, 2 or 4; more than 1 only when the row fills every chunk of the
+// slice), blockIdx.x + k * gridDim.x for k < KS, with the raw loads of the next block in flight
+// while a block is scanned and stored -- the workgroup steps of the LayerNorm kernel.  The block
+// totals in LDS alternate between two buffers by step parity: a wave writes step k + 2's totals
+// only after the barrier of step k + 1, which every wave reaches after reading step k's.  The
+// arithmetic per row does not depend on KS, so the results are bit-identical for every KS.
+template <DT D, bool VECP, int NV, int WPR, int KS>
 __global__ void __launch_bounds__(RowShape<WPR>::THREADS)
 cumsum_scale_kernel(const typename Elem<D>::T* x, typename Elem<D>::T* y, int64_t rows, int cols,
                     float scale) {
     using S = RowSlice<D, VECP, NV, WPR>;
     constexpr int V = S::V;
     constexpr int RPB = RowShape<WPR>::ROWS_PER_BLOCK;
-    __shared__ float lds_tot[RPB][NV][WPR];
+    constexpr int DEPTH = KS > 1 ? 2 : 1;
+    static_assert(KS == 1 || KS == 2 || KS == 4, "workgroup steps");
+    __shared__ float lds_tot[KS > 1 ? 2 : 1][RPB][NV][WPR];
 
     const S s(cols);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rib = wave / WPR, wpos = wave % WPR;
-    const int64_t row = (int64_t)blockIdx.x * RPB + rib;
-    const uint32_t row_bytes = row < rows ? (uint32_t)cols * (uint32_t)sizeof(typename S::T) : 0u;
-    const rsrc_t rx = make_rsrc(x + row * cols, row_bytes);
-    const rsrc_t ry = make_rsrc(y + row * cols, row_bytes);
-
-    float v[NV][V];
+    const uint32_t full_bytes = (uint32_t)cols * (uint32_t)sizeof(typename S::T);
+    auto row_of = [&](int k) { return ((int64_t)blockIdx.x + (int64_t)k * gridDim.x) * RPB + rib; };
+    // raw chunks of step k; a row past the end gets an empty resource (loads return zeros)
+    typename S::Raw in[DEPTH][NV];
+    auto issue = [&](int k, typename S::Raw (&w)[NV]) {
+        const int64_t row = row_of(k);
+        const rsrc_t rx = make_rsrc(x + row * cols, row < rows ? full_bytes : 0u);
 #pragma unroll
-    for (int j = 0; j < NV; j++) s.template load<AUX_STREAM>(rx, j, v[j]);  // zeros past the row
-
-    // chunk-local inclusive scans, then the exclusive scan of the chunk totals over the wave
-    float excl[NV], btot[NV];
+        for (int j = 0; j < NV; j++) w[j] = s.template load_raw<AUX_STREAM>(rx, j);
+    };
 #pragma unroll
-    for (int j = 0; j < NV; j++) {
-#pragma unroll
-        for (int k = 1; k < V; k++) v[j][k] += v[j][k - 1];
-        const float inc = wave_inclusive_scan(v[j][V - 1]);
-        excl[j] = dpp_zero<0x138, 0xF>(inc);  // wave_shr:1 -- lane 0 gets 0
-        btot[j] = lane_read(inc, 63);
-    }
+    for (int d = 0; d < DEPTH; d++) issue(d, in[d]);
+    __builtin_amdgcn_sched_barrier(0);  // issue all of the above before anything below
 
-    // offsets of the blocks before this wave's (j, wpos) blocks
-    float pre[NV];
-    if constexpr (WPR == 1) {
-        float off = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KS; k++) {
+        const int64_t row = row_of(k);
+        const rsrc_t ry = make_rsrc(y + row * cols, row < rows ? full_bytes : 0u);
+        float v[NV][V];
+#pragma unroll
+        for (int j = 0; j < NV; j++) s.unpack_raw(in[k % DEPTH][j], v[j]);  // zeros past the row
+
+        // chunk-local inclusive scans, then the exclusive scan of the chunk totals over the wave
+        float excl[NV], btot[NV];
 #pragma unroll
         for (int j = 0; j < NV; j++) {
-            pre[j] = off;
-            off += btot[j];
+#pragma unroll
+            for (int e = 1; e < V; e++) v[j][e] += v[j][e - 1];
+            const float inc = wave_inclusive_scan(v[j][V - 1]);
+            excl[j] = dpp_zero<0x138, 0xF>(inc);  // wave_shr:1 -- lane 0 gets 0
+            btot[j] = lane_read(inc, 63);
         }
-    } else {
-        if ((threadIdx.x & 63) == 0) {
+
+        // offsets of the blocks before this wave's (j, wpos) blocks
+        float pre[NV];
+        if constexpr (WPR == 1) {
+            float off = 0.0f;
 #pragma unroll
-            for (int j = 0; j < NV; j++) lds_tot[rib][j][wpos] = btot[j];
-        }
-        __syncthreads();
-        float off = 0.0f;
-#pragma unroll
-        for (int j = 0; j < NV; j++)
-#pragma unroll
-            for (int w = 0; w < WPR; w++) {
-                if (w == wpos) pre[j] = off;
-                off += lds_tot[rib][j][w];
+            for (int j = 0; j < NV; j++) {
+                pre[j] = off;
+                off += btot[j];
             }
-    }
+        } else {
+            float (&tot)[NV][WPR] = lds_tot[KS > 1 ? (k & 1) : 0][rib];
+            if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+                for (int j = 0; j < NV; j++) tot[j][wpos] = btot[j];
+            }
+            __syncthreads();
+            float off = 0.0f;
+#pragma unroll
+            for (int j = 0; j < NV; j++)
+#pragma unroll
+                for (int w = 0; w < WPR; w++) {
+                    if (w == wpos) pre[j] = off;
+                    off += tot[j][w];
+                }
+        }
 
 #pragma unroll
-    for (int j = 0; j < NV; j++) {
-        const float base = pre[j] + excl[j];
-        float o[V];
+        for (int j = 0; j < NV; j++) {
+            const float base = pre[j] + excl[j];
+            float o[V];
 #pragma unroll
-        for (int k = 0; k < V; k++) o[k] = scale * (base + v[j][k]);
-        s.template store<AUX_STREAM>(ry, j, o);
+            for (int e = 0; e < V; e++) o[e] = scale * (base + v[j][e]);
+            s.template store<AUX_STREAM>(ry, j, o);
+        }
+        if (k + DEPTH < KS) issue(k + DEPTH, in[k % DEPTH]);
     }
 }
 

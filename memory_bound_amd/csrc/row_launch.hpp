@@ -44,12 +44,12 @@ template <class F> bool with_plan(const RowPlan& p, F&& f) {
 
 }  // namespace detail
 
-// Calls run.template operator()<KS>() with the workgroup steps row_steps() picks: 1, 2 or 4 on
-// the 128-bit path with up to 4 chunks per lane when the row fills every chunk of the slice
-// (full), 1 otherwise.
-template <bool VECP, int NV, class R> void with_steps(int64_t blocks, bool full, R&& run) {
+// Calls run.template operator()<KS>() with KS = steps (1, 2 or 4, from row_steps or scan_steps)
+// on the 128-bit path with up to 4 chunks per lane when the row fills every chunk of the slice
+// (full), KS = 1 otherwise.
+template <bool VECP, int NV, class R> void with_steps(int steps, bool full, R&& run) {
     if constexpr (VECP && NV <= 4) {
-        switch (full ? row_steps(blocks) : 1) {
+        switch (full ? steps : 1) {
             case 2: run.template operator()<2>(); return;
             case 4: run.template operator()<4>(); return;
             default: run.template operator()<1>(); return;
@@ -68,7 +68,7 @@ hipError_t launch_add_layernorm(const void* x, const void* res, const void* gamm
     auto go = [&]<bool VECP, int NV, int WPR>() {
         const int64_t blocks = detail::row_blocks<WPR>(rows);
         const bool full = VECP && (int64_t)hidden == (int64_t)NV * WPR * 64 * Elem<D>::VEC;
-        with_steps<VECP, NV>(blocks, full, [&]<int KS>() {
+        with_steps<VECP, NV>(row_steps(blocks), full, [&]<int KS>() {
             const dim3 grid((unsigned)((blocks + KS - 1) / KS)), block(RowShape<WPR>::THREADS);
             if (res)
                 hipLaunchKernelGGL((add_layernorm_kernel<D, VECP, NV, WPR, true, KS>), grid, block, 0, stream,
@@ -95,7 +95,7 @@ hipError_t launch_add_layernorm_ex(const void* x, const void* res, const void* g
     auto go = [&]<bool VECP, int NV, int WPR>() {
         const int64_t blocks = detail::row_blocks<WPR>(rows);
         const bool full = VECP && (int64_t)hidden == (int64_t)NV * WPR * 64 * Elem<D>::VEC;
-        with_steps<VECP, NV>(blocks, full, [&]<int KS>() {
+        with_steps<VECP, NV>(row_steps(blocks), full, [&]<int KS>() {
             const dim3 grid((unsigned)((blocks + KS - 1) / KS)), block(RowShape<WPR>::THREADS);
             if (res)
                 hipLaunchKernelGGL((add_layernorm_ex_kernel<D, VECP, NV, WPR, true, KS>), grid, block, 0, stream,
@@ -133,10 +133,14 @@ hipError_t launch_cumsum_scale(const void* x, void* y, int64_t rows, int cols, f
     using T = typename Elem<D>::T;
     hipError_t err = hipErrorInvalidValue;
     auto go = [&]<bool VECP, int NV, int WPR>() {
-        const dim3 grid((unsigned)detail::row_blocks<WPR>(rows)), block(RowShape<WPR>::THREADS);
-        hipLaunchKernelGGL((cumsum_scale_kernel<D, VECP, NV, WPR>), grid, block, 0, stream,
-                           (const T*)x, (T*)y, rows, cols, scale);
-        err = hipGetLastError();
+        const int64_t blocks = detail::row_blocks<WPR>(rows);
+        const bool full = VECP && (int64_t)cols == (int64_t)NV * WPR * 64 * Elem<D>::VEC;
+        with_steps<VECP, NV>(scan_steps(blocks), full, [&]<int KS>() {
+            const dim3 grid((unsigned)((blocks + KS - 1) / KS)), block(RowShape<WPR>::THREADS);
+            hipLaunchKernelGGL((cumsum_scale_kernel<D, VECP, NV, WPR, KS>), grid, block, 0, stream,
+                               (const T*)x, (T*)y, rows, cols, scale);
+            err = hipGetLastError();
+        });
     };
     if (!detail::with_plan(plan, go)) return hipErrorInvalidValue;
     return err;

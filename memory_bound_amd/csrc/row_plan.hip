@@ -48,13 +48,19 @@ int device_cus() {
     return n;
 }
 
-}  // namespace
-
-int row_steps(int64_t blocks) {
+// FUSE_ROW_STEPS = 1, 2 or 4, else 0.
+int steps_override() {
     if (const char* e = getenv("FUSE_ROW_STEPS")) {
         const int v = atoi(e);
         if (v == 1 || v == 2 || v == 4) return v;
     }
+    return 0;
+}
+
+}  // namespace
+
+int row_steps(int64_t blocks) {
+    if (const int v = steps_override()) return v;
     // Measured on MI355X (256 CUs), [R, 4096] fp16 Add+LayerNorm: 2048 rows (8 blocks per CU)
     // fastest with 4 steps (512 workgroups, 10.0 vs 10.4 us), 16384 rows (64 per CU) with 2
     // (66.3 vs 68.3 us); 4 steps start once they still leave two workgroups per CU, 2 steps
@@ -64,6 +70,15 @@ int row_steps(int64_t blocks) {
     if (blocks >= 8 * cus) return 4;
     if (blocks >= 4 * cus) return 2;
     return 1;
+}
+
+int scan_steps(int64_t blocks) {
+    if (const int v = steps_override()) return v;
+    // Measured on MI355X (256 CUs), [2048, 4096] fp16 cumsum + scale (8 blocks per CU), three
+    // alternating runs each: 2 steps 6.9-7.1 us, 1 step 7.2-7.3 us, 4 steps 7.4 us.  The scan
+    // stores a block's words right after one LDS exchange, so it needs less of the read-ahead
+    // that the LayerNorm's two reductions do; 2 steps once they still leave four workgroups per CU.
+    return blocks >= 8 * device_cus() ? 2 : 1;
 }
 
 }  // namespace fuse

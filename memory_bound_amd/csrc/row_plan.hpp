@@ -22,4 +22,7 @@ RowPlan plan_row(int64_t n, int elem_bytes, bool aligned, int wpr_override);
 // row blocks on the current device.  FUSE_ROW_STEPS = 1, 2 or 4 overrides it (tests, tuning).
 int row_steps(int64_t blocks);
 
+// The same for the cumsum + scale kernel (1 or 2; FUSE_ROW_STEPS overrides it the same way).
+int scan_steps(int64_t blocks);
+
 }  // namespace fuse

@@ -445,6 +445,38 @@ def test_cumsum_exact_counts_every_wpr(monkeypatch, wpr):
         assert torch.equal(y, torch.cumsum(x.double(), dim=1).float()), f"cols={cols} wpr={wpr}"
 
 
+@pytest.mark.parametrize("rows,cols,dtype", [(2048, 4096, "f16"), (2047, 4096, "f16"), (4096, 2048, "bf16"),
+                                             (1000, 1024, "f32"), (3, 4096, "f16"), (130, 4000, "f16")])
+def test_cumsum_steps_bit_identical(monkeypatch, rows, cols, dtype):
+    # workgroups that walk 1, 2 or 4 row blocks (the next block's loads in flight, block totals in
+    # LDS alternating by step parity) run the same arithmetic per row: bit-identical outputs for
+    # ragged row counts (steps past the last row) and in place; rows that leave chunks of the
+    # slice empty (4000 columns) take one step whatever the override.  Integer-valued rows make
+    # every partial sum exact, so a carry taken from the wrong step's totals is an exact mismatch.
+    announce(f"cumsum steps 1/2/4 {rows}x{cols} {dtype}")
+    d = synth.cumsum_inputs(rows, cols, dtype, seed=61 + rows)
+    x = d["x"].cuda()
+    ints = ((torch.arange(rows * cols) * 7 % 9) - 4.0).reshape(rows, cols)
+    ints[rows // 2] = 1.0
+    exact = torch.cumsum(ints.double(), dim=1).to(x.dtype)
+    ints = ints.to(x.dtype).cuda()
+    outs = {}
+    for st in ("1", "2", "4"):
+        monkeypatch.setenv("FUSE_ROW_STEPS", st)
+        outs[st] = api.fuse_cumsum_scale_rows(x, d["scale"])
+        xi = x.clone()
+        assert api.fuse_cumsum_scale_rows(xi, d["scale"], y=xi) is xi
+        assert torch.equal(xi, outs[st]), f"in place, steps {st}"
+        assert torch.equal(api.fuse_cumsum_scale_rows(ints, 1.0).cpu(), exact), f"exact carries, steps {st}"
+    for st in ("2", "4"):
+        assert torch.equal(outs["1"], outs[st]), f"steps {st}"
+    monkeypatch.delenv("FUSE_ROW_STEPS")
+    y = api.fuse_cumsum_scale_rows(x, d["scale"])
+    assert torch.equal(y, outs["1"])
+    assert_close(y, oracle.cumsum_scale_rows(d["x"], np.float32(d["scale"])), KIND[dtype],
+                 f"cumsum steps default {rows}x{cols} {dtype}")
+
+
 def test_cumsum_workload_full_and_inplace():
     w = synth.WORKLOADS["cumsum_f16_2048x4096"]
     announce("cumsum workload 2048x4096 fp16")
