@@ -2,6 +2,9 @@
 
     python -m memory_bound_amd.profsum trace  <results.db>   # dispatch durations
     python -m memory_bound_amd.profsum pmc    <results.db>   # hardware counter values
+    python -m memory_bound_amd.profsum split  <results.db> <kernel> <grid> <n>
+        # one kernel at one grid size: its first n dispatches and the rest, apart (a benchmark
+        # that times the same kernel first on rotating cold buffers, then on one hot buffer set)
 
 rocprofv3's own --stats table groups dispatches by kernel name only; the same kernel
 instantiation runs at several shapes here (the [2048,4096] and [16384,4096] Add+LayerNorm share
@@ -22,19 +25,30 @@ def short_name(name: str) -> str:
     return n.replace("void ", "").replace("fuse::", "").replace("(anonymous namespace)::", "").replace("(DT)", "")
 
 
+def _stats(d: list[float]) -> dict:
+    q = statistics.quantiles(d, n=10, method="inclusive") if len(d) > 1 else [d[0]] * 9
+    return {"calls": len(d), "mean_us": statistics.mean(d), "median_us": statistics.median(d),
+            "p10_us": q[0], "p90_us": q[8], "min_us": min(d), "max_us": max(d)}
+
+
 def trace(db_path: str) -> list[dict]:
     db = sqlite3.connect(db_path)
     rows = db.execute("select name, grid_x, workgroup_x, duration from kernels order by start").fetchall()
     g = defaultdict(list)
     for name, gx, wx, dur in rows:
         g[(short_name(name), gx, wx)].append(dur / 1e3)
-    out = []
-    for (n, gx, wx), d in g.items():
-        q = statistics.quantiles(d, n=10, method="inclusive") if len(d) > 1 else [d[0]] * 9
-        out.append({"kernel": n, "grid": gx, "wg": wx, "calls": len(d), "mean_us": statistics.mean(d),
-                    "median_us": statistics.median(d), "p10_us": q[0], "p90_us": q[8],
-                    "min_us": min(d), "max_us": max(d)})
-    return out
+    return [{"kernel": n, "grid": gx, "wg": wx, **_stats(d)} for (n, gx, wx), d in g.items()]
+
+
+def split(db_path: str, kernel: str, grid: int, first: int) -> tuple[dict, dict | None]:
+    """Durations of `kernel` (its short name) at `grid`, in dispatch order: the first `first`
+    dispatches and the rest."""
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select name, grid_x, duration from kernels order by start").fetchall()
+    d = [dur / 1e3 for name, gx, dur in rows if gx == grid and short_name(name) == kernel]
+    if len(d) < first or first < 1:
+        raise SystemExit(f"{kernel} at grid {grid}: {len(d)} dispatches, fewer than {first}")
+    return _stats(d[:first]), (_stats(d[first:]) if len(d) > first else None)
 
 
 def pmc(db_path: str) -> list[dict]:
@@ -65,6 +79,12 @@ def main(argv):
         for r in pmc(path):
             print(f"{r['kernel'][:64]:64s} {r['grid']:9d} {r['counter']:>11s} {r['calls']:5d} {r['mean']:12.2f} "
                   f"{r['median']:12.2f}")
+    elif mode == "split":
+        head, rest = split(path, argv[3], int(argv[4]), int(argv[5]))
+        for label, r in (("first", head), ("rest", rest)):
+            if r:
+                print(f"{label:5s} calls {r['calls']:5d} mean {r['mean_us']:.3f} median {r['median_us']:.3f} "
+                      f"p10 {r['p10_us']:.3f} p90 {r['p90_us']:.3f} min {r['min_us']:.3f} max {r['max_us']:.3f} us")
     else:
         raise SystemExit(__doc__)
 
