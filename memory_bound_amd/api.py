@@ -126,6 +126,8 @@ def _check(t, name, dtype=None, shape=None):
         return
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}; the kernels run on cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -322,8 +324,11 @@ def fuse_unfused_add_layernorm(x, residual, gamma, beta, eps=1e-5, y=None, works
     rows, hidden = _rows_cols(x)
     _check(x, "x")
     _check(residual, "residual", x.dtype, x.shape)
+    _check(gamma, "gamma", x.dtype, (hidden,))
+    _check(beta, "beta", x.dtype, (hidden,))
     if y is None:
         y = torch.empty_like(x)
+    _check(y, "y", x.dtype, x.shape)
     ws = workspace or _workspace(FUSE_OP_ADD_LAYERNORM, rows, hidden, 0, _dt(x), x.device)
     _ok(load().fuse_unfused_add_layernorm(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y), rows,
                                           hidden, float(eps), _dt(x), ws[1], ws[2], _stream(stream)),
@@ -334,8 +339,11 @@ def fuse_unfused_add_layernorm(x, residual, gamma, beta, eps=1e-5, y=None, works
 def fuse_unfused_bias_gelu_residual(x, bias, residual, y=None, workspace=None, stream=None):
     rows, hidden = _rows_cols(x)
     _check(x, "x")
+    _check(bias, "bias", x.dtype, (hidden,))
+    _check(residual, "residual", x.dtype, x.shape)
     if y is None:
         y = torch.empty_like(x)
+    _check(y, "y", x.dtype, x.shape)
     ws = workspace or _workspace(FUSE_OP_BIAS_GELU_RESIDUAL, rows, hidden, 0, _dt(x), x.device)
     _ok(load().fuse_unfused_bias_gelu_residual(_ptr(x), _ptr(bias), _ptr(residual), _ptr(y), rows, hidden,
                                                _dt(x), ws[1], ws[2], _stream(stream)),
@@ -348,6 +356,7 @@ def fuse_unfused_softmax_rows(x, scale=1.0, y=None, workspace=None, stream=None)
     _check(x, "x")
     if y is None:
         y = torch.empty_like(x)
+    _check(y, "y", x.dtype, x.shape)
     ws = workspace or _workspace(FUSE_OP_SOFTMAX_ROWS, rows, cols, 0, _dt(x), x.device)
     _ok(load().fuse_unfused_softmax_rows(_ptr(x), _ptr(y), rows, cols, float(scale), _dt(x), ws[1], ws[2],
                                          _stream(stream)), "fuse_unfused_softmax_rows")
@@ -359,6 +368,7 @@ def fuse_unfused_cumsum_scale_rows(x, scale=1.0, y=None, workspace=None, stream=
     _check(x, "x")
     if y is None:
         y = torch.empty_like(x)
+    _check(y, "y", x.dtype, x.shape)
     ws = workspace or _workspace(FUSE_OP_CUMSUM_SCALE, rows, cols, 0, _dt(x), x.device)
     _ok(load().fuse_unfused_cumsum_scale_rows(_ptr(x), _ptr(y), rows, cols, float(scale), _dt(x), ws[1], ws[2],
                                               _stream(stream)), "fuse_unfused_cumsum_scale_rows")
@@ -369,8 +379,11 @@ def fuse_unfused_swiglu(a, b1, b2, out=None, workspace=None, stream=None):
     M, K = a.shape
     N = b1.shape[1]
     _check(a, "a")
+    _check(b1, "b1", a.dtype, (K, N))
+    _check(b2, "b2", a.dtype, (K, N))
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    _check(out, "out", a.dtype, (M, N))
     ws = workspace or _workspace(FUSE_OP_SWIGLU, M, N, K, _dt(a), a.device)
     _ok(load().fuse_unfused_swiglu(_ptr(a), _ptr(b1), _ptr(b2), _ptr(out), M, N, K, _dt(a), ws[1], ws[2],
                                    _stream(stream)), "fuse_unfused_swiglu")
@@ -386,8 +399,11 @@ def fuse_unfused_gemm_bias_act(x, w, bias=None, act="relu", y=None, workspace=No
     M, K = x.shape
     N = w.shape[1]
     _check(x, "x")
+    _check(w, "w", x.dtype, (K, N))
+    _check(bias, "bias", x.dtype, (N,))
     if y is None:
         y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _check(y, "y", x.dtype, (M, N))
     ws = workspace or _workspace(FUSE_OP_GEMM_BIAS_ACT, M, N, K, _dt(x), x.device)
     _ok(load().fuse_unfused_gemm_bias_act(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), M, N, K, FUSE_ACT[act], _dt(x),
                                           ws[1], ws[2], _stream(stream)), "fuse_unfused_gemm_bias_act")

@@ -288,3 +288,84 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 64, dtype=torch.float16)
     with pytest.raises(ValueError):
         libfuse.fuse_add_layernorm(x, x, x[0], x[0])
+
+
+class _GpuStandIn:
+    """Looks like a contiguous GPU tensor to the binding's checks; taking its pointer fails the
+    test, so any call that gets past the checks is caught before it reaches the library."""
+    is_cuda = True
+
+    def __init__(self, shape, dtype, index=0):
+        import torch
+        self.shape, self.dtype, self.device = torch.Size(shape), dtype, torch.device("cuda", index)
+
+    def is_contiguous(self):
+        return True
+
+    def dim(self):
+        return len(self.shape)
+
+    def numel(self):
+        n = 1
+        for d in self.shape:
+            n *= d
+        return n
+
+    def element_size(self):
+        return 4 if str(self.dtype) == "torch.float32" else 2
+
+    def data_ptr(self):
+        raise AssertionError("a pointer was taken before every operand was checked")
+
+
+def _binding_cases():
+    import torch
+    h, b, f = torch.float16, torch.bfloat16, torch.float32
+    R, H, M, N, K = 4, 64, 32, 48, 16
+    row = dict(x=((R, H), h), y=((R, H), h))
+    ln = dict(x=((R, H), h), residual=((R, H), h), gamma=((H,), h), beta=((H,), h), y=((R, H), h))
+    gelu = dict(x=((R, H), h), bias=((H,), h), residual=((R, H), h), y=((R, H), h))
+    sw = dict(a=((M, K), b), b1=((K, N), b), b2=((K, N), b), out=((M, N), b))
+    gm = dict(x=((M, K), b), w=((K, N), b), bias=((N,), b), y=((M, N), b))
+    return [
+        ("fuse_add_layernorm", ln, {}),
+        ("fuse_add_layernorm_ex", dict(ln, sum_out=((R, H), h), mean_out=((R,), f), var_out=((R,), f)), {}),
+        ("fuse_bias_gelu_residual", gelu, {}),
+        ("fuse_softmax_rows", row, {}),
+        ("fuse_cumsum_scale_rows", row, {}),
+        ("fuse_swiglu_dualgemm", sw, {}),
+        ("fuse_swiglu_auto", sw, {"workspace": (None, None, 0)}),
+        ("fuse_gemm_bias_act", gm, {}),
+        ("fuse_gemm_bias_act_auto", gm, {"workspace": (None, None, 0)}),
+        ("fuse_unfused_add_layernorm", ln, {"workspace": (None, None, 0)}),
+        ("fuse_unfused_bias_gelu_residual", gelu, {"workspace": (None, None, 0)}),
+        ("fuse_unfused_softmax_rows", row, {"workspace": (None, None, 0)}),
+        ("fuse_unfused_cumsum_scale_rows", row, {"workspace": (None, None, 0)}),
+        ("fuse_unfused_swiglu", sw, {"workspace": (None, None, 0)}),
+        ("fuse_unfused_gemm_bias_act", gm, {"workspace": (None, None, 0)}),
+        ("fuse_copy", dict(src=((R, H), h), dst=((R, H), h)), {}),
+    ]
+
+
+@pytest.mark.parametrize("case", _binding_cases(), ids=lambda c: c[0])
+def test_python_binding_checks_every_operand(monkeypatch, case):
+    # one operand at a time is a CPU tensor, or a GPU tensor on another device than the current
+    # one: the wrapper must raise before taking any pointer, whichever operand it is
+    import torch
+    from memory_bound_amd import api as libfuse
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 0)
+    monkeypatch.setattr(libfuse, "load", lambda: pytest.fail("the library was called"))
+    name, ops, extra = case
+    fn = getattr(libfuse, name)
+    for bad in ops:
+        for kind in ("cpu", "other device"):
+            args = {}
+            for k, (shape, dt) in ops.items():
+                if k != bad:
+                    args[k] = _GpuStandIn(shape, dt)
+                elif kind == "cpu":
+                    args[k] = torch.zeros(shape, dtype=dt)
+                else:
+                    args[k] = _GpuStandIn(shape, dt, index=1)
+            with pytest.raises(ValueError):
+                fn(**args, **extra)
