@@ -731,6 +731,83 @@ def test_unfused_gemm_bias_act(act):
     _loose(y, oracle.gemm_bias_act_unfused(d["x"], d["w"], None, act, "bf16"), "bf16", f"unfused gemm {act} no bias")
 
 
+# ------------------------------------------------------------------------------------------------
+# Captured graphs: the benchmark times every kernel as launches captured in a HIP graph over
+# rotating buffer sets
+# ------------------------------------------------------------------------------------------------
+
+def _graph_op(op, seed):
+    """(inputs on the GPU, launch(inputs, outs) -> outs, fresh outputs) for one fused operation."""
+    if op in ("add_layernorm", "add_layernorm_ex"):
+        rows = 2048 if op == "add_layernorm" else 512
+        d = cuda(synth.add_layernorm_inputs(rows, 4096, "f16", seed))
+        if op == "add_layernorm":
+            run = lambda d, o: (api.fuse_add_layernorm(d["x"], d["residual"], d["gamma"], d["beta"], d["eps"],
+                                                       y=o[0]),)
+        else:
+            run = lambda d, o: api.fuse_add_layernorm_ex(d["x"], d["residual"], d["gamma"], d["beta"], d["eps"],
+                                                         relu=True, want_sum=True, want_stats=True, y=o[0],
+                                                         sum_out=o[1], mean_out=o[2], var_out=o[3])
+    elif op == "bias_gelu_residual":
+        d = cuda(synth.bias_gelu_residual_inputs(512, 4096, "f16", seed))
+        run = lambda d, o: (api.fuse_bias_gelu_residual(d["x"], d["bias"], d["residual"], y=o[0]),)
+    elif op == "softmax":
+        d = cuda(synth.softmax_inputs(1024, 2048, "f16", seed))
+        run = lambda d, o: (api.fuse_softmax_rows(d["x"], d["scale"], y=o[0]),)
+    elif op == "cumsum":
+        d = cuda(synth.cumsum_inputs(2048, 4096, "f16", seed))
+        run = lambda d, o: (api.fuse_cumsum_scale_rows(d["x"], d["scale"], y=o[0]),)
+    elif op in ("swiglu", "swiglu_auto"):
+        M, N, K = (512, 768, 256) if op == "swiglu" else (256, 256, 1536)
+        d = cuda(synth.swiglu_inputs(M, N, K, "bf16", seed))
+        if op == "swiglu":
+            run = lambda d, o: (api.fuse_swiglu_dualgemm(d["a"], d["b1"], d["b2"], out=o[0]),)
+        else:
+            d["ws"] = api._auto_workspace(api.FUSE_OP_SWIGLU, M, N, K, d["a"].device)
+            assert api.fuse_auto_splits(api.FUSE_OP_SWIGLU, M, N, K) > 1
+            run = lambda d, o: (api.fuse_swiglu_auto(d["a"], d["b1"], d["b2"], out=o[0], workspace=d["ws"]),)
+    else:  # GEMM + bias + ReLU
+        d = cuda(synth.gemm_inputs(512, 1024, 256, "bf16", seed))
+        run = lambda d, o: (api.fuse_gemm_bias_act(d["x"], d["w"], d["bias"], "relu", y=o[0]),)
+    return d, run
+
+
+@pytest.mark.parametrize("op", ["add_layernorm", "add_layernorm_ex", "bias_gelu_residual", "softmax", "cumsum",
+                                "swiglu", "swiglu_auto", "gemm_relu"])
+def test_fused_ops_in_a_replayed_graph(op):
+    # three launches on three buffer sets captured in one graph, replayed three times with eager
+    # work and cleared outputs in between: every replay equals the eager launches bit for bit
+    announce(f"graph replay {op}")
+    sets, eager = [], []
+    for seed in (3, 4, 5):
+        d, run = _graph_op(op, seed)
+        sets.append(d)
+        e = run(d, (None, None, None, None))
+        eager.append(tuple(t for t in e if t is not None))
+    outs = [tuple(torch.empty_like(t) for t in e) for e in eager]
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for d, o in zip(sets, outs):
+            run(d, o + (None,) * (4 - len(o)))
+    for rep in range(3):
+        for o in outs:
+            for t in o:
+                t.zero_()
+        run(sets[0], (None, None, None, None))  # eager work between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (e, o) in enumerate(zip(eager, outs)):
+            for a, b in zip(e, o):
+                assert torch.equal(a, b), f"{op}: replay {rep}, buffer set {i}"
+    if op == "add_layernorm":
+        d = synth.add_layernorm_inputs(2048, 4096, "f16", 3)
+        assert_close(outs[0][0], oracle.add_layernorm(d["x"], d["residual"], d["gamma"], d["beta"], d["eps"]),
+                     "f16", "graph replay add_layernorm")
+
+
 def test_copy_kernel():
     announce("copy")
     src = torch.randint(0, 255, ((1 << 20) + 7,), dtype=torch.uint8, device="cuda")
