@@ -248,11 +248,12 @@ __device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, u32x2 v) {
 // Stores the tile at (m0, n0) (64 WMT rows).  Block (i, j) element r of lane l sits at row
 // 8 (r/4) + 4 (l/32) + r%4, column l%32 of the block; the wave's blocks start at row 32 WMT wm,
 // column 64 wn of each product's 128-column tile.  Rows past M and columns past N fall outside
-// the store resources.  QUAD (whole tiles, N a multiple of the tile width; the product-store and
-// GEMM epilogues): each group of four rows goes out through quad_rows_bf16 as one 8-byte store
-// per lane instead of four 2-byte ones.  Measured per dispatch at 2048x8960x1536: GEMM + bias +
-// ReLU 70.6 -> 69.3 us; the SwiGLU epilogue, whose SiLU already keeps the vector ALU busy, lost
-// about 1 us with it and keeps the element stores.
+// the store resources.  QUAD (whole tiles, N a multiple of the tile width): each group of four
+// rows goes out through quad_rows_bf16 as one 8-byte store per lane instead of four 2-byte ones.
+// Measured at 2048x8960x1536: GEMM + bias + ReLU 70.6 -> 69.3 us per synchronised dispatch;
+// SwiGLU about 1 us slower per synchronised dispatch but 2.5 us faster (138.5 -> 136.3 and 135.1
+// -> 132.1 us, faster in 7 of 8 interleaved pairs) over the back-to-back launches of the
+// benchmark, where the clock sits at the power limit.
 template <int MODE, int WMT = WM, bool QUAD = false>
 __device__ __forceinline__ void store_tile(const DualArgs& p, const floatx16 (&acc1)[WMT][WN],
                                            const floatx16 (&acc2)[WMT][WN], int m0, int n0, int wm, int wn,
@@ -262,8 +263,8 @@ __device__ __forceinline__ void store_tile(const DualArgs& p, const floatx16 (&a
     const uint32_t out_bytes = (uint32_t)mrows * (uint32_t)p.N * 2u;
     // QUAD: lane l stores row 8 b + 4 (l/32) + l%4 of block (i, j), columns 4 ((l%32)/4) .. +3
     const int qrow = 4 * (lane >> 5) + (lane & 3), qcol = 4 * ((lane & 31) >> 2);
-    if constexpr (QUAD && MODE == MODE_PRODUCTS) {
-        constexpr bool PROD = true;
+    if constexpr (QUAD && (MODE == MODE_PRODUCTS || MODE == MODE_SWIGLU)) {
+        constexpr bool PROD = MODE == MODE_PRODUCTS;
         const rsrc_t ro = make_rsrc((PROD ? p.c1 : p.out) + (int64_t)m0 * p.N, out_bytes);
         const rsrc_t ro2 = make_rsrc(PROD ? p.c2 + (int64_t)m0 * p.N : p.out, PROD ? out_bytes : 0u);
 #pragma unroll

@@ -529,6 +529,21 @@ def test_swiglu_full_tile_paths(monkeypatch, env):
             assert_close(out, oracle.swiglu(d["a"], d["b1"], d["b2"]), "bf16", f"swiglu N={N} K={K} {env}")
 
 
+def test_swiglu_full_tile_stores_match_general_kernel(monkeypatch):
+    # the full-tile kernel stores each 4 x 4 quad of lanes as four 8-byte rows, the general kernel
+    # one element per lane; both sum the same 16-deep k slices in ascending order, so every output
+    # must be bit-identical, and a value stored at the wrong row or column cannot hide
+    announce("swiglu full-tile quad stores vs general kernel")
+    for M, N, K in ((512, 384, 320), (256, 640, 96), (512, 8960 // 35 * 3, 1536)):
+        d = synth.swiglu_inputs(M, N, K, "bf16", seed=5 + N)
+        a, b1, b2 = d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda()
+        direct = api.fuse_swiglu_dualgemm(a, b1, b2)
+        monkeypatch.setenv("FUSE_SWIGLU_GENERAL", "1")
+        general = api.fuse_swiglu_dualgemm(a, b1, b2)
+        monkeypatch.delenv("FUSE_SWIGLU_GENERAL")
+        assert torch.equal(direct, general), f"{M}x{N}x{K}"
+
+
 def test_swiglu_last_round_slices(monkeypatch):
     # 5 x 53 = 265 tiles on 256 CUs: the last 9 tiles run as 64-row quarters by default, as 128-row
     # halves with FUSE_SWIGLU_TAIL=2, whole with =0.  Same k order per element every way, so the
