@@ -2,6 +2,8 @@
 
     python -m memory_bound_amd.profsum trace  <results.db>   # dispatch durations
     python -m memory_bound_amd.profsum pmc    <results.db>   # hardware counter values
+    python -m memory_bound_amd.profsum dispatches <results.db> <kernel>
+        # one kernel, per dispatch: duration (a --kernel-trace run) and every counter collected
     python -m memory_bound_amd.profsum split  <results.db> <kernel> <grid> <n>
         # one kernel at one grid size: its first n dispatches and the rest, apart (a benchmark
         # that times the same kernel first on rotating cold buffers, then on one hot buffer set)
@@ -51,6 +53,18 @@ def split(db_path: str, kernel: str, grid: int, first: int) -> tuple[dict, dict 
     return _stats(d[:first]), (_stats(d[first:]) if len(d) > first else None)
 
 
+def dispatches(db_path: str, kernel: str) -> list[dict]:
+    """Per dispatch of `kernel` (its short name), in order: duration in us and counter values."""
+    db = sqlite3.connect(db_path)
+    dur = {d: t / 1e3 for n, d, t in db.execute("select name, dispatch_id, duration from kernels")
+           if short_name(n) == kernel}
+    out = defaultdict(dict)
+    for n, d, c, v in db.execute("select kernel_name, dispatch_id, counter_name, value from counters_collection"):
+        if short_name(n) == kernel:
+            out[d][c] = v
+    return [{"dispatch": d, "us": dur.get(d), **out[d]} for d in sorted(set(dur) | set(out))]
+
+
 def pmc(db_path: str) -> list[dict]:
     db = sqlite3.connect(db_path)
     rows = db.execute("select kernel_name, grid_size, workgroup_size, counter_name, value "
@@ -79,6 +93,13 @@ def main(argv):
         for r in pmc(path):
             print(f"{r['kernel'][:64]:64s} {r['grid']:9d} {r['counter']:>11s} {r['calls']:5d} {r['mean']:12.2f} "
                   f"{r['median']:12.2f}")
+    elif mode == "dispatches":
+        rows = dispatches(path, argv[3])
+        names = sorted({k for r in rows for k in r} - {"dispatch", "us"})
+        print(f"{'dispatch':>9s} {'us':>9s} " + " ".join(f"{n:>26s}" for n in names))
+        for r in rows:
+            us = f"{r['us']:9.3f}" if r["us"] is not None else f"{'-':>9s}"
+            print(f"{r['dispatch']:9d} {us} " + " ".join(f"{r.get(n, float('nan')):26.0f}" for n in names))
     elif mode == "split":
         head, rest = split(path, argv[3], int(argv[4]), int(argv[5]))
         for label, r in (("first", head), ("rest", rest)):
