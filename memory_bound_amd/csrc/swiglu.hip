@@ -636,9 +636,8 @@ __device__ __forceinline__ void direct_tile(const DualArgs& p, char* lds, int m0
 #pragma unroll
             for (int r = 0; r < 16; r++) acc1[i][j][r] = acc2[i][j][r] = 0.0f;
 
-    // Prologue: stages 0 .. S-2.  Every step issues the loads of one stage; past the last K step
-    // they reload the last stage into a buffer nobody reads again, which keeps the vmcnt
-    // bookkeeping the same on every step.
+    // Prologue: stages 0 .. S-2.  With fewer K steps than that, the missing stages reload the last
+    // one into a buffer nobody reads, which keeps the prologue's vmcnt count fixed.
 #pragma unroll
     for (int s = 0; s < S - 1; s++) {
         const uint32_t base = lds_addr(lds + s * C::STAGE_BYTES);
@@ -659,16 +658,27 @@ __device__ __forceinline__ void direct_tile(const DualArgs& p, char* lds, int m0
                         b_frag_half(lds + C::A_BYTES + C::B_BYTES, 64 * wn + 32 * j, 0, lane, 1));
     }
 
-    for (int kt = 0; kt < kt_n; kt++) {
+    // Steps that load stage kt + S - 1, then the last S - 1 steps, which load nothing and wait for
+    // every load still in flight (the stage they need next is the newest one).
+    int kt = 0;
+    for (; kt + S - 1 < kt_n; kt++) {
         const char* st = lds + (kt % S) * C::STAGE_BYTES;
         const char* sn = lds + ((kt + 1) % S) * C::STAGE_BYTES;
         const uint32_t nbase = lds_addr(lds + ((kt + S - 1) % S) * C::STAGE_BYTES);
-        const int nk0 = (kt0 + min(kt + S - 1, kt_n - 1)) * C::BKD;
+        const int nk0 = (kt0 + kt + S - 1) * C::BKD;
         slice_step<TM>(f0, f1, st, 1, acc1, acc2, 0, LPS / 2, a, b1, b2, N, K, m0, n0, nk0, nbase, wm, wn, wave,
                        lane);
         slice_step<TM>(f1, f0, sn, 0, acc1, acc2, LPS / 2, LPS - LPS / 2, a, b1, b2, N, K, m0, n0, nk0, nbase, wm, wn, wave,
                        lane);
         wait_vmcnt<LPS * (S - 3)>();
+        __syncthreads();
+    }
+    for (; kt < kt_n; kt++) {
+        const char* st = lds + (kt % S) * C::STAGE_BYTES;
+        const char* sn = lds + ((kt + 1) % S) * C::STAGE_BYTES;
+        slice_step<TM>(f0, f1, st, 1, acc1, acc2, 0, 0, a, b1, b2, N, K, m0, n0, 0, 0, wm, wn, wave, lane);
+        slice_step<TM>(f1, f0, sn, 0, acc1, acc2, 0, 0, a, b1, b2, N, K, m0, n0, 0, 0, wm, wn, wave, lane);
+        wait_vmcnt<0>();
         __syncthreads();
     }
     wait_vmcnt<0>();  // no load may still be writing this workgroup's LDS when it ends
