@@ -569,6 +569,25 @@ def test_swiglu_last_round_slices(monkeypatch):
     assert_close(y1[rows.cuda()], oracle.gemm_bias_act(d["x"][rows], d["w"], d["bias"], "gelu"), "bf16", "gemm quarters")
 
 
+@pytest.mark.parametrize("M,N", [(2048, 8960), (2048, 5248)])
+def test_swiglu_tail_slices_at_full_grids(monkeypatch, M, N):
+    # 560 tiles on 256 CUs leave 48 for a last round run as 64-row quarters (the workload's tile
+    # grid), 328 tiles leave 72 run as 128-row halves.  The k order per element is the same every
+    # way: bit-identical to whole tiles and to halves, and checked against the oracle on sampled
+    # rows.
+    K = 256
+    announce(f"swiglu {M}x{N}x{K} tail slices")
+    d = synth.swiglu_inputs(M, N, K, "bf16", seed=N)
+    a, b1, b2 = d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda()
+    out = api.fuse_swiglu_dualgemm(a, b1, b2)
+    for tail in ("2", "0"):
+        monkeypatch.setenv("FUSE_SWIGLU_TAIL", tail)
+        assert torch.equal(out, api.fuse_swiglu_dualgemm(a, b1, b2)), f"tail {tail}"
+    monkeypatch.delenv("FUSE_SWIGLU_TAIL")
+    rows = torch.arange(3, M, 29)
+    assert_close(out[rows.cuda()], oracle.swiglu(d["a"][rows], d["b1"], d["b2"]), "bf16", f"swiglu {M}x{N} tail")
+
+
 @pytest.mark.parametrize("stages", [None, "3", "5"])
 def test_swiglu_workload_sampled_rows(monkeypatch, stages):
     # the default ring depth and the shallowest and deepest rings at the full size
