@@ -30,7 +30,19 @@
  *    each element is read before it is written by the same lane).  Any other overlap between
  *    an output and an input returns FUSE_ERR_ALIAS.
  *  - Sizes.  rows == 0 (or M == 0) is a valid no-op.  Negative sizes are FUSE_ERR_BAD_SHAPE.
- *  - Thread safety.  The library keeps no state besides a per-thread last-error code.
+ *  - Thread safety.  The library keeps no state besides a per-thread last-error code and a
+ *    per-device cache of the compute-unit count (read once with hipDeviceGetAttribute).
+ *  - Tuning overrides.  Launch plans are chosen per shape and device; these environment
+ *    variables, read at every call, override them for measurement and tests and never change
+ *    what is computed.  FUSE_ROW_STEPS, FUSE_EW_CHUNKS, FUSE_SWIGLU_STAGES, FUSE_SWIGLU_TAIL and
+ *    FUSE_SWIGLU_GENERAL leave every result bit-identical; FUSE_ROW_WPR and FUSE_SPLITK change
+ *    the order of the sums, within the same tolerance:
+ *    FUSE_ROW_WPR (waves per row: 1, 2, 4, 8), FUSE_ROW_STEPS (row blocks per workgroup: 1, 2,
+ *    4), FUSE_EW_CHUNKS (16-byte chunks per thread of the streaming kernels: 1, 2, 4, 8),
+ *    FUSE_SWIGLU_STAGES (LDS ring depth of the dual-product kernels: 3, 4, 5),
+ *    FUSE_SWIGLU_TAIL (last-round slices: 0 off, 2 halves only), FUSE_SWIGLU_GENERAL (any
+ *    value: the general dual-product kernel for every shape), FUSE_SPLITK (K splits of the
+ *    per-shape plan; 1 = never split).
  */
 #ifndef LIBFUSE_H
 #define LIBFUSE_H
