@@ -532,7 +532,8 @@ def test_swiglu_full_tile_paths(monkeypatch, env):
 def test_swiglu_full_tile_stores_match_general_kernel(monkeypatch):
     # the full-tile kernel stores each 4 x 4 quad of lanes as four 8-byte rows, the general kernel
     # one element per lane; both sum the same 16-deep k slices in ascending order, so every output
-    # must be bit-identical, and a value stored at the wrong row or column cannot hide
+    # (SwiGLU, and GEMM + bias + activation) must be bit-identical, and a value stored at the
+    # wrong row or column cannot hide
     announce("swiglu full-tile quad stores vs general kernel")
     for M, N, K in ((512, 384, 320), (256, 640, 96), (512, 8960 // 35 * 3, 1536)):
         d = synth.swiglu_inputs(M, N, K, "bf16", seed=5 + N)
@@ -542,6 +543,15 @@ def test_swiglu_full_tile_stores_match_general_kernel(monkeypatch):
         general = api.fuse_swiglu_dualgemm(a, b1, b2)
         monkeypatch.delenv("FUSE_SWIGLU_GENERAL")
         assert torch.equal(direct, general), f"{M}x{N}x{K}"
+    # the GEMM epilogue (bias, activation) on the same two kernels
+    d = synth.gemm_inputs(512, 768, 320, "bf16", seed=7)
+    x, w, bias = d["x"].cuda(), d["w"].cuda(), d["bias"].cuda()
+    for act in ("none", "relu", "gelu", "silu"):
+        direct = api.fuse_gemm_bias_act(x, w, bias, act)
+        monkeypatch.setenv("FUSE_SWIGLU_GENERAL", "1")
+        general = api.fuse_gemm_bias_act(x, w, bias, act)
+        monkeypatch.delenv("FUSE_SWIGLU_GENERAL")
+        assert torch.equal(direct, general), f"gemm {act}"
 
 
 def test_swiglu_last_round_slices(monkeypatch):
