@@ -49,6 +49,46 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_header_is_c99_and_every_symbol_links(tmp_path, lib):
+    # a plain C program (no C++, no HIP headers) compiled against the header with -pedantic and
+    # linked against the library: it takes the address of every declared entry point and makes
+    # calls that validation answers or that are documented no-ops, so nothing is launched
+    import shutil
+    import subprocess
+    from memory_bound_amd import api as libfuse
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    names = declared_functions()
+    src = "\n".join([
+        "#include <stdio.h>", "#include <string.h>", '#include "libfuse.h"',
+        "typedef void (*fn_t)(void);",
+        "static const fn_t every_entry_point[] = {" + ", ".join(f"(fn_t){n}" for n in names) + "};",
+        "int main(void) {",
+        "    int bad = 0;",
+        "    if (sizeof every_entry_point / sizeof every_entry_point[0] != %d) bad |= 1;" % len(names),
+        '    if (strstr(fuse_version(), "gfx950") == NULL) bad |= 2;',
+        "    if (fuse_add_layernorm(NULL, NULL, NULL, NULL, NULL, 4, 64, 1e-5f, FUSE_F16, NULL)",
+        "        != FUSE_ERR_NULL_PTR) bad |= 4;",
+        "    if (fuse_add_layernorm(NULL, NULL, NULL, NULL, NULL, 0, 64, 1e-5f, FUSE_F16, NULL) != FUSE_OK) bad |= 8;",
+        "    if (fuse_softmax_rows(NULL, NULL, 4, 0, 1.0f, FUSE_F16, NULL) != FUSE_ERR_BAD_SHAPE) bad |= 16;",
+        "    if (fuse_swiglu_dualgemm(NULL, NULL, NULL, NULL, 64, 64, 64, FUSE_F16, NULL) != FUSE_ERR_BAD_DTYPE)",
+        "        bad |= 32;",
+        '    if (strncmp(fuse_status_string(FUSE_ERR_ALIAS), "FUSE_ERR_ALIAS", 14) != 0) bad |= 64;',
+        '    printf("bad=%d\\n", bad);',
+        "    return bad;",
+        "}", ""])
+    (tmp_path / "abi.c").write_text(src)
+    libdir = os.path.dirname(libfuse.LIB_PATH)
+    cmd = [cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.dirname(HEADER),
+           str(tmp_path / "abi.c"), "-L", libdir, "-lfuse", f"-Wl,-rpath,{libdir}",
+           "-Wl,-rpath-link,/opt/rocm/lib", "-o", str(tmp_path / "abi")]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    assert p.returncode == 0, p.stderr
+    r = subprocess.run([str(tmp_path / "abi")], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
 def test_status_strings_and_version(lib):
     for code in range(10):
         s = lib.fuse_status_string(code).decode()
