@@ -130,3 +130,17 @@ def test_oracle_thread_count_round_trip():
     finally:
         oracle.set_threads(n)
     assert oracle.threads() == n
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the path is single-GPU: asking the benchmark for N > 1 GPUs ends with a message and a
+    # non-zero status before anything touches a device
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for n in ("2", "8"):
+        p = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", n], capture_output=True,
+                           text=True, timeout=120)
+        assert p.returncode == 2, p.stderr
+        assert "one GPU only" in p.stderr and not p.stdout.strip()
