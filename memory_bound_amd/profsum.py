@@ -4,6 +4,9 @@
     python -m memory_bound_amd.profsum pmc    <results.db>   # hardware counter values
     python -m memory_bound_amd.profsum dispatches <results.db> <kernel>
         # one kernel, per dispatch: duration (a --kernel-trace run) and every counter collected
+    python -m memory_bound_amd.profsum hbm    <fetch.db> <write.db>
+        # bytes moved per dispatch from a FETCH_SIZE run and a WRITE_SIZE run of the same
+        # program, each counter scaled by what it reads for the plain copy of 24 MiB in that run
     python -m memory_bound_amd.profsum split  <results.db> <kernel> <grid> <n>
         # one kernel at one grid size: its first n dispatches and the rest, apart (a benchmark
         # that times the same kernel first on rotating cold buffers, then on one hot buffer set)
@@ -65,6 +68,33 @@ def dispatches(db_path: str, kernel: str) -> list[dict]:
     return [{"dispatch": d, "us": dur.get(d), **out[d]} for d in sorted(set(dur) | set(out))]
 
 
+COPY_KERNEL, COPY_BYTES = "copy16_kernel<4>", 24 << 20  # the calibration copy: 24 MiB read, 24 MiB written
+
+
+def hbm(fetch_db: str, write_db: str) -> tuple[float, float, list[dict]]:
+    """Per kernel and grid: mean FETCH_SIZE and WRITE_SIZE (KiB) and the bytes they stand for.
+    Each counter is scaled by the bytes the calibration copy in the same run moves over what the
+    counter reads for it."""
+    mean = {}
+    for db, cname in ((fetch_db, "FETCH_SIZE"), (write_db, "WRITE_SIZE")):
+        for r in pmc(db):
+            if r["counter"] == cname:
+                mean[(r["kernel"], r["grid"], cname)] = r["mean"]
+    copy = [k for k in mean if k[0] == COPY_KERNEL and k[1] == COPY_BYTES // 64]
+    if len(copy) != 2:
+        raise SystemExit("the runs hold no 24 MiB calibration copy")
+    fs = COPY_BYTES / 1024 / mean[(COPY_KERNEL, COPY_BYTES // 64, "FETCH_SIZE")]
+    ws = COPY_BYTES / 1024 / mean[(COPY_KERNEL, COPY_BYTES // 64, "WRITE_SIZE")]
+    out = []
+    for (k, g) in sorted({(k, g) for k, g, _ in mean}, key=lambda t: (t[0], t[1])):
+        f, w = mean.get((k, g, "FETCH_SIZE")), mean.get((k, g, "WRITE_SIZE"))
+        if f is None or w is None:
+            continue
+        out.append({"kernel": k, "grid": g, "fetch_kib": f, "write_kib": w,
+                    "bytes": f * 1024 * fs + w * 1024 * ws})
+    return fs, ws, out
+
+
 def pmc(db_path: str) -> list[dict]:
     db = sqlite3.connect(db_path)
     rows = db.execute("select kernel_name, grid_size, workgroup_size, counter_name, value "
@@ -100,6 +130,13 @@ def main(argv):
         for r in rows:
             us = f"{r['us']:9.3f}" if r["us"] is not None else f"{'-':>9s}"
             print(f"{r['dispatch']:9d} {us} " + " ".join(f"{r.get(n, float('nan')):26.0f}" for n in names))
+    elif mode == "hbm":
+        fs, ws, rows = hbm(path, argv[3])
+        print(f"# fetch_scale {fs:.5f}  write_scale {ws:.5f}  (24 MiB copy in the same runs)")
+        print(f"{'kernel':64s} {'grid':>9s} {'fetch_KiB':>11s} {'write_KiB':>11s} {'bytes':>12s}")
+        for r in rows:
+            print(f"{r['kernel'][:64]:64s} {r['grid']:9d} {r['fetch_kib']:11.2f} {r['write_kib']:11.2f} "
+                  f"{r['bytes']:12.0f}")
     elif mode == "split":
         head, rest = split(path, argv[3], int(argv[4]), int(argv[5]))
         for label, r in (("first", head), ("rest", rest)):

@@ -144,3 +144,29 @@ def test_bench_refuses_more_than_one_gpu():
                            text=True, timeout=120)
         assert p.returncode == 2, p.stderr
         assert "one GPU only" in p.stderr and not p.stdout.strip()
+
+
+def test_profile_summary_scales_counters_by_the_calibration_copy(tmp_path):
+    # FETCH_SIZE and WRITE_SIZE of a kernel become bytes through the ratio the 24 MiB copy of the
+    # same run gives: here the copy reads back half its bytes on FETCH_SIZE and all on WRITE_SIZE
+    import sqlite3
+    from memory_bound_amd import profsum
+    dbs = []
+    for cname, copy_kib, k_kib in (("FETCH_SIZE", 12288.0, 1000.0), ("WRITE_SIZE", 24576.0, 2000.0)):
+        path = str(tmp_path / f"{cname}.db")
+        db = sqlite3.connect(path)
+        db.execute("create table counters_collection (dispatch_id, kernel_name, grid_size, workgroup_size, "
+                   "counter_name, value)")
+        rows = [(1, "void fuse::copy16_kernel<4>(uint4 const*, uint4*, unsigned long)", 393216, 256, cname, copy_kib),
+                (2, "void fuse::k<1, true>(float const*)", 100, 256, cname, k_kib),
+                (3, "void fuse::k<1, true>(float const*)", 100, 256, cname, k_kib + 2.0)]
+        db.executemany("insert into counters_collection values (?, ?, ?, ?, ?, ?)", rows)
+        db.commit()
+        dbs.append(path)
+    fs, ws, out = profsum.hbm(*dbs)
+    assert fs == 2.0 and ws == 1.0
+    k = [r for r in out if r["kernel"] == "k<1, true>"][0]
+    assert k["fetch_kib"] == 1001.0 and k["write_kib"] == 2001.0
+    assert k["bytes"] == 1001.0 * 1024 * 2 + 2001.0 * 1024
+    c = [r for r in out if r["kernel"] == "copy16_kernel<4>"][0]
+    assert c["bytes"] == 2 * (24 << 20)
