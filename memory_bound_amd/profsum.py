@@ -4,6 +4,10 @@
     python -m memory_bound_amd.profsum pmc    <results.db>   # hardware counter values
     python -m memory_bound_amd.profsum dispatches <results.db> <kernel>
         # one kernel, per dispatch: duration (a --kernel-trace run) and every counter collected
+    python -m memory_bound_amd.profsum clock  <results.db> <kernel> <flop>
+        # per dispatch of a --kernel-trace run with SQ_CYCLES and SQ_VALU_MFMA_BUSY_CYCLES: shader
+        # clock, matrix-core busy fraction, achieved TFLOP/s for `flop` per dispatch, bf16 peak at
+        # that clock (MI355X: 32 shader engines, 1024 SIMDs, 1024 bf16 flop per SIMD per cycle)
     python -m memory_bound_amd.profsum hbm    <fetch.db> <write.db>
         # bytes moved per dispatch from a FETCH_SIZE run and a WRITE_SIZE run of the same
         # program, each counter scaled by what it reads for the plain copy of 24 MiB in that run
@@ -68,6 +72,22 @@ def dispatches(db_path: str, kernel: str) -> list[dict]:
     return [{"dispatch": d, "us": dur.get(d), **out[d]} for d in sorted(set(dur) | set(out))]
 
 
+SHADER_ENGINES, SIMDS, BF16_FLOP_PER_SIMD_CYCLE = 32, 1024, 1024
+
+
+def clock(db_path: str, kernel: str, flop: float) -> list[dict]:
+    """Per dispatch: duration, clock (SQ_CYCLES per engine over the duration), MFMA busy fraction
+    (busy cycles per SIMD over cycles per engine), achieved TFLOP/s and the peak at that clock."""
+    out = []
+    for r in dispatches(db_path, kernel):
+        eng = r["SQ_CYCLES"] / SHADER_ENGINES
+        mhz = eng / r["us"]
+        out.append({"us": r["us"], "mhz": mhz, "mfma_busy": r["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS / eng,
+                    "tflops": flop / (r["us"] * 1e-6) / 1e12,
+                    "peak_tflops": SIMDS * BF16_FLOP_PER_SIMD_CYCLE * mhz * 1e6 / 1e12})
+    return out
+
+
 COPY_KERNEL, COPY_BYTES = "copy16_kernel<4>", 24 << 20  # the calibration copy: 24 MiB read, 24 MiB written
 
 
@@ -130,6 +150,15 @@ def main(argv):
         for r in rows:
             us = f"{r['us']:9.3f}" if r["us"] is not None else f"{'-':>9s}"
             print(f"{r['dispatch']:9d} {us} " + " ".join(f"{r.get(n, float('nan')):26.0f}" for n in names))
+    elif mode == "clock":
+        rows = clock(path, argv[3], float(argv[4]))
+        print("dispatch       us    MHz mfma_busy  TFLOP/s peak_at_clock")
+        for i, r in enumerate(rows, 1):
+            print(f"{i:8d} {r['us']:8.1f} {r['mhz']:6.0f} {r['mfma_busy']:9.3f} {r['tflops']:8.0f} "
+                  f"{r['peak_tflops']:13.0f}")
+        med = {k: statistics.median(r[k] for r in rows) for k in rows[0]}
+        print(f"  median {med['us']:8.1f} {med['mhz']:6.0f} {med['mfma_busy']:9.3f} {med['tflops']:8.0f} "
+              f"{med['peak_tflops']:13.0f}")
     elif mode == "hbm":
         fs, ws, rows = hbm(path, argv[3])
         print(f"# fetch_scale {fs:.5f}  write_scale {ws:.5f}  (24 MiB copy in the same runs)")

@@ -170,3 +170,23 @@ def test_profile_summary_scales_counters_by_the_calibration_copy(tmp_path):
     assert k["bytes"] == 1001.0 * 1024 * 2 + 2001.0 * 1024
     c = [r for r in out if r["kernel"] == "copy16_kernel<4>"][0]
     assert c["bytes"] == 2 * (24 << 20)
+
+
+def test_profile_summary_clock_and_matrix_core_busy(tmp_path):
+    # one dispatch of 1 us with 2000 cycles per shader engine runs at 2000 MHz; busy cycles of
+    # half the SIMD-cycles give a busy fraction of 0.5; 1 GFLOP in 1 us is 1000 TFLOP/s
+    import sqlite3
+    from memory_bound_amd import profsum
+    path = str(tmp_path / "clk.db")
+    db = sqlite3.connect(path)
+    db.execute("create table kernels (name, dispatch_id, duration)")
+    db.execute("create table counters_collection (kernel_name, dispatch_id, counter_name, value)")
+    name = "void fuse::k<4, 0>(fuse::DualArgs)"
+    db.execute("insert into kernels values (?, 7, 1000)", (name,))
+    db.executemany("insert into counters_collection values (?, 7, ?, ?)",
+                   [(name, "SQ_CYCLES", 32 * 2000.0), (name, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 1000.0)])
+    db.commit()
+    (r,) = profsum.clock(path, "k<4, 0>", 1e9)
+    assert r["us"] == 1.0 and r["mhz"] == 2000.0 and r["mfma_busy"] == 0.5
+    assert abs(r["tflops"] - 1000.0) < 1e-9
+    assert abs(r["peak_tflops"] - 1024 * 1024 * 2e9 / 1e12) < 1e-9
