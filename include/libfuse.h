@@ -34,15 +34,16 @@
  *    per-device cache of the compute-unit count (read once with hipDeviceGetAttribute).
  *  - Tuning overrides.  Launch plans are chosen per shape and device; these environment
  *    variables, read at every call, override them for measurement and tests and never change
- *    what is computed.  FUSE_ROW_STEPS, FUSE_EW_CHUNKS, FUSE_SWIGLU_STAGES and FUSE_SWIGLU_TAIL
- *    leave every result bit-identical, and so does FUSE_SWIGLU_GENERAL for fuse_swiglu_dualgemm
+ *    what is computed.  FUSE_ROW_STEPS, FUSE_EW_CHUNKS, FUSE_SWIGLU_STAGES, FUSE_SWIGLU_TAIL and
+ *    FUSE_SWIGLU_PERSIST leave every result bit-identical, and so does FUSE_SWIGLU_GENERAL for fuse_swiglu_dualgemm
  *    and fuse_gemm_bias_act; FUSE_ROW_WPR, FUSE_SPLITK and FUSE_SWIGLU_GENERAL on the *_auto
  *    entry points (it turns the split-K plan off) change the order of the sums, within the same
  *    tolerance:
  *    FUSE_ROW_WPR (waves per row: 1, 2, 4, 8), FUSE_ROW_STEPS (row blocks per workgroup: 1, 2,
  *    4), FUSE_EW_CHUNKS (16-byte chunks per thread of the streaming kernels: 1, 2, 4, 8),
  *    FUSE_SWIGLU_STAGES (LDS ring depth of the dual-product kernels: 3, 4, 5),
- *    FUSE_SWIGLU_TAIL (last-round slices: 0 off, 2 halves only), FUSE_SWIGLU_GENERAL (any
+ *    FUSE_SWIGLU_TAIL (last-round slices: 0 off, 2 halves only), FUSE_SWIGLU_PERSIST (0: one
+ *    workgroup per tile instead of one per CU walking its tiles), FUSE_SWIGLU_GENERAL (any
  *    value: the general dual-product kernel for every shape), FUSE_SPLITK (K splits of the
  *    per-shape plan; 1 = never split).
  */

@@ -209,6 +209,8 @@ struct DualArgs {
     float* part;           // split K: [splits][planes][M][N] fp32 partial products
     int tail;              // full-tile kernel: the last `tail` tiles run as `parts` row slices each
     int parts;             // 2 (128-row halves) or 4 (64-row quarters)
+    int units;             // full-tile kernel: work units (whole tiles, then last-round slices; or
+                           // tiles x splits), walked by workgroup b as b, b + grid, b + 2 grid, ...
 };
 
 template <int ACT> __device__ __forceinline__ float activation(float t) {
@@ -686,11 +688,13 @@ __device__ __forceinline__ void direct_tile(const DualArgs& p, char* lds, int m0
     store_tile<MODE, WMT, true>(p, acc1, acc2, m0, n0, wm, wn, lane, split);
 }
 
-// Workgroup roles.  Split K (p.tail = 0): workgroup (split, tile) = (bid / tiles, bid % tiles)
-// covers K steps [split * ksteps, split * ksteps + ksteps) of its tile.  Otherwise the first
-// tiles - tail workgroups take a whole tile each, and the last parts * tail workgroups take the
-// remaining tiles as 128-row halves or 64-row quarters: when the tiles leave a last round that
-// fills few CUs, that round is spread over more of them.
+// Work units.  Split K (p.tail = 0): unit (split, tile) = (bid / tiles, bid % tiles) covers K
+// steps [split * ksteps, split * ksteps + ksteps) of its tile.  Otherwise the first tiles - tail
+// units are a whole tile each, and the last parts * tail units the remaining tiles as 128-row
+// halves or 64-row quarters: when the tiles leave a last round that fills few CUs, that round is
+// spread over more of them.  Workgroup b takes units b, b + grid, ...: one unit each when the grid
+// covers them all, otherwise (a grid of one workgroup per CU, rounded down to a multiple of 8)
+// every unit of its CU in turn, so unit u still runs on XCD u % 8, the one the tile map assumes.
 template <int S, int MODE>
 __global__ void __launch_bounds__(THREADS, 1)
 swiglu_direct_kernel(DualArgs p) {
@@ -698,8 +702,9 @@ swiglu_direct_kernel(DualArgs p) {
     __shared__ __attribute__((aligned(1024))) char lds[S * DirectCfg::STAGE_BYTES];
     const int ntiles = p.tiles_m * p.tiles_n;
     const int kt_all = p.K / DirectCfg::BKD;
-    const int bid = blockIdx.x;
     const int head = ntiles - p.tail;
+    for (int bid = blockIdx.x; bid < p.units; bid += gridDim.x) {
+    if (bid > (int)blockIdx.x) __syncthreads();  // the previous unit's last LDS reads are done
     if (p.tail == 0 || bid < head) {
         const int split = bid / ntiles;
         const Tile tile = tile_of(bid - split * ntiles, p.tiles_m, p.tiles_n, p.bn_step);
@@ -713,6 +718,7 @@ swiglu_direct_kernel(DualArgs p) {
         const int q = bid - head;
         const Tile tile = tile_of(head + (q >> 2), p.tiles_m, p.tiles_n, p.bn_step);
         direct_tile<BM / 4, S, MODE>(p, lds, tile.m0 + (BM / 4) * (q & 3), tile.n0, 0, kt_all, 0);
+    }
     }
 }
 
@@ -772,6 +778,16 @@ int direct_stages(int M, int N, int K, bool aligned, int tile_cols) {
     return (st >= 3 && st <= 5) ? st : 4;
 }
 
+// One resident workgroup per CU walking the work units (b, b + grid, ...) instead of one
+// workgroup per unit: no workgroup ends and launches between a CU's tiles.  Measured per
+// synchronised dispatch at 2048x8960x1536: SwiGLU 113.2-114.4 -> 111.5-113.3 us median (mean
+// 115.4-118.2 -> 112.3-113.0), GEMM + bias + ReLU 70.8-71.0 -> 70.4-70.6 us.  Results are
+// bit-identical.  FUSE_SWIGLU_PERSIST=0 launches one workgroup per unit, for measurement.
+bool persistent() {
+    const char* e = getenv("FUSE_SWIGLU_PERSIST");
+    return !(e && atoi(e) == 0);
+}
+
 // Tiles of the last round that the full-tile kernel runs in row slices, and how many slices:
 // when the tiles take two or more rounds over the CUs and the last round fills at most half of
 // them, its tiles run as halves, or as quarters when even those fill at most a quarter (560
@@ -807,7 +823,12 @@ hipError_t launch(DualArgs p, int tile_cols, hipStream_t stream) {
     const TailPlan tp = st != 0 ? tail_plan(p.tiles_m * p.tiles_n) : TailPlan{0, 0};
     p.tail = tp.tail;
     p.parts = tp.parts;
-    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n + (tp.parts - 1) * tp.tail)), block(THREADS);
+    p.units = p.tiles_m * p.tiles_n + (tp.parts - 1) * tp.tail;
+    dim3 grid((unsigned)p.units), block(THREADS);
+    if (st != 0 && persistent()) {
+        const int cus = cu_count(), g = cus >= NUM_XCD ? cus / NUM_XCD * NUM_XCD : cus;
+        grid = dim3((unsigned)min(p.units, g));
+    }
     if (st == 3) hipLaunchKernelGGL((swiglu_direct_kernel<3, MODE>), grid, block, 0, stream, p);
     else if (st == 4) hipLaunchKernelGGL((swiglu_direct_kernel<4, MODE>), grid, block, 0, stream, p);
     else if (st == 5) hipLaunchKernelGGL((swiglu_direct_kernel<5, MODE>), grid, block, 0, stream, p);
@@ -875,7 +896,8 @@ hipError_t launch_split(DualArgs p, int tile_cols, const SplitPlan& sp, float* p
     p.ksteps = sp.ksteps;
     p.part = part;
     const int st = direct_stages(p.M, p.N, p.K, true, tile_cols);
-    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n * sp.splits)), block(THREADS);
+    p.units = p.tiles_m * p.tiles_n * sp.splits;
+    const dim3 grid((unsigned)p.units), block(THREADS);
     if (st == 3) hipLaunchKernelGGL((swiglu_direct_kernel<3, PMODE>), grid, block, 0, stream, p);
     else if (st == 5) hipLaunchKernelGGL((swiglu_direct_kernel<5, PMODE>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((swiglu_direct_kernel<4, PMODE>), grid, block, 0, stream, p);

@@ -582,8 +582,9 @@ def test_swiglu_last_round_slices(monkeypatch):
 @pytest.mark.parametrize("M,N", [(2048, 8960), (2048, 5248)])
 def test_swiglu_tail_slices_at_full_grids(monkeypatch, M, N):
     # 560 tiles on 256 CUs leave 48 for a last round run as 64-row quarters (the workload's tile
-    # grid), 328 tiles leave 72 run as 128-row halves.  The k order per element is the same every
-    # way: bit-identical to whole tiles and to halves, and checked against the oracle on sampled
+    # grid), 328 tiles leave 72 run as 128-row halves; by default one resident workgroup per CU
+    # walks its units.  The k order per element is the same every way: bit-identical to whole
+    # tiles, to halves and to one workgroup per unit, and checked against the oracle on sampled
     # rows.
     K = 256
     announce(f"swiglu {M}x{N}x{K} tail slices")
@@ -594,6 +595,10 @@ def test_swiglu_tail_slices_at_full_grids(monkeypatch, M, N):
         monkeypatch.setenv("FUSE_SWIGLU_TAIL", tail)
         assert torch.equal(out, api.fuse_swiglu_dualgemm(a, b1, b2)), f"tail {tail}"
     monkeypatch.delenv("FUSE_SWIGLU_TAIL")
+    # one workgroup per unit instead of one resident workgroup per CU walking its units
+    monkeypatch.setenv("FUSE_SWIGLU_PERSIST", "0")
+    assert torch.equal(out, api.fuse_swiglu_dualgemm(a, b1, b2)), "one workgroup per unit"
+    monkeypatch.delenv("FUSE_SWIGLU_PERSIST")
     rows = torch.arange(3, M, 29)
     assert_close(out[rows.cuda()], oracle.swiglu(d["a"][rows], d["b1"], d["b2"]), "bf16", f"swiglu {M}x{N} tail")
 
