@@ -352,7 +352,7 @@ add_layernorm_ex_kernel(const typename Elem<D>::T* x, const typename Elem<D>::T*
 // Row softmax of scaled scores.  z = scale * x; m = max z; e = 2^((z - m) log2 e); y = e / sum e
 // (as e times the correctly rounded reciprocal of the sum).
 // ------------------------------------------------------------------------------------------------
-template <DT D, bool VECP, int NV, int WPR>
+template <DT D, bool VECP, int NV, int WPR, bool FULL>
 __global__ void __launch_bounds__(RowShape<WPR>::THREADS)
 softmax_rows_kernel(const typename Elem<D>::T* x, typename Elem<D>::T* y, int64_t rows, int cols,
                     float scale) {
@@ -371,25 +371,36 @@ softmax_rows_kernel(const typename Elem<D>::T* x, typename Elem<D>::T* y, int64_
 #pragma unroll
     for (int j = 0; j < NV; j++) s.template load<AUX_STREAM>(rx, j, z[j]);
 
-    float m = -__builtin_inff();
+    // e_j = exp(s x_j - max_k s x_k) = 2^(c x_j - m) with c = s log2(e) and m = |c| max_k (sign(c) x_k),
+    // which is c times the largest scaled value whatever the sign of s: one FMA per element.
+    // Chunks past the row hold zeros and take no part in the max or the sum (FULL: there are none).
+    const float c = scale * LOG2E;
+    float mx = -__builtin_inff();
+    if (c >= 0.0f) {
 #pragma unroll
-    for (int j = 0; j < NV; j++) {
-        const bool in_row = s.ok(j);
+        for (int j = 0; j < NV; j++) {
+            const bool in_row = FULL || s.ok(j);
 #pragma unroll
-        for (int k = 0; k < V; k++) {
-            z[j][k] *= scale;
-            m = fmaxf(m, in_row ? z[j][k] : -__builtin_inff());
+            for (int k = 0; k < V; k++) mx = fmaxf(mx, in_row ? z[j][k] : -__builtin_inff());
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NV; j++) {
+            const bool in_row = FULL || s.ok(j);
+#pragma unroll
+            for (int k = 0; k < V; k++) mx = fmaxf(mx, in_row ? -z[j][k] : -__builtin_inff());
         }
     }
-    m = row_allreduce<WPR>(m, MaxOp{}, lds_max);
+    mx = row_allreduce<WPR>(mx, MaxOp{}, lds_max);
+    const float m = fabsf(c) * mx;
 
     float sum = 0.0f;
 #pragma unroll
     for (int j = 0; j < NV; j++) {
-        const bool in_row = s.ok(j);
+        const bool in_row = FULL || s.ok(j);
 #pragma unroll
         for (int k = 0; k < V; k++) {
-            z[j][k] = exp2_fast((z[j][k] - m) * LOG2E);
+            z[j][k] = __builtin_amdgcn_exp2f(fmaf(z[j][k], c, -m));
             sum += in_row ? z[j][k] : 0.0f;
         }
     }

@@ -119,8 +119,14 @@ hipError_t launch_softmax_rows(const void* x, void* y, int64_t rows, int cols, f
     hipError_t err = hipErrorInvalidValue;
     auto go = [&]<bool VECP, int NV, int WPR>() {
         const dim3 grid((unsigned)detail::row_blocks<WPR>(rows)), block(RowShape<WPR>::THREADS);
-        hipLaunchKernelGGL((softmax_rows_kernel<D, VECP, NV, WPR>), grid, block, 0, stream,
-                           (const T*)x, (T*)y, rows, cols, scale);
+        // rows that fill every chunk of the slice need no masking of empty chunks
+        const bool full = VECP && (int64_t)cols == (int64_t)NV * WPR * 64 * Elem<D>::VEC;
+        if (full)
+            hipLaunchKernelGGL((softmax_rows_kernel<D, VECP, NV, WPR, true>), grid, block, 0, stream,
+                               (const T*)x, (T*)y, rows, cols, scale);
+        else
+            hipLaunchKernelGGL((softmax_rows_kernel<D, VECP, NV, WPR, false>), grid, block, 0, stream,
+                               (const T*)x, (T*)y, rows, cols, scale);
         err = hipGetLastError();
     };
     if (!detail::with_plan(plan, go)) return hipErrorInvalidValue;

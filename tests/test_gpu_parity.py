@@ -366,6 +366,9 @@ def test_bias_gelu_residual_inplace_and_deterministic():
     (3, 1, "f16", 1.0),                      # one column: exactly 1
     (6, 333, "f32", -0.7),                   # negative scale
     (12, 4096, "f16", 1 / math.sqrt(128)),
+    (64, 2048, "f16", -1 / math.sqrt(128)),  # negative scale on full rows (max of -x)
+    (33, 1024, "bf16", -0.3),
+    (16, 2048, "f16", 0.0),                  # scale 0: every row uniform, 1/cols
 ])
 def test_softmax_parity(rows, cols, dtype, scale):
     announce(f"softmax {rows}x{cols} {dtype} scale={scale}")
