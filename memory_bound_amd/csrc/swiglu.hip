@@ -253,9 +253,9 @@ __device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, u32x2 v) {
 // the store resources.  QUAD (whole tiles, N a multiple of the tile width): each group of four
 // rows goes out through quad_rows_bf16 as one 8-byte store per lane instead of four 2-byte ones.
 // Measured at 2048x8960x1536: GEMM + bias + ReLU 70.6 -> 69.3 us per synchronised dispatch;
-// SwiGLU about 1 us slower per synchronised dispatch but 2.5 us faster (138.5 -> 136.3 and 135.1
-// -> 132.1 us, faster in 7 of 8 interleaved pairs) over the back-to-back launches of the
-// benchmark, where the clock sits at the power limit.
+// SwiGLU 112.4 -> 110.2 us per synchronised dispatch and about 2.5 us faster over the back-to-back
+// launches of the benchmark (faster in 7 of 8 interleaved pairs), where the clock sits at the
+// power limit.
 template <int MODE, int WMT = WM, bool QUAD = false>
 __device__ __forceinline__ void store_tile(const DualArgs& p, const floatx16 (&acc1)[WMT][WN],
                                            const floatx16 (&acc2)[WMT][WN], int m0, int n0, int wm, int wn,
@@ -704,21 +704,21 @@ swiglu_direct_kernel(DualArgs p) {
     const int kt_all = p.K / DirectCfg::BKD;
     const int head = ntiles - p.tail;
     for (int bid = blockIdx.x; bid < p.units; bid += gridDim.x) {
-    if (bid > (int)blockIdx.x) __syncthreads();  // the previous unit's last LDS reads are done
-    if (p.tail == 0 || bid < head) {
-        const int split = bid / ntiles;
-        const Tile tile = tile_of(bid - split * ntiles, p.tiles_m, p.tiles_n, p.bn_step);
-        const int kt0 = split * p.ksteps;
-        direct_tile<BM, S, MODE>(p, lds, tile.m0, tile.n0, kt0, min(p.ksteps, kt_all - kt0), split);
-    } else if (p.parts == 2) {
-        const int q = bid - head;
-        const Tile tile = tile_of(head + (q >> 1), p.tiles_m, p.tiles_n, p.bn_step);
-        direct_tile<BM / 2, S, MODE>(p, lds, tile.m0 + (BM / 2) * (q & 1), tile.n0, 0, kt_all, 0);
-    } else {
-        const int q = bid - head;
-        const Tile tile = tile_of(head + (q >> 2), p.tiles_m, p.tiles_n, p.bn_step);
-        direct_tile<BM / 4, S, MODE>(p, lds, tile.m0 + (BM / 4) * (q & 3), tile.n0, 0, kt_all, 0);
-    }
+        if (bid > (int)blockIdx.x) __syncthreads();  // the previous unit's last LDS reads are done
+        if (p.tail == 0 || bid < head) {
+            const int split = bid / ntiles;
+            const Tile tile = tile_of(bid - split * ntiles, p.tiles_m, p.tiles_n, p.bn_step);
+            const int kt0 = split * p.ksteps;
+            direct_tile<BM, S, MODE>(p, lds, tile.m0, tile.n0, kt0, min(p.ksteps, kt_all - kt0), split);
+        } else if (p.parts == 2) {
+            const int q = bid - head;
+            const Tile tile = tile_of(head + (q >> 1), p.tiles_m, p.tiles_n, p.bn_step);
+            direct_tile<BM / 2, S, MODE>(p, lds, tile.m0 + (BM / 2) * (q & 1), tile.n0, 0, kt_all, 0);
+        } else {
+            const int q = bid - head;
+            const Tile tile = tile_of(head + (q >> 2), p.tiles_m, p.tiles_n, p.bn_step);
+            direct_tile<BM / 4, S, MODE>(p, lds, tile.m0 + (BM / 4) * (q & 3), tile.n0, 0, kt_all, 0);
+        }
     }
 }
 
