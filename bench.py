@@ -23,6 +23,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -90,6 +91,24 @@ class Timed:
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         return t1 - t0, e0.elapsed_time(e1)
+
+
+def single_dispatch_us(torch, stream, launch, n=10, spin_cycles=2_000_000):
+    """Median duration of n dispatches timed one at a time, each after a device synchronisation.
+    A spin kernel (about 1 ms) keeps the stream busy while the start event, the dispatch and the
+    end event are enqueued, so the host's enqueue time is not part of what is timed."""
+    ts = []
+    for i in range(n):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(spin_cycles)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launch(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    return statistics.median(ts)
 
 
 def rotation_sets(torch, tensors: dict, outputs: dict, min_bytes: int):
@@ -162,6 +181,14 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
     out = {}
     stream = torch.cuda.Stream()
     peak_bw = roofline.HBM_PEAK_GBPS
+
+    def single_dispatch(us, work):
+        # the matrix-core kernels: one dispatch at a time beside the back-to-back figure, whose
+        # launches run with the clock at the board's power limit
+        return {"single_dispatch_us": round(us, 3),
+                "single_dispatch_tflops": round(work["flops"] / (us * 1e-6) / 1e12, 1),
+                "note": "avg_launch_us: back-to-back launches (sustained); single_dispatch_us: median of "
+                        "10 synchronised single dispatches"}
 
     def record(name, op, shape, dtype, fused, ev_ms, n, extra=None):
         work = roofline.workload_work(op, shape, dtype, fused)
@@ -314,8 +341,12 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
 
         def sw_unf(i):
             api.fuse_unfused_swiglu(a, b1, b2, out=o, workspace=ws)
+        for i in range(3):
+            sw(i)
+        one = single_dispatch_us(torch, stream, sw)
         _, ev = time_launches(torch, stream, sw, n_launch // 2)
-        record("swiglu_bf16_2048x8960x1536", w.op, w.shape, w.dtype, True, ev, n_launch // 2)
+        record("swiglu_bf16_2048x8960x1536", w.op, w.shape, w.dtype, True, ev, n_launch // 2,
+               single_dispatch(one, roofline.workload_work(w.op, w.shape, w.dtype, True)))
         _, ev = time_launches(torch, stream, sw_unf, n_launch // 2)
         record("swiglu_unfused_bf16_2048x8960x1536", w.op, w.shape, w.dtype, False, ev, n_launch // 2)
         del ws
@@ -334,8 +365,12 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
 
         def gm_vendor(i):  # reference only: torch's library GEMM, not part of the path
             torch.matmul(x, wt, out=y)
+        for i in range(3):
+            gm(i)
+        one = single_dispatch_us(torch, stream, gm)
         _, ev = time_launches(torch, stream, gm, n_launch // 2)
-        record("gemm_bias_relu_bf16_2048x8960x1536", w.op, w.shape, w.dtype, True, ev, n_launch // 2)
+        record("gemm_bias_relu_bf16_2048x8960x1536", w.op, w.shape, w.dtype, True, ev, n_launch // 2,
+               single_dispatch(one, roofline.workload_work(w.op, w.shape, w.dtype, True)))
         _, ev = time_launches(torch, stream, gm_unf, n_launch // 2)
         record("gemm_bias_relu_unfused_bf16_2048x8960x1536", w.op, w.shape, w.dtype, False, ev, n_launch // 2,
                {"note": "GEMM kernel, bias kernel, ReLU kernel"})
