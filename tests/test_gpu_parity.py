@@ -369,6 +369,7 @@ def test_bias_gelu_residual_inplace_and_deterministic():
     (64, 2048, "f16", -1 / math.sqrt(128)),  # negative scale on full rows (max of -x)
     (33, 1024, "bf16", -0.3),
     (16, 2048, "f16", 0.0),                  # scale 0: every row uniform, 1/cols
+    (7, 4000, "f16", -0.25),                 # 128-bit path, chunks past the row, negative scale
 ])
 def test_softmax_parity(rows, cols, dtype, scale):
     announce(f"softmax {rows}x{cols} {dtype} scale={scale}")
