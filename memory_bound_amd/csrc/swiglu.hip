@@ -692,33 +692,51 @@ __device__ __forceinline__ void direct_tile(const DualArgs& p, char* lds, int m0
 // steps [split * ksteps, split * ksteps + ksteps) of its tile.  Otherwise the first tiles - tail
 // units are a whole tile each, and the last parts * tail units the remaining tiles as 128-row
 // halves or 64-row quarters: when the tiles leave a last round that fills few CUs, that round is
-// spread over more of them.  Workgroup b takes units b, b + grid, ...: one unit each when the grid
-// covers them all, otherwise (a grid of one workgroup per CU, rounded down to a multiple of 8)
-// every unit of its CU in turn, so unit u still runs on XCD u % 8, the one the tile map assumes.
+// spread over more of them.  One workgroup per unit, or, with more units than CUs, a grid of one
+// workgroup per CU (rounded down to a multiple of 8) walking units b, b + grid, ..., so that unit u
+// still runs on XCD u % 8, the one the tile map assumes.
+// Work unit `bid` of the full-tile kernel, in the ring `lds`.
+template <int S, int MODE>
+__device__ __forceinline__ void direct_unit(const DualArgs& p, char* lds, int bid) {
+    const int ntiles = p.tiles_m * p.tiles_n;
+    const int kt_all = p.K / DirectCfg::BKD;
+    const int head = ntiles - p.tail;
+    if (p.tail == 0 || bid < head) {
+        const int split = bid / ntiles;
+        const Tile tile = tile_of(bid - split * ntiles, p.tiles_m, p.tiles_n, p.bn_step);
+        const int kt0 = split * p.ksteps;
+        direct_tile<BM, S, MODE>(p, lds, tile.m0, tile.n0, kt0, min(p.ksteps, kt_all - kt0), split);
+    } else if (p.parts == 2) {
+        const int q = bid - head;
+        const Tile tile = tile_of(head + (q >> 1), p.tiles_m, p.tiles_n, p.bn_step);
+        direct_tile<BM / 2, S, MODE>(p, lds, tile.m0 + (BM / 2) * (q & 1), tile.n0, 0, kt_all, 0);
+    } else {
+        const int q = bid - head;
+        const Tile tile = tile_of(head + (q >> 2), p.tiles_m, p.tiles_n, p.bn_step);
+        direct_tile<BM / 4, S, MODE>(p, lds, tile.m0 + (BM / 4) * (q & 3), tile.n0, 0, kt_all, 0);
+    }
+}
+
+// One workgroup per work unit.
 template <int S, int MODE>
 __global__ void __launch_bounds__(THREADS, 1)
 swiglu_direct_kernel(DualArgs p) {
     static_assert(S >= 3 && S * DirectCfg::STAGE_BYTES <= 160 * 1024, "ring of 3 to 5 stages of 32 KiB");
     __shared__ __attribute__((aligned(1024))) char lds[S * DirectCfg::STAGE_BYTES];
-    const int ntiles = p.tiles_m * p.tiles_n;
-    const int kt_all = p.K / DirectCfg::BKD;
-    const int head = ntiles - p.tail;
+    direct_unit<S, MODE>(p, lds, blockIdx.x);
+}
+
+// One workgroup per CU walking units b, b + grid, ... (shapes with more units than CUs).  A kernel
+// of its own: the loop costs 17-20 spilled VGPRs of per-unit state (none inside the K loops), which
+// the one-unit kernel above, used for split K and for shapes that fit in one round, does not pay.
+template <int S, int MODE>
+__global__ void __launch_bounds__(THREADS, 1)
+swiglu_persist_kernel(DualArgs p) {
+    static_assert(S >= 3 && S * DirectCfg::STAGE_BYTES <= 160 * 1024, "ring of 3 to 5 stages of 32 KiB");
+    __shared__ __attribute__((aligned(1024))) char lds[S * DirectCfg::STAGE_BYTES];
     for (int bid = blockIdx.x; bid < p.units; bid += gridDim.x) {
         if (bid > (int)blockIdx.x) __syncthreads();  // the previous unit's last LDS reads are done
-        if (p.tail == 0 || bid < head) {
-            const int split = bid / ntiles;
-            const Tile tile = tile_of(bid - split * ntiles, p.tiles_m, p.tiles_n, p.bn_step);
-            const int kt0 = split * p.ksteps;
-            direct_tile<BM, S, MODE>(p, lds, tile.m0, tile.n0, kt0, min(p.ksteps, kt_all - kt0), split);
-        } else if (p.parts == 2) {
-            const int q = bid - head;
-            const Tile tile = tile_of(head + (q >> 1), p.tiles_m, p.tiles_n, p.bn_step);
-            direct_tile<BM / 2, S, MODE>(p, lds, tile.m0 + (BM / 2) * (q & 1), tile.n0, 0, kt_all, 0);
-        } else {
-            const int q = bid - head;
-            const Tile tile = tile_of(head + (q >> 2), p.tiles_m, p.tiles_n, p.bn_step);
-            direct_tile<BM / 4, S, MODE>(p, lds, tile.m0 + (BM / 4) * (q & 3), tile.n0, 0, kt_all, 0);
-        }
+        direct_unit<S, MODE>(p, lds, bid);
     }
 }
 
@@ -824,10 +842,14 @@ hipError_t launch(DualArgs p, int tile_cols, hipStream_t stream) {
     p.tail = tp.tail;
     p.parts = tp.parts;
     p.units = p.tiles_m * p.tiles_n + (tp.parts - 1) * tp.tail;
-    dim3 grid((unsigned)p.units), block(THREADS);
-    if (st != 0 && persistent()) {
-        const int cus = cu_count(), g = cus >= NUM_XCD ? cus / NUM_XCD * NUM_XCD : cus;
-        grid = dim3((unsigned)min(p.units, g));
+    const dim3 grid((unsigned)p.units), block(THREADS);
+    const int cus = cu_count(), g = cus >= NUM_XCD ? cus / NUM_XCD * NUM_XCD : cus;
+    if (st != 0 && persistent() && p.units > g) {
+        const dim3 pg((unsigned)g);
+        if (st == 3) hipLaunchKernelGGL((swiglu_persist_kernel<3, MODE>), pg, block, 0, stream, p);
+        else if (st == 5) hipLaunchKernelGGL((swiglu_persist_kernel<5, MODE>), pg, block, 0, stream, p);
+        else hipLaunchKernelGGL((swiglu_persist_kernel<4, MODE>), pg, block, 0, stream, p);
+        return hipGetLastError();
     }
     if (st == 3) hipLaunchKernelGGL((swiglu_direct_kernel<3, MODE>), grid, block, 0, stream, p);
     else if (st == 4) hipLaunchKernelGGL((swiglu_direct_kernel<4, MODE>), grid, block, 0, stream, p);
