@@ -190,3 +190,28 @@ def test_profile_summary_clock_and_matrix_core_busy(tmp_path):
     assert r["us"] == 1.0 and r["mhz"] == 2000.0 and r["mfma_busy"] == 0.5
     assert abs(r["tflops"] - 1000.0) < 1e-9
     assert abs(r["peak_tflops"] - 1024 * 1024 * 2e9 / 1e12) < 1e-9
+
+
+def test_profiles_name_kernels_the_library_still_has():
+    # every kernel a committed profile summary names (outside torch's own) is a __global__
+    # function of the library's sources, with as many template arguments as its template has
+    # parameters, so that a renamed or re-templated kernel shows up as a stale summary
+    import pathlib
+    import re
+    root = pathlib.Path(__file__).resolve().parent.parent
+    src = "\n".join(p.read_text() for p in sorted((root / "memory_bound_amd" / "csrc").iterdir())
+                    if p.suffix in (".hip", ".hpp", ".h"))
+    arity = {}
+    for m in re.finditer(r"(?:template\s*<([^>]*)>\s*)?__global__\s+void\s+(?:__launch_bounds__\([^)]*\)\s*)?"
+                         r"(\w+_kernel)\s*\(", src):
+        arity[m.group(2)] = len(m.group(1).split(",")) if m.group(1) else 0
+    assert {"add_layernorm_kernel", "swiglu_persist_kernel", "copy16_kernel", "empty_kernel"} <= set(arity)
+    named = 0
+    for prof in sorted((root / "profiles").glob("*.txt")):
+        for m in re.finditer(r"(?<![\w:])(\w+_kernel)(?!\w)(?:<([^<>\n]*)>)?", prof.read_text()):
+            name, args = m.group(1), m.group(2)
+            assert name in arity, f"{prof.name} names {name}, which the library no longer defines"
+            if args is not None:
+                assert len(args.split(",")) == arity[name], f"{prof.name}: {name}<{args}>"
+            named += 1
+    assert named > 50
