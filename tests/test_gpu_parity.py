@@ -679,6 +679,27 @@ def test_gemm_workload_sampled_rows():
     assert torch.equal(y, y2)
 
 
+@pytest.mark.parametrize("act", ["relu", "gelu"])
+def test_gemm_tail_slices_at_full_grid(monkeypatch, act):
+    # 2048x8960 in 256x256 tiles is 280 tiles: one round on 256 CUs and 24 tiles left, run as
+    # 64-row quarters, the 352 units walked by one resident workgroup per CU.  The k order per
+    # element does not depend on how the tiles are cut or launched: bit-identical to whole tiles
+    # and to one workgroup per unit, and checked against the oracle on sampled rows.
+    M, N, K = 2048, 8960, 256
+    announce(f"gemm_bias_act {M}x{N}x{K} {act} tail slices")
+    d = synth.gemm_inputs(M, N, K, "bf16", seed=77)
+    x, w, bias = d["x"].cuda(), d["w"].cuda(), d["bias"].cuda()
+    y = api.fuse_gemm_bias_act(x, w, bias, act)
+    for env in ({"FUSE_SWIGLU_TAIL": "0"}, {"FUSE_SWIGLU_PERSIST": "0"}):
+        with monkeypatch.context() as m:
+            for k, v in env.items():
+                m.setenv(k, v)
+            assert torch.equal(y, api.fuse_gemm_bias_act(x, w, bias, act)), f"{env}"
+    rows = torch.arange(5, M, 31)
+    assert_close(y[rows.cuda()], oracle.gemm_bias_act(d["x"][rows], d["w"], d["bias"], act), "bf16",
+                 f"gemm {M}x{N}x{K} {act} tail")
+
+
 # ------------------------------------------------------------------------------------------------
 # Shape-dependent plans: split K for shapes whose tiles cannot fill the GPU
 # ------------------------------------------------------------------------------------------------
