@@ -6,11 +6,12 @@
  * the benchmark do.  It shares no code, header, table or helper with the HIP
  * library.
  *
- * Every routine is the plain definition of what the fused kernels compute,
- * written out in double precision with simple loops, in the order the pages
- * state the steps.  No blocking, no fusion, no reordering of a sum beyond the
- * natural ascending index.  Rows are independent, so an OpenMP loop over rows
- * changes nothing in the arithmetic of any one row.
+ * Every routine is the plain mathematical definition of what the fused
+ * kernels compute, written out in double precision with simple loops: the
+ * row moments of LayerNorm and the exponential sum of softmax by pairwise
+ * summation, products and prefix sums in ascending index order.  No blocking
+ * and no fusion.  Rows are independent, so an OpenMP loop over rows changes
+ * nothing in the arithmetic of any one row.
  *
  * Pages cited (titles abbreviated):
  *   [P1] "CUDA算子融合优化：提升GPU推理性能的核心机制"
@@ -24,65 +25,115 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 /*
- * Residual add followed by LayerNorm.
+ * Sum of n doubles by recursive halving (pairwise summation).  Its rounding
+ * error grows with log2(n) instead of n, so in double precision the row
+ * statistics below are exact to far more digits than any fp32 / fp16 result
+ * can resolve.  Blocks of up to eight terms are added left to right.
+ */
+static double pairwise_sum(const double *v, int64_t n)
+{
+    double s = 0.0;
+    int64_t i, h;
+
+    if (n <= 8) {
+        for (i = 0; i < n; i++)
+            s += v[i];
+        return s;
+    }
+    h = n / 2;
+    return pairwise_sum(v, h) + pairwise_sum(v + h, n - h);
+}
+
+/*
+ * First two moments of a row of n values, by their definitions: the mean
+ * mu = (1/n) sum v, the centred values c[i] = v[i] - mu (written to c), and
+ * the population variance (1/n) sum c[i]^2 (divisor n, not n - 1).  Returns
+ * the variance.  c may be v itself.
+ */
+static double row_moments(const double *v, double *c, int64_t n, double *mu)
+{
+    int64_t i;
+    double m = pairwise_sum(v, n) / (double)n;
+
+    for (i = 0; i < n; i++)
+        c[i] = v[i] - m;
+    for (i = 0; i < n; i++)
+        c[i] = c[i] * c[i];
+    *mu = m;
+    return pairwise_sum(c, n) / (double)n;
+}
+
+/*
+ * Residual add followed by LayerNorm (page "算子融合的收益量化", §1
+ * 物理流量量化: the fused sub-graph is the sum A = X + R normalised by a
+ * LayerNorm, and only the normalised Y leaves the kernel; page "4. 算子融合与
+ * Kernel合并", §4.2: the normaliser is the population standard deviation with
+ * eps added to the variance inside the root, and gamma / beta are indexed by
+ * the position in the row).
  *
- * [P3] §1 (物理流量量化): the fused sub-graph is A = X + R followed by a
- * LayerNorm of A; only the normalised Y is produced.
- * [P2] §4.2 (the fused_layernorm sketch): mean = (sum of the row) / N; var =
- * (sum of squared deviations from that mean) / N, i.e. the population
- * variance, taken in a second sweep over the row; std = sqrt(var + eps);
- * out = gamma * (v - mean) / std + beta, with gamma and beta indexed by the
- * position in the row.
+ * Per row: v = x + r; mu and var = the moments of v (row_moments);
+ * y[i] = gamma[i] * (v[i] - mu) * (1 / sqrt(var + eps)) + beta[i].
  *
  * residual may be NULL, which gives the plain LayerNorm of x.
  * y may not alias x or residual.
  */
+static void layernorm_row(const double *xr, const double *rr, const double *gamma,
+                          const double *beta, double *v, double *work,
+                          int64_t hidden, double eps, double *mu_out,
+                          double *var_out)
+{
+    int64_t i;
+    double mu, var, inv;
+
+    for (i = 0; i < hidden; i++)
+        v[i] = rr ? xr[i] + rr[i] : xr[i];
+    var = row_moments(v, work, hidden, &mu);
+    inv = 1.0 / sqrt(var + eps);
+    if (mu_out)
+        *mu_out = mu;
+    if (var_out)
+        *var_out = var;
+    for (i = 0; i < hidden; i++)
+        v[i] = gamma[i] * ((v[i] - mu) * inv) + beta[i];
+}
+
 void oracle_add_layernorm(const double *x, const double *residual,
                           const double *gamma, const double *beta, double *y,
                           int64_t rows, int64_t hidden, double eps)
 {
     int64_t row;
-#pragma omp parallel for schedule(static)
-    for (row = 0; row < rows; row++) {
-        const double *xr = x + row * hidden;
-        const double *rr = residual ? residual + row * hidden : NULL;
-        double *v = y + row * hidden; /* holds x + r until overwritten */
-        double sum = 0.0, var = 0.0, mean, std;
-        int64_t i;
-
-        for (i = 0; i < hidden; i++)
-            v[i] = rr ? xr[i] + rr[i] : xr[i];
-
-        for (i = 0; i < hidden; i++)
-            sum += v[i];
-        mean = sum / (double)hidden;
-
-        for (i = 0; i < hidden; i++)
-            var += (v[i] - mean) * (v[i] - mean);
-        std = sqrt(var / (double)hidden + eps);
-
-        for (i = 0; i < hidden; i++)
-            v[i] = gamma[i] * (v[i] - mean) / std + beta[i];
+#pragma omp parallel
+    {
+        double *work = malloc((size_t)(hidden > 0 ? hidden : 1) * sizeof(double));
+#pragma omp for schedule(static)
+        for (row = 0; row < rows; row++)
+            layernorm_row(x + row * hidden,
+                          residual ? residual + row * hidden : NULL, gamma,
+                          beta, y + row * hidden, work, hidden, eps, NULL,
+                          NULL);
+        free(work);
     }
 }
 
 /*
  * Variants of the same residual-add + LayerNorm row operation.
  *
- * [P1] §二.1 lists "LayerNorm + ReLU" as one vertical fusion: the
- * activation is applied to the normalised value before it is stored,
- * y = max(LN(v), 0); relu != 0 selects it.  A NaN stays NaN (the test is
- * "below zero", which a NaN is not).
- * [P2] §4.4 (multi-output fusion): one pass over the input yields several
- * outputs, with mean and var computed together as its example.  Besides y,
- * any of these may be requested (NULL = not wanted):
+ * Page "CUDA算子融合优化", §二.1 lists "LayerNorm + ReLU" as one vertical
+ * fusion: the activation is applied to the normalised value before it is
+ * stored, y = max(LN(v), 0); relu != 0 selects it.  A NaN stays NaN (the test
+ * is "below zero", which a NaN is not).
+ * Page "4. 算子融合与Kernel合并", §4.4 (multi-output fusion): one pass over
+ * the input yields several outputs, with mean and variance computed together
+ * as its example.  Besides y, any of these may be requested (NULL = not
+ * wanted):
  *   sum  [rows, hidden]  the pre-norm sum v = x + residual (the residual
  *                        stream a pre-norm block carries on);
  *   mean [rows]          mean of v;
  *   var  [rows]          population variance of v (without eps).
- * The statistics are those of oracle_add_layernorm, computed the same way.
+ * The statistics are those of oracle_add_layernorm (row_moments).
  */
 void oracle_add_layernorm_ex(const double *x, const double *residual,
                              const double *gamma, const double *beta, double *y,
@@ -90,37 +141,27 @@ void oracle_add_layernorm_ex(const double *x, const double *residual,
                              int64_t rows, int64_t hidden, double eps, int relu)
 {
     int64_t row;
-#pragma omp parallel for schedule(static)
-    for (row = 0; row < rows; row++) {
-        const double *xr = x + row * hidden;
-        const double *rr = residual ? residual + row * hidden : NULL;
-        double *v = y + row * hidden; /* holds x + r until overwritten */
-        double s = 0.0, q = 0.0, mu, std;
-        int64_t i;
+#pragma omp parallel
+    {
+        double *work = malloc((size_t)(hidden > 0 ? hidden : 1) * sizeof(double));
+#pragma omp for schedule(static)
+        for (row = 0; row < rows; row++) {
+            const double *xr = x + row * hidden;
+            const double *rr = residual ? residual + row * hidden : NULL;
+            double *yr = y + row * hidden;
+            int64_t i;
 
-        for (i = 0; i < hidden; i++)
-            v[i] = rr ? xr[i] + rr[i] : xr[i];
-        if (sum)
-            for (i = 0; i < hidden; i++)
-                sum[row * hidden + i] = v[i];
-
-        for (i = 0; i < hidden; i++)
-            s += v[i];
-        mu = s / (double)hidden;
-
-        for (i = 0; i < hidden; i++)
-            q += (v[i] - mu) * (v[i] - mu);
-        std = sqrt(q / (double)hidden + eps);
-        if (mean)
-            mean[row] = mu;
-        if (var)
-            var[row] = q / (double)hidden;
-
-        for (i = 0; i < hidden; i++) {
-            v[i] = gamma[i] * (v[i] - mu) / std + beta[i];
-            if (relu && v[i] < 0.0)
-                v[i] = 0.0;
+            if (sum)
+                for (i = 0; i < hidden; i++)
+                    sum[row * hidden + i] = rr ? xr[i] + rr[i] : xr[i];
+            layernorm_row(xr, rr, gamma, beta, yr, work, hidden, eps,
+                          mean ? mean + row : NULL, var ? var + row : NULL);
+            if (relu)
+                for (i = 0; i < hidden; i++)
+                    if (yr[i] < 0.0)
+                        yr[i] = 0.0;
         }
+        free(work);
     }
 }
 
@@ -186,11 +227,16 @@ void oracle_cumsum_scale_rows(const double *x, double *y, int64_t rows,
 }
 
 /*
- * Row softmax of scaled scores.
+ * Row softmax of scaled scores (page "CUDA算子融合优化", §二.1: "Softmax +
+ * Scale" is one vertical fusion, so the scores are z = scale * x; page "4.
+ * 算子融合与Kernel合并", §4.3: the row's maximum, the sum of the
+ * exponentials, then the normalisation).
  *
- * [P1] §二.1 lists "Softmax + Scale" as one vertical fusion: z = scale * x.
- * [P2] §4.3 (the fused_softmax sketch): m = max over the row; each term is
- * exp(z - m); s = their sum; out = exp(z - m) / s.
+ * Per row, by the definition y_j = e^{z_j} / sum_k e^{z_k} written in its
+ * overflow-free form (numerator and denominator both multiplied by e^{-m}):
+ * m = max_k z_k, e_k = e^{z_k - m}, s = sum_k e_k (pairwise), y_j = e_j / s.
+ * m is an element of the row, so every exponent is at most 0 and s is in
+ * [1, cols].
  */
 void oracle_softmax_rows(const double *x, double *y, int64_t rows,
                          int64_t cols, double scale)
@@ -200,18 +246,18 @@ void oracle_softmax_rows(const double *x, double *y, int64_t rows,
     for (row = 0; row < rows; row++) {
         const double *xr = x + row * cols;
         double *yr = y + row * cols;
-        double m = -INFINITY, s = 0.0;
+        double m = -INFINITY, s;
         int64_t j;
 
-        for (j = 0; j < cols; j++) {
-            double z = scale * xr[j];
-            if (z > m)
-                m = z;
-        }
         for (j = 0; j < cols; j++)
-            s += exp(scale * xr[j] - m);
+            yr[j] = scale * xr[j];
         for (j = 0; j < cols; j++)
-            yr[j] = exp(scale * xr[j] - m) / s;
+            m = (yr[j] > m || isnan(yr[j])) ? yr[j] : m;
+        for (j = 0; j < cols; j++)
+            yr[j] = exp(yr[j] - m);
+        s = pairwise_sum(yr, cols);
+        for (j = 0; j < cols; j++)
+            yr[j] = yr[j] / s;
     }
 }
 
