@@ -434,6 +434,41 @@ def test_unfused_softmax_equals_rounded_terms_over_sum():
     np.testing.assert_allclose(y[0], [1365 * 2.0 ** -12 * 0.75, 0.75], rtol=0, atol=1e-15)
 
 
+def _rne_integer(k: int, frac_bits: int) -> int:
+    """Integer k rounded to a float with frac_bits fraction bits, ties to even, written out by
+    hand: above 2^(frac_bits+1) the spacing is 2^(e - frac_bits); a tie goes to the neighbour
+    whose last kept bit is zero."""
+    e = k.bit_length() - 1
+    q = 1 << max(0, e - frac_bits)
+    lo, rem = (k // q) * q, k % q
+    if 2 * rem < q:
+        return lo
+    if 2 * rem > q:
+        return lo + q
+    return lo if (lo // q) % 2 == 0 else lo + q
+
+
+@pytest.mark.parametrize("kind,frac_bits,n", [("f16", 10, 4096), ("bf16", 7, 600)])
+def test_unfused_cumsum_rounds_prefix_sums_before_the_scale(kind, frac_bits, n):
+    # a row of ones: the stored prefix sums are the integers 1..n, exact up to 2^(frac_bits+1)
+    # and rounded to even beyond it (f16: 2049 -> 2048, 2051 -> 2052); the scale kernel then
+    # multiplies the stored value.  Scale 3: scaling before the rounding would give a different
+    # grid point (f16: 3 * 2052 = 6156 against round(3 * 2051) = 6152).
+    x = np.ones((2, n))
+    y = oracle.cumsum_scale_rows_unfused(x, 3.0, kind)
+    want = np.array([3.0 * _rne_integer(k, frac_bits) for k in range(1, n + 1)])
+    np.testing.assert_array_equal(y[0], want)
+    np.testing.assert_array_equal(y[1], want)
+    # below 2^(frac_bits+1) every prefix sum is exact: the unfused chain equals the fused result
+    m = 1 << (frac_bits + 1)
+    np.testing.assert_array_equal(y[0, :m], oracle.cumsum_scale_rows(x, 3.0)[0, :m])
+
+
+def test_rne_integer_helper_against_numpy_f16():
+    ks = np.arange(1, 8193)
+    np.testing.assert_array_equal([_rne_integer(int(k), 10) for k in ks], ks.astype(np.float16).astype(np.int64))
+
+
 def test_unfused_swiglu_rounds_both_products():
     a = np.array([[1.0]])
     b1 = np.array([[1.0 + 2.0 ** -10]])  # not a bf16 value: rounds to 1
