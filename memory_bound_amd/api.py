@@ -146,12 +146,28 @@ def _ok(status: int, what: str):
         raise FuseError(status, what)
 
 
-def _workspace(op, d0, d1, d2, dtype_code, device):
-    n = load().fuse_unfused_workspace_bytes(op, d0, d1, d2, dtype_code)
-    # one extra 256 bytes so that the base can be rounded up to a 256-byte boundary
+def _torch_stream(stream):
+    """The torch stream object for a stream argument (None = the current stream)."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream))
+
+
+def _scratch(n, device, stream):
+    """n bytes of device memory whose base is rounded up to a 256-byte boundary.  The kernels
+    that use it are enqueued on `stream`, which may not be torch's current stream: the block is
+    marked as used there, so the caching allocator does not hand it out again (after this
+    wrapper drops it) before the work already enqueued on that stream has finished."""
     buf = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    buf.record_stream(_torch_stream(stream))
     off = (-buf.data_ptr()) % 256
     return buf, ctypes.c_void_p(buf.data_ptr() + off), n
+
+
+def _workspace(op, d0, d1, d2, dtype_code, device, stream=None):
+    return _scratch(load().fuse_unfused_workspace_bytes(op, d0, d1, d2, dtype_code), device, stream)
 
 
 # ------------------------------------------------------------------------------------------------
@@ -270,13 +286,11 @@ def fuse_gemm_bias_act(x, w, bias=None, act="relu", y=None, stream=None):
     return y
 
 
-def _auto_workspace(op, M, N, K, device):
+def _auto_workspace(op, M, N, K, device, stream=None):
     n = load().fuse_auto_workspace_bytes(op, M, N, K, FUSE_BF16)
     if n == 0:
         return None, None, 0
-    buf = torch.empty(n + 256, dtype=torch.uint8, device=device)
-    off = (-buf.data_ptr()) % 256
-    return buf, ctypes.c_void_p(buf.data_ptr() + off), n
+    return _scratch(n, device, stream)
 
 
 def fuse_auto_splits(op, M, N, K) -> int:
@@ -294,7 +308,7 @@ def fuse_swiglu_auto(a, b1, b2, out=None, workspace=None, stream=None):
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
     _check(out, "out", a.dtype, (M, N))
-    ws = workspace or _auto_workspace(FUSE_OP_SWIGLU, M, N, K, a.device)
+    ws = workspace or _auto_workspace(FUSE_OP_SWIGLU, M, N, K, a.device, stream)
     _ok(load().fuse_swiglu_auto(_ptr(a), _ptr(b1), _ptr(b2), _ptr(out), M, N, K, _dt(a), ws[1], ws[2],
                                 _stream(stream)), "fuse_swiglu_auto")
     return out
@@ -310,7 +324,7 @@ def fuse_gemm_bias_act_auto(x, w, bias=None, act="relu", y=None, workspace=None,
     if y is None:
         y = torch.empty((M, N), dtype=x.dtype, device=x.device)
     _check(y, "y", x.dtype, (M, N))
-    ws = workspace or _auto_workspace(FUSE_OP_GEMM_BIAS_ACT, M, N, K, x.device)
+    ws = workspace or _auto_workspace(FUSE_OP_GEMM_BIAS_ACT, M, N, K, x.device, stream)
     _ok(load().fuse_gemm_bias_act_auto(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), M, N, K, FUSE_ACT[act], _dt(x),
                                        ws[1], ws[2], _stream(stream)), "fuse_gemm_bias_act_auto")
     return y
@@ -329,7 +343,7 @@ def fuse_unfused_add_layernorm(x, residual, gamma, beta, eps=1e-5, y=None, works
     if y is None:
         y = torch.empty_like(x)
     _check(y, "y", x.dtype, x.shape)
-    ws = workspace or _workspace(FUSE_OP_ADD_LAYERNORM, rows, hidden, 0, _dt(x), x.device)
+    ws = workspace or _workspace(FUSE_OP_ADD_LAYERNORM, rows, hidden, 0, _dt(x), x.device, stream)
     _ok(load().fuse_unfused_add_layernorm(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y), rows,
                                           hidden, float(eps), _dt(x), ws[1], ws[2], _stream(stream)),
         "fuse_unfused_add_layernorm")
@@ -344,7 +358,7 @@ def fuse_unfused_bias_gelu_residual(x, bias, residual, y=None, workspace=None, s
     if y is None:
         y = torch.empty_like(x)
     _check(y, "y", x.dtype, x.shape)
-    ws = workspace or _workspace(FUSE_OP_BIAS_GELU_RESIDUAL, rows, hidden, 0, _dt(x), x.device)
+    ws = workspace or _workspace(FUSE_OP_BIAS_GELU_RESIDUAL, rows, hidden, 0, _dt(x), x.device, stream)
     _ok(load().fuse_unfused_bias_gelu_residual(_ptr(x), _ptr(bias), _ptr(residual), _ptr(y), rows, hidden,
                                                _dt(x), ws[1], ws[2], _stream(stream)),
         "fuse_unfused_bias_gelu_residual")
@@ -357,7 +371,7 @@ def fuse_unfused_softmax_rows(x, scale=1.0, y=None, workspace=None, stream=None)
     if y is None:
         y = torch.empty_like(x)
     _check(y, "y", x.dtype, x.shape)
-    ws = workspace or _workspace(FUSE_OP_SOFTMAX_ROWS, rows, cols, 0, _dt(x), x.device)
+    ws = workspace or _workspace(FUSE_OP_SOFTMAX_ROWS, rows, cols, 0, _dt(x), x.device, stream)
     _ok(load().fuse_unfused_softmax_rows(_ptr(x), _ptr(y), rows, cols, float(scale), _dt(x), ws[1], ws[2],
                                          _stream(stream)), "fuse_unfused_softmax_rows")
     return y
@@ -369,7 +383,7 @@ def fuse_unfused_cumsum_scale_rows(x, scale=1.0, y=None, workspace=None, stream=
     if y is None:
         y = torch.empty_like(x)
     _check(y, "y", x.dtype, x.shape)
-    ws = workspace or _workspace(FUSE_OP_CUMSUM_SCALE, rows, cols, 0, _dt(x), x.device)
+    ws = workspace or _workspace(FUSE_OP_CUMSUM_SCALE, rows, cols, 0, _dt(x), x.device, stream)
     _ok(load().fuse_unfused_cumsum_scale_rows(_ptr(x), _ptr(y), rows, cols, float(scale), _dt(x), ws[1], ws[2],
                                               _stream(stream)), "fuse_unfused_cumsum_scale_rows")
     return y
@@ -384,7 +398,7 @@ def fuse_unfused_swiglu(a, b1, b2, out=None, workspace=None, stream=None):
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
     _check(out, "out", a.dtype, (M, N))
-    ws = workspace or _workspace(FUSE_OP_SWIGLU, M, N, K, _dt(a), a.device)
+    ws = workspace or _workspace(FUSE_OP_SWIGLU, M, N, K, _dt(a), a.device, stream)
     _ok(load().fuse_unfused_swiglu(_ptr(a), _ptr(b1), _ptr(b2), _ptr(out), M, N, K, _dt(a), ws[1], ws[2],
                                    _stream(stream)), "fuse_unfused_swiglu")
     return out
@@ -404,7 +418,7 @@ def fuse_unfused_gemm_bias_act(x, w, bias=None, act="relu", y=None, workspace=No
     if y is None:
         y = torch.empty((M, N), dtype=x.dtype, device=x.device)
     _check(y, "y", x.dtype, (M, N))
-    ws = workspace or _workspace(FUSE_OP_GEMM_BIAS_ACT, M, N, K, _dt(x), x.device)
+    ws = workspace or _workspace(FUSE_OP_GEMM_BIAS_ACT, M, N, K, _dt(x), x.device, stream)
     _ok(load().fuse_unfused_gemm_bias_act(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), M, N, K, FUSE_ACT[act], _dt(x),
                                           ws[1], ws[2], _stream(stream)), "fuse_unfused_gemm_bias_act")
     return y
