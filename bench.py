@@ -418,6 +418,75 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
     return out
 
 
+SWEEP_ROWS = (512, 1024, 2048, 4096, 8192, 16384, 32768)
+
+
+def linear_fit(xs, ys):
+    """Least-squares line y = a + b x; returns (a, b)."""
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((x - mx) ** 2 for x in xs)
+    b = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sxx
+    return my - b * mx, b
+
+
+def size_sweep(torch, api, synth, roofline, n=40):
+    """Fused Add+LayerNorm fp16 at H = 4096 and a plain copy of the same byte count, over rows
+    512 ... 32768, cold (each launch on a buffer set not touched for 1 GiB of traffic), each size
+    replayed n times from a HIP graph.  A line t = t0 + bytes / bw fitted to each kernel's times
+    separates the fixed cost per launch (t0) from the streaming rate it approaches (bw).  Under
+    rocprofv3 --kernel-trace every size is a grid of its own, so the trace gives the same sweep in
+    kernel durations."""
+    w = synth.WORKLOADS[HEADLINE]
+    base = w.inputs()
+    hidden = w.shape[1]
+    bx, br = base["x"].cuda(), base["residual"].cuda()
+    gamma, beta = base["gamma"].cuda(), base["beta"].cuda()
+    stream = torch.cuda.Stream()
+    sizes = []
+
+    def rows_of(t, rows):
+        return t[:rows].clone() if rows <= t.shape[0] else t.repeat(rows // t.shape[0], 1)
+
+    with torch.cuda.stream(stream):
+        for rows in SWEEP_ROWS:
+            work = roofline.workload_work("add_layernorm", (rows, hidden), "f16")
+            per_set = 3 * rows * hidden * 2
+            nsets = max(2, math.ceil(ROTATE_BYTES / per_set))
+            sets = [(rows_of(bx, rows), rows_of(br, rows), torch.empty(rows, hidden, dtype=torch.float16, device="cuda"))
+                    for _ in range(nsets)]
+
+            def ln(i):
+                x, r, y = sets[i % nsets]
+                api.fuse_add_layernorm(x, r, gamma, beta, 1e-5, y=y)
+            _, ev = time_launches(torch, stream, ln, n)
+            ln_us = ev * 1e3 / n
+            del sets
+            nbytes = 3 * rows * hidden  # a copy of this many bytes moves the three tensors' bytes
+            nb = max(2, math.ceil(ROTATE_BYTES / (2 * nbytes)))
+            bufs = [(torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1),
+                     torch.empty(nbytes, dtype=torch.uint8, device="cuda")) for _ in range(nb)]
+
+            def cp(i):
+                s, t = bufs[i % nb]
+                api.fuse_copy(s, t)
+            _, ev = time_launches(torch, stream, cp, n)
+            cp_us = ev * 1e3 / n
+            del bufs
+            sizes.append({"rows": rows, "bytes": work["bytes"], "add_layernorm_us": round(ln_us, 3),
+                          "copy_us": round(cp_us, 3), "copy_bytes": 2 * nbytes,
+                          "add_layernorm_frac": round(work["bytes"] / (ln_us * 1e-6) / 1e9 / roofline.HBM_PEAK_GBPS, 4),
+                          "copy_frac": round(2 * nbytes / (cp_us * 1e-6) / 1e9 / roofline.HBM_PEAK_GBPS, 4)})
+            log(f"sweep rows={rows}: add_layernorm {ln_us:.2f} us, copy {cp_us:.2f} us")
+    out = {"hidden": hidden, "dtype": "f16", "launches_per_size": n, "timing": "HIP events around a graph replay",
+           "sizes": sizes}
+    for key, bkey in (("add_layernorm", "bytes"), ("copy", "copy_bytes")):
+        t0, inv_bw = linear_fit([s[bkey] for s in sizes], [s[f"{key}_us"] for s in sizes])
+        out[f"{key}_fit"] = {"t0_us": round(t0, 3), "bw_gbps": round(1e-3 / inv_bw, 1),
+                             "bw_frac": round(1e-3 / inv_bw / roofline.HBM_PEAK_GBPS, 4)}
+    return out
+
+
 def counters_pass(torch, api, synth, n=8):
     """A few eager dispatches of each kernel whose HBM bytes the hardware counters are read for
     (run under rocprofv3 --pmc): fused Add+LayerNorm, its unfused chain, the fused and unfused
@@ -603,16 +672,44 @@ def launch_study(torch, api, synth, n_empty=4000, n_graph=1000, n_steps=200):
     return out
 
 
-def selection_study(torch, api, synth, K=1536, n=20):
+def interleaved(torch, stream, variants, n, rounds):
+    """Times several variants against each other without an order bias: each variant is captured
+    as a graph of n launches, then `rounds` rounds replay every graph once, the starting variant
+    rotating from round to round (ABCD, BCDA, ...), so the clock's drift under the power limit
+    and the caches left by the previous variant fall on every variant alike.  Returns, per
+    variant, the median, minimum and maximum over the rounds of the time per launch (us)."""
+    graphs = {}
+    for name, f in variants.items():
+        for i in range(3):
+            f(i)
+        torch.cuda.synchronize()
+        graphs[name] = Timed(torch, stream, f, n)
+        graphs[name].run()
+    names = list(graphs)
+    times = {k: [] for k in names}
+    for r in range(rounds):
+        for j in range(len(names)):
+            k = names[(r + j) % len(names)]
+            _, ev = graphs[k].run()
+            times[k].append(ev * 1e3 / n)
+    return {k: {"median_us": round(statistics.median(v), 2), "min_us": round(min(v), 2), "max_us": round(max(v), 2)}
+            for k, v in times.items()}
+
+
+def selection_study(torch, api, synth, K=1536, n=20, rounds=5):
     """Fused (scheme B) against unfused (scheme A) SwiGLU over shapes ([P4] 不同场景下的选型建议
     derives its thresholds from block counts against SM counts): this library's own scheme A
-    (the product kernel storing c1 and c2, then SiLU * product), and for context the library-GEMM
-    form of scheme A (two torch matmuls, then SiLU and product as torch kernels).  Same buffers
-    every launch (the weights stay cache-resident, as they would across a model's layers)."""
+    (the product kernel storing c1 and c2, then SiLU * product), its per-shape plan (the fused
+    kernel or its split-K form) and, for context, the library-GEMM form of scheme A (two torch
+    matmuls, then SiLU and product as torch kernels).  Same buffers every launch (the weights stay
+    cache-resident, as they would across a model's layers).  The four are timed interleaved (see
+    `interleaved`); a ratio between two of them is marked significant only when their ranges over
+    the rounds do not overlap."""
     import torch.nn.functional as F
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     stream = torch.cuda.Stream()
-    out = {"cus": cus, "K": K, "shapes": []}
+    out = {"cus": cus, "K": K, "launches_per_replay": n, "rounds": rounds,
+           "timing": "median (min..max) over interleaved rounds of a graph replay", "shapes": []}
     with torch.cuda.stream(stream):
         for M in (256, 1024, 2048):
             for N in (256, 512, 1024, 2048, 4096, 8960):
@@ -621,32 +718,28 @@ def selection_study(torch, api, synth, K=1536, n=20):
                 o = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
                 c1, c2 = torch.empty_like(o), torch.empty_like(o)
                 ws = api._workspace(api.FUSE_OP_SWIGLU, M, N, K, api.FUSE_BF16, "cuda")
-
-                def fused(i):
-                    api.fuse_swiglu_dualgemm(a, b1, b2, out=o)
-
-                def ours_a(i):
-                    api.fuse_unfused_swiglu(a, b1, b2, out=o, workspace=ws)
+                wsa = api._auto_workspace(api.FUSE_OP_SWIGLU, M, N, K, "cuda")
 
                 def lib_a(i):
                     torch.matmul(a, b1, out=c1)
                     torch.matmul(a, b2, out=c2)
                     torch.mul(F.silu(c1), c2, out=o)
-                wsa = api._auto_workspace(api.FUSE_OP_SWIGLU, M, N, K, "cuda")
-
-                def auto(i):
-                    api.fuse_swiglu_auto(a, b1, b2, out=o, workspace=wsa)
+                variants = {
+                    "fused": lambda i: api.fuse_swiglu_dualgemm(a, b1, b2, out=o),
+                    "unfused": lambda i: api.fuse_unfused_swiglu(a, b1, b2, out=o, workspace=ws),
+                    "auto": lambda i: api.fuse_swiglu_auto(a, b1, b2, out=o, workspace=wsa),
+                    "library_gemm_scheme_a": lib_a,
+                }
+                t = interleaved(torch, stream, variants, n, rounds)
                 r = {"M": M, "N": N, "tiles_fused": -(-M // 256) * -(-N // 128),
-                     "auto_splits": api.fuse_auto_splits(api.FUSE_OP_SWIGLU, M, N, K)}
-                for name, f in (("fused_us", fused), ("unfused_us", ours_a), ("auto_us", auto),
-                                ("library_gemm_scheme_a_us", lib_a)):
-                    _, ev = time_launches(torch, stream, f, n)
-                    r[name] = round(ev * 1e3 / n, 2)
-                r["fused_speedup_vs_unfused"] = round(r["unfused_us"] / r["fused_us"], 3)
+                     "auto_splits": api.fuse_auto_splits(api.FUSE_OP_SWIGLU, M, N, K), "times": t}
+                for a_, b_ in (("unfused", "fused"), ("fused", "auto"), ("library_gemm_scheme_a", "auto")):
+                    ratio = t[a_]["median_us"] / t[b_]["median_us"]
+                    apart = t[a_]["min_us"] > t[b_]["max_us"] or t[b_]["min_us"] > t[a_]["max_us"]
+                    r[f"{a_}_over_{b_}"] = {"ratio": round(ratio, 3), "significant": apart}
                 out["shapes"].append(r)
-                log(f"selection M={M} N={N}: fused {r['fused_us']} us, unfused {r['unfused_us']} us, "
-                    f"auto ({r['auto_splits']} splits) {r['auto_us']} us, "
-                    f"library-GEMM scheme A {r['library_gemm_scheme_a_us']} us")
+                log(f"selection M={M} N={N}: " + ", ".join(f"{k} {v['median_us']} ({v['min_us']}..{v['max_us']})"
+                                                          for k, v in t.items()) + f" us; {r['auto_splits']} splits")
                 del ws, wsa
     return out
 
@@ -716,6 +809,8 @@ def main():
     ap.add_argument("--dispatch-count", type=int, default=3)
     ap.add_argument("--counters-rows", action="store_true",
                     help="the same for the other rows of the path (their fused and unfused kernels)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only the size sweep of fused Add+LayerNorm and the copy (fixed cost and streaming rate)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): the fused row kernels are "
@@ -737,6 +832,9 @@ def main():
         return
     if a.dispatch:
         dispatch_only(torch, api, synth, a.dispatch, a.dispatch_count)
+        return
+    if a.sweep:
+        print(json.dumps({"size_sweep": size_sweep(torch, api, synth, roofline)}), flush=True)
         return
     h = headline(torch, api, synth, roofline, a.steps, a.warmup)
     log(f"headline: {h['avg_launch_us']:.2f} us/launch, value {h['value_gbps']:.0f} GB/s")
