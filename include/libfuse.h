@@ -57,7 +57,17 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enumerations below are passed by value across the ABI, where a caller may pass any int.
+ * Compiled as C++ they get int as their fixed underlying type, so that every int a caller passes
+ * is a value of the type (validation then rejects the ones that name nothing); in C an
+ * enumeration is an int already. */
+#ifdef __cplusplus
+#define FUSE_ENUM_BASE : int
+#else
+#define FUSE_ENUM_BASE
+#endif
+
+typedef enum fuse_status_e FUSE_ENUM_BASE {
     FUSE_OK = 0,
     FUSE_ERR_NULL_PTR = 1,    /* a required pointer is NULL */
     FUSE_ERR_BAD_SHAPE = 2,   /* a size is negative, zero where it must be positive, or too big */
@@ -70,7 +80,7 @@ typedef enum {
     FUSE_ERR_HIP = 9          /* the HIP runtime reported an error at launch */
 } fuse_status_t;
 
-typedef enum { FUSE_F32 = 0, FUSE_F16 = 1, FUSE_BF16 = 2 } fuse_dtype_t;
+typedef enum fuse_dtype_e FUSE_ENUM_BASE { FUSE_F32 = 0, FUSE_F16 = 1, FUSE_BF16 = 2 } fuse_dtype_t;
 
 /* Longest row the register-resident row kernels accept (elements). */
 #define FUSE_MAX_HIDDEN 16384
@@ -195,7 +205,7 @@ fuse_status_t fuse_swiglu_dualgemm(const void *a, const void *b1, const void *b2
  *   chain) or FUSE_ACT_SILU; another value is FUSE_ERR_BAD_VALUE.
  * M >= 0, N >= 1, K >= 1, each below 2^31; K or N above 2^21 is FUSE_ERR_UNSUPPORTED.
  */
-typedef enum { FUSE_ACT_NONE = 0, FUSE_ACT_RELU = 1, FUSE_ACT_GELU = 2, FUSE_ACT_SILU = 3 } fuse_act_t;
+typedef enum fuse_act_e FUSE_ENUM_BASE { FUSE_ACT_NONE = 0, FUSE_ACT_RELU = 1, FUSE_ACT_GELU = 2, FUSE_ACT_SILU = 3 } fuse_act_t;
 fuse_status_t fuse_gemm_bias_act(const void *x, const void *w, const void *bias, void *y, int64_t M,
                                  int64_t N, int64_t K, fuse_act_t act, fuse_dtype_t dtype,
                                  void *stream);
@@ -213,7 +223,7 @@ fuse_status_t fuse_gemm_bias_act(const void *x, const void *w, const void *bias,
  * The workspace is caller-owned device memory of at least fuse_unfused_workspace_bytes()
  * bytes (256-byte aligned), not overlapping any argument.  `op` selects the operation:
  */
-typedef enum {
+typedef enum fuse_op_e FUSE_ENUM_BASE {
     FUSE_OP_ADD_LAYERNORM = 0,
     FUSE_OP_BIAS_GELU_RESIDUAL = 1,
     FUSE_OP_SOFTMAX_ROWS = 2,
@@ -282,6 +292,7 @@ fuse_status_t fuse_gemm_bias_act_auto(const void *x, const void *w, const void *
                                       int64_t M, int64_t N, int64_t K, fuse_act_t act,
                                       fuse_dtype_t dtype, void *workspace, size_t workspace_bytes,
                                       void *stream);
+
 
 /*
  * Plain device-to-device copy of `bytes` bytes, the calibration kernel of the roofline: its

@@ -11,6 +11,9 @@
     python -m memory_bound_amd.profsum hbm    <fetch.db> <write.db>
         # bytes moved per dispatch from a FETCH_SIZE run and a WRITE_SIZE run of the same
         # program, each counter scaled by what it reads for the plain copy of 24 MiB in that run
+    python -m memory_bound_amd.profsum sweep  <results.db>
+        # a `bench.py --sweep` run: Add+LayerNorm and copy kernel medians per size, and the line
+        # t = t0 + bytes / bw fitted to each
     python -m memory_bound_amd.profsum split  <results.db> <kernel> <grid> <n>
         # one kernel at one grid size: its first n dispatches and the rest, apart (a benchmark
         # that times the same kernel first on rotating cold buffers, then on one hot buffer set)
@@ -129,6 +132,44 @@ def pmc(db_path: str) -> list[dict]:
     return out
 
 
+SWEEP_ROWS, SWEEP_HIDDEN = (512, 1024, 2048, 4096, 8192, 16384, 32768), 4096
+
+
+def sweep(db_path: str, skip: int = 3) -> dict:
+    """Kernel durations of a `bench.py --sweep` run: for each size in turn, its Add+LayerNorm
+    dispatches, then its copy dispatches (the first `skip` of each, eager warm-up launches,
+    dropped).  Groups are runs of consecutive dispatches of one kernel at one grid.  Each size's
+    median and a least-squares line t = t0 + bytes / bw per kernel (fp16 at H = 4096: 3 row
+    tensors plus gamma and beta for Add+LayerNorm, the same 3 tensors' bytes for the copy)."""
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select name, grid_x, duration from kernels order by start").fetchall()
+    groups = []
+    for name, gx, dur in rows:
+        n = short_name(name)
+        if not (n.startswith("add_layernorm_kernel") or n.startswith("copy16_kernel")):
+            continue
+        if not groups or groups[-1][0] != (n, gx):
+            groups.append(((n, gx), []))
+        groups[-1][1].append(dur / 1e3)
+    if len(groups) != 2 * len(SWEEP_ROWS):
+        raise SystemExit(f"expected {2 * len(SWEEP_ROWS)} groups (Add+LN, copy per size), found {len(groups)}")
+    sizes = []
+    for i, r in enumerate(SWEEP_ROWS):
+        (ln_k, ln_g), ln_d = groups[2 * i]
+        (cp_k, cp_g), cp_d = groups[2 * i + 1]
+        t = 3 * r * SWEEP_HIDDEN * 2
+        sizes.append({"rows": r, "bytes": t + 2 * SWEEP_HIDDEN * 2, "copy_bytes": t, "ln_kernel": ln_k,
+                      "ln_grid": ln_g, "ln": _stats(ln_d[skip:]), "copy": _stats(cp_d[skip:])})
+    fits = {}
+    for key, bkey in (("ln", "bytes"), ("copy", "copy_bytes")):
+        xs = [s[bkey] for s in sizes]
+        ys = [s[key]["median_us"] for s in sizes]
+        mx, my = statistics.mean(xs), statistics.mean(ys)
+        b = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sum((x - mx) ** 2 for x in xs)
+        fits[key] = {"t0_us": my - b * mx, "bw_gbps": 1e-3 / b}
+    return {"sizes": sizes, "fits": fits}
+
+
 def main(argv):
     mode, path = argv[1], argv[2]
     if mode == "trace":
@@ -166,6 +207,20 @@ def main(argv):
         for r in rows:
             print(f"{r['kernel'][:64]:64s} {r['grid']:9d} {r['fetch_kib']:11.2f} {r['write_kib']:11.2f} "
                   f"{r['bytes']:12.0f}")
+    elif mode == "sweep":
+        r = sweep(path)
+        print(f"{'rows':>6s} {'MB_moved':>9s} {'addln_med_us':>12s} {'p10':>7s} {'p90':>7s} {'frac':>6s} "
+              f"{'copy_med_us':>11s} {'p10':>7s} {'p90':>7s} {'frac':>6s}  kernel")
+        for z in r["sizes"]:
+            ln, cp = z["ln"], z["copy"]
+            print(f"{z['rows']:6d} {z['bytes'] / 1e6:9.2f} {ln['median_us']:12.3f} {ln['p10_us']:7.3f} "
+                  f"{ln['p90_us']:7.3f} {z['bytes'] / (ln['median_us'] * 1e-6) / 8e12:6.3f} {cp['median_us']:11.3f} "
+                  f"{cp['p10_us']:7.3f} {cp['p90_us']:7.3f} {z['copy_bytes'] / (cp['median_us'] * 1e-6) / 8e12:6.3f}  "
+                  f"{z['ln_kernel']} grid {z['ln_grid']}")
+        for k, f in r["fits"].items():
+            name = "Add+LayerNorm" if k == "ln" else "copy"
+            print(f"fit {name:13s} t = {f['t0_us']:.3f} us + bytes / {f['bw_gbps']:.1f} GB/s "
+                  f"({f['bw_gbps'] / 8000:.3f} of 8 TB/s)")
     elif mode == "split":
         head, rest = split(path, argv[3], int(argv[4]), int(argv[5]))
         for label, r in (("first", head), ("rest", rest)):

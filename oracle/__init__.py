@@ -33,6 +33,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB names another build of oracle.c to load instead (the sanitizer test runs the pins
+# against an AddressSanitizer / UndefinedBehaviorSanitizer build this way)
+_LIB_OVERRIDE = os.environ.get("ORACLE_LIB")
 _lib = None
 
 GCC_CMD = [
@@ -52,9 +55,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
     dp = ctypes.POINTER(ctypes.c_double)
     i64 = ctypes.c_int64
     lib.oracle_add_layernorm.argtypes = [dp, dp, dp, dp, dp, i64, i64, ctypes.c_double]
