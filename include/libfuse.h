@@ -293,6 +293,24 @@ fuse_status_t fuse_gemm_bias_act_auto(const void *x, const void *w, const void *
                                       fuse_dtype_t dtype, void *workspace, size_t workspace_bytes,
                                       void *stream);
 
+/*
+ * Allocation-free form of fuse_swiglu_auto, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments without the workspace, same plan, same kernels and the same result bit for bit.
+ * When the plan splits K, the fp32 partial products go to a fixed array inside the library of
+ * FUSE_NOALLOC_SCRATCH_BYTES (64 MiB) per device, which each device the library runs on holds
+ * from the first call there until the process ends; on a device of up to 256 CUs every plan
+ * fits.  A plan that needs more returns FUSE_ERR_WORKSPACE with nothing launched.  The call
+ * allocates nothing (the array's device address is looked up once per device, on the first
+ * call there).  Every call on one device shares that device's array: calls that overlap on a
+ * device (on two streams, or from two threads) race on it and must be serialised by the
+ * caller.  Nothing in the array needs clearing between calls.  Validation and other errors as
+ * fuse_swiglu_dualgemm.
+ */
+#define FUSE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+fuse_status_t fuse_swiglu_auto_noalloc(const void *a, const void *b1, const void *b2, void *out,
+                                       int64_t M, int64_t N, int64_t K, fuse_dtype_t dtype,
+                                       void *stream);
 
 /*
  * Plain device-to-device copy of `bytes` bytes, the calibration kernel of the roofline: its

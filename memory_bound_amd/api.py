@@ -34,6 +34,7 @@ EXPORTS = [
     "fuse_add_layernorm", "fuse_add_layernorm_ex", "fuse_bias_gelu_residual", "fuse_softmax_rows",
     "fuse_cumsum_scale_rows", "fuse_swiglu_dualgemm", "fuse_gemm_bias_act", "fuse_unfused_gemm_bias_act",
     "fuse_auto_splits", "fuse_auto_workspace_bytes", "fuse_swiglu_auto", "fuse_gemm_bias_act_auto",
+    "fuse_swiglu_auto_noalloc",
     "fuse_unfused_workspace_bytes", "fuse_unfused_add_layernorm", "fuse_unfused_bias_gelu_residual",
     "fuse_unfused_softmax_rows", "fuse_unfused_cumsum_scale_rows", "fuse_unfused_swiglu", "fuse_copy", "fuse_empty_kernels",
     "fuse_status_string", "fuse_last_hip_error", "fuse_version",
@@ -73,6 +74,7 @@ def load() -> ctypes.CDLL:
         "fuse_swiglu_dualgemm": [vp, vp, vp, vp, i64, i64, i64, i32, vp],
         "fuse_gemm_bias_act": [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp],
         "fuse_swiglu_auto": [vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp],
+        "fuse_swiglu_auto_noalloc": [vp, vp, vp, vp, i64, i64, i64, i32, vp],
         "fuse_gemm_bias_act_auto": [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp],
         "fuse_auto_splits": [i32, i64, i64, i64],
         "fuse_unfused_gemm_bias_act": [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp],
@@ -311,6 +313,22 @@ def fuse_swiglu_auto(a, b1, b2, out=None, workspace=None, stream=None):
     ws = workspace or _auto_workspace(FUSE_OP_SWIGLU, M, N, K, a.device, stream)
     _ok(load().fuse_swiglu_auto(_ptr(a), _ptr(b1), _ptr(b2), _ptr(out), M, N, K, _dt(a), ws[1], ws[2],
                                 _stream(stream)), "fuse_swiglu_auto")
+    return out
+
+
+def fuse_swiglu_auto_noalloc(a, b1, b2, out=None, stream=None):
+    """fuse_swiglu_auto without a workspace: the split-K partials go to the library's fixed
+    per-device array (calls that overlap on one device race on it)."""
+    M, K = a.shape
+    N = b1.shape[1]
+    _check(a, "a")
+    _check(b1, "b1", a.dtype, (K, N))
+    _check(b2, "b2", a.dtype, (K, N))
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    _check(out, "out", a.dtype, (M, N))
+    _ok(load().fuse_swiglu_auto_noalloc(_ptr(a), _ptr(b1), _ptr(b2), _ptr(out), M, N, K, _dt(a), _stream(stream)),
+        "fuse_swiglu_auto_noalloc")
     return out
 
 

@@ -400,6 +400,17 @@ fuse_status_t fuse_swiglu_auto(const void* a, const void* b1, const void* b2, vo
     return hip_status(fuse::launch_swiglu_auto(a, b1, b2, out, (int)M, (int)N, (int)K, ws, (hipStream_t)stream));
 }
 
+static_assert(FUSE_NOALLOC_SCRATCH_BYTES == fuse::SWIGLU_NOALLOC_SCRATCH_BYTES, "header and library agree");
+
+fuse_status_t fuse_swiglu_auto_noalloc(const void* a, const void* b1, const void* b2, void* out, int64_t M,
+                                       int64_t N, int64_t K, fuse_dtype_t dt, void* stream) {
+    fuse_status_t st = check_swiglu(a, b1, b2, out, M, N, K, dt);
+    if (st != FUSE_OK || M == 0) return st;
+    if (fuse::swiglu_noalloc_need((int)M, (int)N, (int)K, a, b1, b2, out) > FUSE_NOALLOC_SCRATCH_BYTES)
+        return FUSE_ERR_WORKSPACE;
+    return hip_status(fuse::launch_swiglu_auto_noalloc(a, b1, b2, out, (int)M, (int)N, (int)K, (hipStream_t)stream));
+}
+
 fuse_status_t fuse_gemm_bias_act_auto(const void* x, const void* w, const void* bias, void* y, int64_t M, int64_t N,
                                       int64_t K, fuse_act_t act, fuse_dtype_t dt, void* ws, size_t ws_bytes,
                                       void* stream) {

@@ -59,6 +59,12 @@ hipError_t launch_swiglu_auto(const void* a, const void* b1, const void* b2, voi
                               void* ws, hipStream_t stream);
 hipError_t launch_gemm_bias_act_auto(const void* x, const void* w, const void* bias, void* y, int M, int N, int K,
                                      int act, void* ws, hipStream_t stream);
+// Allocation-free form of launch_swiglu_auto: split-K partials in a fixed per-device array of
+// SWIGLU_NOALLOC_SCRATCH_BYTES; swiglu_noalloc_need gives the bytes a shape's plan needs (0: no split).
+constexpr size_t SWIGLU_NOALLOC_SCRATCH_BYTES = size_t(64) << 20;
+size_t swiglu_noalloc_need(int M, int N, int K, const void* a, const void* b1, const void* b2, const void* out);
+hipError_t launch_swiglu_auto_noalloc(const void* a, const void* b1, const void* b2, void* out, int M, int N, int K,
+                                      hipStream_t stream);
 hipError_t launch_gemm_bias_act_unfused(const void* x, const void* w, const void* bias, void* y, int M, int N,
                                         int K, int act, void* c, void* t, hipStream_t stream);
 

@@ -35,6 +35,7 @@
 #include <stdlib.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "launch.hpp"
 #include "stream_kernels.hpp"
@@ -956,6 +957,67 @@ hipError_t launch_swiglu_auto(const void* a, const void* b1, const void* b2, voi
     DualArgs p = dual_args(a, b1, b2, M, N, K);
     p.out = (uint16_t*)out;
     return launch_split<MODE_PART_DUAL, ACT_NONE>(p, BN, sp, (float*)ws, stream);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Allocation-free split-K SwiGLU, for callers that cannot allocate device memory.  The fp32 partial
+// products go to `scratch`, a fixed array of the library, instead of a caller workspace.  Its size
+// covers every split plan on a device of up to 256 CUs: the plan splits only when the tiles fill
+// less than a quarter of the CUs and keeps tiles x splits at most one workgroup per CU, each
+// holding two fp32 planes of a 256 x 128 tile (256 KiB), so 256 CUs need at most 64 MiB.  Each
+// device holds its own copy from the first call on it until the process ends.  Every call on a
+// device shares that copy, so calls that overlap on one device (two streams, two threads) race
+// on it.  Every partial a launch reads is written earlier in the same launch, so nothing needs
+// clearing between calls.
+// ------------------------------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[SWIGLU_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> scratch_addr[MAX_DEVICES];
+std::mutex scratch_mu;
+
+// Device address of `scratch` on the current device, looked up once per device.  The array's
+// name in host code is only a stand-in for the symbol; this address is what kernels get.
+hipError_t scratch_on_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    void* p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        p = scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+}  // namespace
+
+size_t swiglu_noalloc_need(int M, int N, int K, const void* a, const void* b1, const void* b2, const void* out) {
+    size_t need = 0;
+    swiglu_auto_splits(M, N, K, a, b1, b2, out, &need);
+    return need;
+}
+
+hipError_t launch_swiglu_auto_noalloc(const void* a, const void* b1, const void* b2, void* out, int M, int N, int K,
+                                      hipStream_t stream) {
+    const SplitPlan sp =
+        split_plan(M, N, K, BN, aligned_args(a, b1, N, K) && ((((uintptr_t)b2) | (uintptr_t)out) & 15u) == 0);
+    if (sp.splits < 2) return launch_swiglu(a, b1, b2, out, M, N, K, stream);
+    if (split_bytes(sp, M, N, 2) > SWIGLU_NOALLOC_SCRATCH_BYTES) return hipErrorInvalidValue;  // checked by the caller
+    void* part = nullptr;
+    const hipError_t e = scratch_on_current_device(&part);
+    if (e != hipSuccess) return e;
+    DualArgs p = dual_args(a, b1, b2, M, N, K);
+    p.out = (uint16_t*)out;
+    return launch_split<MODE_PART_DUAL, ACT_NONE>(p, BN, sp, (float*)part, stream);
 }
 
 hipError_t launch_gemm_bias_act_auto(const void* x, const void* w, const void* bias, void* y, int M, int N, int K,

@@ -282,6 +282,24 @@ def test_auto_plan_and_validation(lib):
     assert gm(4 * Q, 1 << 24) == WS             # overlaps y
 
 
+def test_swiglu_noalloc_validation(lib, monkeypatch):
+    SW = 3
+    Q = 16 * P
+    def call(a=Q, M=256, N=512, K=1536, dt=BF16):
+        return lib.fuse_swiglu_auto_noalloc(v(a), v(2 * Q), v(3 * Q), v(4 * Q), M, N, K, dt, None)
+    assert call(dt=F16) == DTYPE
+    assert call(a=0) == NULL
+    assert call(M=0) == OK                      # no-op
+    assert call(M=0, a=0) == OK
+    assert call(K=(1 << 21) + 1) == UNSUP
+    assert call(a=Q + 1) == MISAL
+    # a plan whose partials exceed the fixed 64 MiB array is refused before anything is launched
+    monkeypatch.setenv("FUSE_SPLITK", "48")
+    assert lib.fuse_auto_workspace_bytes(SW, 1024, 1024, 1536, BF16) == 48 * 2 * 1024 * 1024 * 4
+    Q2 = 64 * P
+    assert lib.fuse_swiglu_auto_noalloc(v(Q2), v(2 * Q2), v(3 * Q2), v(4 * Q2), 1024, 1024, 1536, BF16, None) == WS
+
+
 def test_unfused_workspace_bytes(lib):
     f = lib.fuse_unfused_workspace_bytes
     t = 2048 * 4096 * 2
@@ -375,6 +393,7 @@ def _binding_cases():
         ("fuse_cumsum_scale_rows", row, {}),
         ("fuse_swiglu_dualgemm", sw, {}),
         ("fuse_swiglu_auto", sw, {"workspace": (None, None, 0)}),
+        ("fuse_swiglu_auto_noalloc", sw, {}),
         ("fuse_gemm_bias_act", gm, {}),
         ("fuse_gemm_bias_act_auto", gm, {"workspace": (None, None, 0)}),
         ("fuse_unfused_add_layernorm", ln, {"workspace": (None, None, 0)}),
