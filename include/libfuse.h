@@ -41,7 +41,8 @@
  *    tolerance:
  *    FUSE_ROW_WPR (waves per row: 1, 2, 4, 8), FUSE_ROW_STEPS (row blocks per workgroup: 1, 2,
  *    4), FUSE_EW_CHUNKS (16-byte chunks per thread of the streaming kernels: 1, 2, 4, 8),
- *    FUSE_SWIGLU_STAGES (LDS ring depth of the dual-product kernels: 3, 4, 5),
+ *    FUSE_SWIGLU_STAGES (LDS ring depth of the dual-product kernels: 3, 4, 5; depths other
+ *    than the default 4 run one workgroup per tile),
  *    FUSE_SWIGLU_TAIL (last-round slices: 0 off, 2 halves only), FUSE_SWIGLU_PERSIST (0: one
  *    workgroup per tile instead of one per CU walking its tiles), FUSE_SWIGLU_GENERAL (any
  *    value: the general dual-product kernel for every shape), FUSE_SPLITK (K splits of the

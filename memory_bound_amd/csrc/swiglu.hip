@@ -627,8 +627,14 @@ __device__ __forceinline__ void direct_tile(const DualArgs& p, char* lds, int m0
     const int N = p.N, K = p.K;
     using C = DirectCfgT<TM>;
     constexpr int LPS = C::LOADS_PER_STAGE, WMT = C::WMT;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // The thread index passes through an empty asm statement, so everything derived from it (the
+    // per-lane load, fragment and store offsets) is formed again for each tile.  Otherwise, when
+    // one workgroup walks several tiles, those values are hoisted out of its tile loop and held
+    // across it, and with the accumulators in the AGPRs that spills VGPRs to scratch.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
     floatx16 acc1[WMT][WN], acc2[WMT][WN];
@@ -845,11 +851,10 @@ hipError_t launch(DualArgs p, int tile_cols, hipStream_t stream) {
     p.units = p.tiles_m * p.tiles_n + (tp.parts - 1) * tp.tail;
     const dim3 grid((unsigned)p.units), block(THREADS);
     const int cus = cu_count(), g = cus >= NUM_XCD ? cus / NUM_XCD * NUM_XCD : cus;
-    if (st != 0 && persistent() && p.units > g) {
-        const dim3 pg((unsigned)g);
-        if (st == 3) hipLaunchKernelGGL((swiglu_persist_kernel<3, MODE>), pg, block, 0, stream, p);
-        else if (st == 5) hipLaunchKernelGGL((swiglu_persist_kernel<5, MODE>), pg, block, 0, stream, p);
-        else hipLaunchKernelGGL((swiglu_persist_kernel<4, MODE>), pg, block, 0, stream, p);
+    // the persistent kernel with the default ring only; the other ring depths (tuning sweeps)
+    // run one workgroup per unit
+    if (st == 4 && persistent() && p.units > g) {
+        hipLaunchKernelGGL((swiglu_persist_kernel<4, MODE>), dim3((unsigned)g), block, 0, stream, p);
         return hipGetLastError();
     }
     if (st == 3) hipLaunchKernelGGL((swiglu_direct_kernel<3, MODE>), grid, block, 0, stream, p);
