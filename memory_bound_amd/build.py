@@ -46,6 +46,23 @@ def _compile(src: str) -> tuple[str, str]:
     return obj, p.stderr
 
 
+def resource_table(path: str | None = None) -> dict[str, dict[str, int]]:
+    """Per kernel (mangled name): the compiler's resource figures from the report of the last
+    build -- VGPRs, AGPRs, SGPRs, spilled VGPRs / SGPRs and scratch bytes per lane."""
+    path = path or os.path.join(BUILD, "resource_usage.txt")
+    table, cur = {}, None
+    for line in open(path):
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            table[cur] = {}
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+(?:\[bytes/lane\])?): (\d+)", line)
+        if m and cur:
+            table[cur][m.group(1).strip()] = int(m.group(2))
+    return table
+
+
 def build(jobs: int | None = None, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
