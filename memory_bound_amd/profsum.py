@@ -14,6 +14,9 @@
     python -m memory_bound_amd.profsum sweep  <results.db>
         # a `bench.py --sweep` run: Add+LayerNorm and copy kernel medians per size, and the line
         # t = t0 + bytes / bw fitted to each
+    python -m memory_bound_amd.profsum headline <results.db> <n_cold>
+        # the headline kernel in a trace of the default benchmark: its first n_cold (cold)
+        # dispatches as `key: value` lines that bench.py reads back, with the source hash
     python -m memory_bound_amd.profsum split  <results.db> <kernel> <grid> <n>
         # one kernel at one grid size: its first n dispatches and the rest, apart (a benchmark
         # that times the same kernel first on rotating cold buffers, then on one hot buffer set)
@@ -132,6 +135,43 @@ def pmc(db_path: str) -> list[dict]:
     return out
 
 
+HEADLINE_SOURCES = ["fuse_common.hpp", "row_plan.hpp", "row_plan.hip", "row_kernels.hpp", "row_launch.hpp"]
+HEADLINE_KERNEL, HEADLINE_GRID = "add_layernorm_kernel<1, true, 2, 4, true, 4>", 131072
+
+
+def source_hash(files=HEADLINE_SOURCES) -> str:
+    """sha256 prefix of the kernel sources a profile was taken with (memory_bound_amd/csrc)."""
+    import hashlib
+    import os
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_profile(path: str) -> dict | None:
+    """The `key: value` lines of a committed profile summary, or None when the file is missing or
+    the kernel sources changed since it was taken (its kernel_source_sha256)."""
+    import os
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#") and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip().split()[0] if v.strip() else ""
+    return kv if kv.get("kernel_source_sha256") == source_hash() else None
+
+
+def headline(db_path: str, cold: int) -> dict:
+    """The headline kernel's first `cold` dispatches in a trace of the default benchmark (the
+    eager, warm-up and timed launches, each on a buffer set not touched for 1 GiB)."""
+    head, rest = split(db_path, HEADLINE_KERNEL, HEADLINE_GRID, cold)
+    return {"cold": head, "hot": rest}
+
+
 SWEEP_ROWS, SWEEP_HIDDEN = (512, 1024, 2048, 4096, 8192, 16384, 32768), 4096
 
 
@@ -221,6 +261,17 @@ def main(argv):
             name = "Add+LayerNorm" if k == "ln" else "copy"
             print(f"fit {name:13s} t = {f['t0_us']:.3f} us + bytes / {f['bw_gbps']:.1f} GB/s "
                   f"({f['bw_gbps'] / 8000:.3f} of 8 TB/s)")
+    elif mode == "headline":
+        r = headline(path, int(argv[3]))
+        c = r["cold"]
+        print(f"kernel: {HEADLINE_KERNEL} grid {HEADLINE_GRID}")
+        print(f"kernel_source_sha256: {source_hash()}")
+        print(f"cold_dispatches: {c['calls']}")
+        for k in ("mean", "median", "p10", "p90", "min", "max"):
+            print(f"cold_{k}_us: {c[k + '_us']:.3f}")
+        if r["hot"]:
+            print(f"hot_dispatches: {r['hot']['calls']}")
+            print(f"hot_mean_us: {r['hot']['mean_us']:.3f}")
     elif mode == "split":
         head, rest = split(path, argv[3], int(argv[4]), int(argv[5]))
         for label, r in (("first", head), ("rest", rest)):
