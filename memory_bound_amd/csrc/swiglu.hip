@@ -702,6 +702,22 @@ __device__ __forceinline__ void direct_tile(const DualArgs& p, char* lds, int m0
 // spread over more of them.  One workgroup per unit, or, with more units than CUs, a grid of one
 // workgroup per CU (rounded down to a multiple of 8) walking units b, b + grid, ..., so that unit u
 // still runs on XCD u % 8, the one the tile map assumes.
+// Last-round slice q (of tail tiles cut in P row slices each): its tile among the tail tiles and
+// its part.  When the tail is a whole number of groups of 8 tiles, the P slices of a tile are 8
+// units apart, so they run on one XCD (unit u runs on XCD u % 8) and its L2 fetches the tile's b
+// columns once for all of them instead of once per slice; otherwise the slices of a tile are
+// consecutive units.  Each slice still sums every k in the same order: results do not change.
+struct Slice {
+    int tile, part;
+};
+template <int P> __device__ __forceinline__ Slice slice_of(int q, int tail) {
+    if (tail % NUM_XCD == 0) {
+        constexpr int G = NUM_XCD * P;  // units of one group of 8 tiles
+        return {(q / G) * NUM_XCD + q % NUM_XCD, (q / NUM_XCD) % P};
+    }
+    return {q / P, q % P};
+}
+
 // Work unit `bid` of the full-tile kernel, in the ring `lds`.
 template <int S, int MODE>
 __device__ __forceinline__ void direct_unit(const DualArgs& p, char* lds, int bid) {
@@ -714,13 +730,13 @@ __device__ __forceinline__ void direct_unit(const DualArgs& p, char* lds, int bi
         const int kt0 = split * p.ksteps;
         direct_tile<BM, S, MODE>(p, lds, tile.m0, tile.n0, kt0, min(p.ksteps, kt_all - kt0), split);
     } else if (p.parts == 2) {
-        const int q = bid - head;
-        const Tile tile = tile_of(head + (q >> 1), p.tiles_m, p.tiles_n, p.bn_step);
-        direct_tile<BM / 2, S, MODE>(p, lds, tile.m0 + (BM / 2) * (q & 1), tile.n0, 0, kt_all, 0);
+        const Slice sl = slice_of<2>(bid - head, p.tail);
+        const Tile tile = tile_of(head + sl.tile, p.tiles_m, p.tiles_n, p.bn_step);
+        direct_tile<BM / 2, S, MODE>(p, lds, tile.m0 + (BM / 2) * sl.part, tile.n0, 0, kt_all, 0);
     } else {
-        const int q = bid - head;
-        const Tile tile = tile_of(head + (q >> 2), p.tiles_m, p.tiles_n, p.bn_step);
-        direct_tile<BM / 4, S, MODE>(p, lds, tile.m0 + (BM / 4) * (q & 3), tile.n0, 0, kt_all, 0);
+        const Slice sl = slice_of<4>(bid - head, p.tail);
+        const Tile tile = tile_of(head + sl.tile, p.tiles_m, p.tiles_n, p.bn_step);
+        direct_tile<BM / 4, S, MODE>(p, lds, tile.m0 + (BM / 4) * sl.part, tile.n0, 0, kt_all, 0);
     }
 }
 
