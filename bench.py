@@ -214,6 +214,13 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
         out[name] = r
         log(f"{name}: {us:.2f} us")
 
+    def of_ceiling(name, ceiling):
+        # the row against what the matrix cores sustain with no memory traffic at all
+        r = out[name]
+        r["frac_of_mfma_ceiling"] = {
+            "single_dispatch": round(r["single_dispatch_tflops"] / ceiling["single_dispatch_tflops"], 4),
+            "back_to_back": round(r["achieved_tflops"] / ceiling["achieved_tflops"], 4)}
+
     with torch.cuda.stream(stream):
         # headline shape, unfused
         w = synth.WORKLOADS[HEADLINE]
@@ -338,6 +345,9 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
         record("softmax_unfused_f16_65536x2048", w.op, w.shape, w.dtype, False, ev, n_launch // 2)
         del sets, ws
 
+        ceiling = mfma_ceiling(torch, api, stream, roofline, n_launch // 2)
+        out["mfma_ceiling"] = ceiling
+
         w = synth.WORKLOADS["swiglu_bf16_2048x8960x1536"]
         d = w.inputs()
         a, b1, b2 = d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda()
@@ -355,6 +365,7 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
         _, ev = time_launches(torch, stream, sw, n_launch // 2)
         record("swiglu_bf16_2048x8960x1536", w.op, w.shape, w.dtype, True, ev, n_launch // 2,
                single_dispatch(one, roofline.workload_work(w.op, w.shape, w.dtype, True)))
+        of_ceiling("swiglu_bf16_2048x8960x1536", ceiling)
         _, ev = time_launches(torch, stream, sw_unf, n_launch // 2)
         record("swiglu_unfused_bf16_2048x8960x1536", w.op, w.shape, w.dtype, False, ev, n_launch // 2)
         del ws
@@ -379,6 +390,7 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
         _, ev = time_launches(torch, stream, gm, n_launch // 2)
         record("gemm_bias_relu_bf16_2048x8960x1536", w.op, w.shape, w.dtype, True, ev, n_launch // 2,
                single_dispatch(one, roofline.workload_work(w.op, w.shape, w.dtype, True)))
+        of_ceiling("gemm_bias_relu_bf16_2048x8960x1536", ceiling)
         _, ev = time_launches(torch, stream, gm_unf, n_launch // 2)
         record("gemm_bias_relu_unfused_bf16_2048x8960x1536", w.op, w.shape, w.dtype, False, ev, n_launch // 2,
                {"note": "GEMM kernel, bias kernel, ReLU kernel"})
@@ -424,6 +436,34 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
         log(f"copy 512 MiB: {us:.2f} us {gb:.0f} GB/s")
         del bufs
     return out
+
+
+def mfma_ceiling(torch, api, stream, roofline, n_launch, iters=448):
+    """The matrix-core calibration kernel (bf16 32x32x16 MFMAs from registers, two workgroups of
+    four waves per CU) sized to run about as long as the SwiGLU workload, timed the two ways the
+    matrix-core rows are: one synchronised dispatch at a time, and back to back."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs = 2 * cus
+    flops = wgs * 4 * iters * 8 * 32768
+    res = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+
+    def run(i):
+        api.fuse_mfma_ceiling(wgs, iters, res)
+    for i in range(3):
+        run(i)
+    one = single_dispatch_us(torch, stream, run)
+    _, ev = time_launches(torch, stream, run, n_launch)
+    us = ev * 1e3 / n_launch
+    peak = roofline.MFMA_PEAK_TFLOPS["bf16"]
+    tf1, tf = flops / (one * 1e-6) / 1e12, flops / (us * 1e-6) / 1e12
+    log(f"mfma ceiling: {one:.2f} us single ({tf1:.0f} TFLOP/s), {us:.2f} us back to back ({tf:.0f} TFLOP/s)")
+    return {"workgroups": wgs, "iters": iters, "flops": flops,
+            "single_dispatch_us": round(one, 3), "single_dispatch_tflops": round(tf1, 1),
+            "avg_launch_us": round(us, 3), "achieved_tflops": round(tf, 1),
+            "frac_of_peak": {"single_dispatch": round(tf1 / peak, 4), "back_to_back": round(tf / peak, 4)},
+            "note": "fuse_mfma_ceiling: only bf16 matrix-core instructions, operands in registers, no memory "
+                    "traffic; the rate the matrix cores sustain on this part, against which the matrix-core "
+                    "rows' frac_of_mfma_ceiling is taken (their roofline frac stays against the spec peak)"}
 
 
 SWEEP_ROWS = (512, 1024, 2048, 4096, 8192, 16384, 32768)

@@ -322,6 +322,21 @@ fuse_status_t fuse_swiglu_auto_noalloc(const void *a, const void *b1, const void
 fuse_status_t fuse_copy(const void *src, void *dst, size_t bytes, void *stream);
 
 /*
+ * Matrix-core calibration kernel ([P4] 核心差异分析 §1 and 对比总结表 place the fused dual GEMM
+ * near the compute peak; this measures the peak the matrix cores actually sustain): each of
+ * `workgroups` workgroups of 256 threads (4 waves, up to 2 workgroups resident per CU) runs
+ * `iters` rounds of 8 independent v_mfma_f32_32x32x16_bf16 per wave, operands in registers and
+ * no memory traffic in the loop -- the instruction the dual-product kernels issue.  Work per
+ * call: workgroups * 4 * iters * 8 * 32768 flops.  Thread t of workgroup b writes the sum of its
+ * accumulators, 2048 * iters exactly for iters <= 8192 (every operand is 1), to
+ * out[256 b + t] (fp32, 4-byte aligned, workgroups * 256 values).
+ * 1 <= workgroups <= FUSE_MAX_CEILING_WORKGROUPS, 1 <= iters <= FUSE_MAX_CEILING_ITERS.
+ */
+#define FUSE_MAX_CEILING_WORKGROUPS 65536
+#define FUSE_MAX_CEILING_ITERS (1 << 24)
+fuse_status_t fuse_mfma_ceiling(int64_t workgroups, int64_t iters, void *out, void *stream);
+
+/*
  * Launch-cost probe ([P2] §4.5 and [P3] §2 argue that per-launch cost, not only traffic, is what
  * fusion and graph capture remove): enqueues `count` launches of a kernel that does nothing (one
  * 64-thread workgroup each) on `stream`, from a plain loop inside the library, so the host cost

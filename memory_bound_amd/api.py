@@ -37,6 +37,7 @@ EXPORTS = [
     "fuse_swiglu_auto_noalloc",
     "fuse_unfused_workspace_bytes", "fuse_unfused_add_layernorm", "fuse_unfused_bias_gelu_residual",
     "fuse_unfused_softmax_rows", "fuse_unfused_cumsum_scale_rows", "fuse_unfused_swiglu", "fuse_copy", "fuse_empty_kernels",
+    "fuse_mfma_ceiling",
     "fuse_status_string", "fuse_last_hip_error", "fuse_version",
 ]
 
@@ -84,6 +85,7 @@ def load() -> ctypes.CDLL:
         "fuse_unfused_swiglu": [vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp],
         "fuse_copy": [vp, vp, sz, vp],
         "fuse_empty_kernels": [i64, vp],
+        "fuse_mfma_ceiling": [i64, i64, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -451,6 +453,16 @@ def fuse_copy(src, dst, stream=None):
     _check(dst, "dst")
     _ok(load().fuse_copy(_ptr(src), _ptr(dst), nb, _stream(stream)), "fuse_copy")
     return dst
+
+
+def fuse_mfma_ceiling(workgroups, iters, out, stream=None):
+    """Matrix-core calibration kernel: `workgroups` x 4 waves x `iters` rounds of 8 bf16 32x32x16
+    MFMAs from registers; out (fp32, >= workgroups * 256 values) receives 2048 * iters per thread."""
+    if out.dtype != torch.float32 or out.numel() < int(workgroups) * 256:
+        raise ValueError("out must be fp32 with at least workgroups * 256 values")
+    _check(out, "out")
+    _ok(load().fuse_mfma_ceiling(int(workgroups), int(iters), _ptr(out), _stream(stream)), "fuse_mfma_ceiling")
+    return out
 
 
 def fuse_empty_kernels(count, stream=None):

@@ -598,6 +598,14 @@ fuse_status_t fuse_copy(const void* src, void* dst, size_t bytes, void* stream) 
     return hip_status(fuse::launch_copy(src, dst, bytes, (hipStream_t)stream));
 }
 
+fuse_status_t fuse_mfma_ceiling(int64_t workgroups, int64_t iters, void* out, void* stream) {
+    if (workgroups < 1 || workgroups > FUSE_MAX_CEILING_WORKGROUPS) return FUSE_ERR_BAD_SHAPE;
+    if (iters < 1 || iters > FUSE_MAX_CEILING_ITERS) return FUSE_ERR_BAD_SHAPE;
+    if (!out) return FUSE_ERR_NULL_PTR;
+    if (((uintptr_t)out & 3u) != 0) return FUSE_ERR_MISALIGNED;
+    return hip_status(fuse::launch_mfma_ceiling((int)workgroups, (int)iters, (float*)out, (hipStream_t)stream));
+}
+
 fuse_status_t fuse_empty_kernels(int64_t count, void* stream) {
     if (count < 0 || count > FUSE_MAX_EMPTY_KERNELS) return FUSE_ERR_BAD_SHAPE;
     return hip_status(fuse::launch_empty(count, (hipStream_t)stream));

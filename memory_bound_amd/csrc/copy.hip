@@ -1,5 +1,6 @@
 // copy.hip -- plain device copy used to calibrate the roofline (achievable streaming bandwidth and
-// the scale of the hardware byte counters), and the empty kernel of the launch-cost probe.
+// the scale of the hardware byte counters), the matrix-core calibration kernel (achievable MFMA
+// rate), and the empty kernel of the launch-cost probe.
 #include "launch.hpp"
 #include "stream_kernels.hpp"
 
@@ -50,6 +51,42 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t str
         return hipGetLastError();
     }
     return hipSuccess;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Matrix-core calibration: 8 independent 32x32x16 bf16 accumulations per wave (128 AGPRs, so two
+// workgroups fit on a CU and each SIMD can hold two waves), operands in registers, nothing but
+// MFMAs in the loop.  The operands are ones built from the thread index, which the compiler cannot
+// fold through the matrix instruction; each accumulator element ends at 16 * iters.
+// ------------------------------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+__global__ void __launch_bounds__(256, 2) mfma_ceiling_kernel(int iters, float* out) {
+    const float one = (float)(1 + (threadIdx.x >> 8));  // 1 for every thread of the launch
+    bf16x8_t a, b;
+#pragma unroll
+    for (int i = 0; i < 8; i++) a[i] = b[i] = (__bf16)one;
+    floatx16_t acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[j][r] = 0.0f;
+    for (int it = 0; it < iters; it++) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) s += acc[j][r];
+    out[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+hipError_t launch_mfma_ceiling(int workgroups, int iters, float* out, hipStream_t stream) {
+    hipLaunchKernelGGL(mfma_ceiling_kernel, dim3((unsigned)workgroups), dim3(256), 0, stream, iters, out);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------------------------

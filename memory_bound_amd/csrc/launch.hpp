@@ -37,6 +37,7 @@ hipError_t launch_softmax_unfused(const void* x, void* y, int64_t rows, int cols
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 hipError_t launch_empty(int64_t count, hipStream_t stream);
+hipError_t launch_mfma_ceiling(int workgroups, int iters, float* out, hipStream_t stream);
 
 // SwiGLU dual GEMM, bf16.  unfused = true runs the scheme-A pair instead: the same product
 // kernel storing c1 and c2 (bf16, in `c1`, `c2`), then the element-wise SiLU(c1) * c2.

@@ -334,6 +334,15 @@ def test_copy_validation(lib):
     assert lib.fuse_copy(v(P), v(2 * P), (1 << 40) + 1, None) == SHAPE
 
 
+def test_mfma_ceiling_validation(lib):
+    assert lib.fuse_mfma_ceiling(0, 16, v(P), None) == SHAPE
+    assert lib.fuse_mfma_ceiling(65537, 16, v(P), None) == SHAPE
+    assert lib.fuse_mfma_ceiling(8, 0, v(P), None) == SHAPE
+    assert lib.fuse_mfma_ceiling(8, (1 << 24) + 1, v(P), None) == SHAPE
+    assert lib.fuse_mfma_ceiling(8, 16, v(0), None) == NULL
+    assert lib.fuse_mfma_ceiling(8, 16, v(P + 2), None) == MISAL
+
+
 def test_empty_kernels_validation(lib):
     assert lib.fuse_empty_kernels(-1, None) == SHAPE
     assert lib.fuse_empty_kernels((1 << 20) + 1, None) == SHAPE

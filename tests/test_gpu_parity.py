@@ -952,6 +952,19 @@ def test_copy_kernel():
     assert torch.equal(s2, d2)
 
 
+def test_mfma_ceiling_kernel():
+    # every accumulator element is a sum of 16 * iters products of ones: exact in fp32
+    announce("mfma ceiling")
+    wgs, iters = 2 * torch.cuda.get_device_properties(0).multi_processor_count, 64
+    out = torch.full((wgs * 256,), -1.0, dtype=torch.float32, device="cuda")
+    api.fuse_mfma_ceiling(wgs, iters, out)
+    assert torch.equal(out, torch.full_like(out, 2048.0 * iters))
+    part = torch.full((300,), -1.0, dtype=torch.float32, device="cuda")
+    api.fuse_mfma_ceiling(1, 8192, part)  # the largest iteration count that stays exact
+    assert torch.equal(part[:256], torch.full((256,), 2048.0 * 8192, device="cuda"))
+    assert torch.equal(part[256:], torch.full((44,), -1.0, device="cuda"))
+
+
 def test_empty_kernels_eager_and_captured():
     # the launch-cost probe runs to completion eagerly and inside a captured graph
     announce("empty kernels")
