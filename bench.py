@@ -438,7 +438,10 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
     return out
 
 
-def mfma_ceiling(torch, api, stream, roofline, n_launch, iters=448):
+CEILING_ITERS = 448  # rounds of the matrix-core calibration kernel: about the SwiGLU workload's length
+
+
+def mfma_ceiling(torch, api, stream, roofline, n_launch, iters=CEILING_ITERS):
     """The matrix-core calibration kernel (bf16 32x32x16 MFMAs from registers, two workgroups of
     four waves per CU) sized to run about as long as the SwiGLU workload, timed the two ways the
     matrix-core rows are: one synchronised dispatch at a time, and back to back."""
@@ -632,7 +635,16 @@ def counters_rows(torch, api, synth, n=4):
 
 
 def dispatch_only(torch, api, synth, name, count):
-    """`count` eager dispatches of one fused row at its workload (for a profiler run), no timing."""
+    """`count` eager dispatches of one fused row at its workload (for a profiler run), no timing.
+    `mfma_ceiling` dispatches the matrix-core calibration kernel as the benchmark sizes it."""
+    if name == "mfma_ceiling":
+        wgs = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+        res = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+        for _ in range(count):
+            api.fuse_mfma_ceiling(wgs, CEILING_ITERS, res)
+            torch.cuda.synchronize()
+        log(f"dispatched {count} x mfma_ceiling ({wgs} workgroups, {CEILING_ITERS} rounds)")
+        return
     w = synth.WORKLOADS[name]
     d = {k: (v.cuda() if hasattr(v, "cuda") else v) for k, v in w.inputs().items()}
     if w.op == "swiglu":
@@ -853,7 +865,8 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="only run the short dispatch sequence read by rocprofv3 --pmc, no timing")
     ap.add_argument("--dispatch", metavar="WORKLOAD",
-                    help="only dispatch the fused kernel of one workload --dispatch-count times (profiling)")
+                    help="only dispatch the fused kernel of one workload (or mfma_ceiling, the matrix-core "
+                         "calibration kernel) --dispatch-count times (profiling)")
     ap.add_argument("--dispatch-count", type=int, default=3)
     ap.add_argument("--counters-rows", action="store_true",
                     help="the same for the other rows of the path (their fused and unfused kernels)")
