@@ -124,6 +124,9 @@ fuse_status_t fuse_add_layernorm(const void *x, const void *residual, const void
  *              The statistics buffers must not overlap each other or any tensor argument.
  *   flags    : 0 or FUSE_LN_RELU; any other bit is FUSE_ERR_BAD_VALUE.  A NaN stays NaN
  *              through the ReLU.
+ * Under one launch plan, y (before the ReLU) and the statistics equal fuse_add_layernorm's bit for
+ * bit.  A call that stores sum_out may run more waves per row than one that does not, and a
+ * different split of the row sums can change the last bit of y and the statistics.
  */
 #define FUSE_LN_RELU 1u
 fuse_status_t fuse_add_layernorm_ex(const void *x, const void *residual, const void *gamma,

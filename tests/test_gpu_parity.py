@@ -150,7 +150,7 @@ def test_add_layernorm_ex_parity(rows, hidden, dtype, relu):
     _check_ln_ex(outs, d, relu, KIND[dtype], f"ln_ex {rows}x{hidden} {dtype} relu={relu}")
 
 
-def test_add_layernorm_ex_workload_full():
+def test_add_layernorm_ex_workload_full(monkeypatch):
     w = synth.WORKLOADS["addln_f16_2048x4096"]
     announce("add_layernorm_ex workload 2048x4096 fp16, relu and every output")
     d = w.inputs()
@@ -158,13 +158,21 @@ def test_add_layernorm_ex_workload_full():
     outs = api.fuse_add_layernorm_ex(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"], relu=True,
                                      want_sum=True, want_stats=True)
     _check_ln_ex(outs, d, True, "f16", "ln_ex workload")
-    # the same y as the plain fused kernel before the clamp, and only the requested outputs
-    y0 = api.fuse_add_layernorm(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"])
-    assert torch.equal(outs[0], torch.where(y0 < 0, torch.zeros_like(y0), y0))
-    y1, s1, m1, v1 = api.fuse_add_layernorm_ex(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"])
-    assert torch.equal(y1, y0) and s1 is None and m1 is None and v1 is None
-    _, s2, m2, v2 = api.fuse_add_layernorm_ex(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"], want_stats=True)
-    assert s2 is None and torch.equal(m2, outs[2]) and torch.equal(v2, outs[3])
+    # under one launch plan (the plain kernel's 4 waves per row, and the 8 a call storing the sum
+    # takes by default): the same y as the plain fused kernel before the clamp, the same
+    # statistics with or without the sum, and only the requested outputs
+    for wpr in ("4", "8"):
+        monkeypatch.setenv("FUSE_ROW_WPR", wpr)
+        full = api.fuse_add_layernorm_ex(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"], relu=True,
+                                         want_sum=True, want_stats=True)
+        y0 = api.fuse_add_layernorm(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"])
+        assert torch.equal(full[0], torch.where(y0 < 0, torch.zeros_like(y0), y0)), wpr
+        assert torch.equal(full[1], outs[1]), wpr  # the sum is exact whatever the plan
+        y1, s1, m1, v1 = api.fuse_add_layernorm_ex(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"])
+        assert torch.equal(y1, y0) and s1 is None and m1 is None and v1 is None, wpr
+        _, s2, m2, v2 = api.fuse_add_layernorm_ex(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"],
+                                                  want_stats=True)
+        assert s2 is None and torch.equal(m2, full[2]) and torch.equal(v2, full[3]), wpr
 
 
 def test_add_layernorm_ex_inplace_sum_and_nan():
