@@ -855,6 +855,76 @@ def cpu_baseline(synth, roofline, budget_s=8.0, single_budget_s=4.0):
             "host_cpu": host_cpu_model(), "host_cpus": os.cpu_count()}
 
 
+# (workload, rows of it in the timed sample) for the oracle timings of the other rows: whole
+# workloads where one oracle call takes well under the budget, leading rows otherwise
+CPU_ROWS = (("addln_f32_64x768", None), ("gelu_f16_2048x4096", None), ("addln_f16_16384x4096", 2048),
+            ("softmax_f16_65536x2048", 4096), ("cumsum_f16_2048x4096", None),
+            ("swiglu_bf16_2048x8960x1536", 8), ("gemm_relu_bf16_2048x8960x1536", 8))
+
+
+def cpu_rows(synth, roofline, budget_s=1.0):
+    """The oracle timed on the host for every other workload, all OpenMP threads and then one
+    thread, about budget_s each, on the whole workload or its leading rows (the row work of these
+    operations is independent, so a row sample scales)."""
+    import numpy as np
+
+    import oracle
+
+    def timed(fn, budget):
+        fn()  # warm
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return el / reps
+
+    out = {}
+    threads = oracle.threads()
+    for name, rows in CPU_ROWS:
+        w = synth.WORKLOADS[name]
+        d = w.inputs()
+        shape = w.shape if rows is None else (rows,) + tuple(w.shape[1:])
+        cut = (lambda t: t) if rows is None else (lambda t: t[:rows])
+        if w.op == "add_layernorm":
+            x, r, g, b = oracle.f64(cut(d["x"])), oracle.f64(cut(d["residual"])), oracle.f64(d["gamma"]), \
+                oracle.f64(d["beta"])
+            eps = float(np.float32(d["eps"]))
+            fn = lambda: oracle.add_layernorm(x, r, g, b, eps)
+        elif w.op == "bias_gelu_residual":
+            x, bias, r = oracle.f64(cut(d["x"])), oracle.f64(d["bias"]), oracle.f64(cut(d["residual"]))
+            fn = lambda: oracle.bias_gelu_residual(x, bias, r)
+        elif w.op == "softmax_rows":
+            x, sc = oracle.f64(cut(d["x"])), float(np.float32(d["scale"]))
+            fn = lambda: oracle.softmax_rows(x, sc)
+        elif w.op == "cumsum_scale_rows":
+            x, sc = oracle.f64(cut(d["x"])), float(np.float32(d["scale"]))
+            fn = lambda: oracle.cumsum_scale_rows(x, sc)
+        elif w.op == "swiglu":
+            a, b1, b2 = oracle.f64(cut(d["a"])), oracle.f64(d["b1"]), oracle.f64(d["b2"])
+            fn = lambda: oracle.swiglu(a, b1, b2)
+        else:
+            x, wt, bias = oracle.f64(cut(d["x"])), oracle.f64(d["w"]), oracle.f64(d["bias"])
+            fn = lambda: oracle.gemm_bias_act(x, wt, bias, "relu")
+        work = roofline.workload_work(w.op, shape, w.dtype)
+        per = timed(fn, budget_s)
+        oracle.set_threads(1)
+        try:
+            per1 = timed(fn, budget_s)
+        finally:
+            oracle.set_threads(threads)
+        if "flops" in work:
+            val, val1, unit = work["flops"] / per / 1e12, work["flops"] / per1 / 1e12, "TFLOP/s"
+        else:
+            val, val1, unit = work["bytes"] / per / 1e9, work["bytes"] / per1 / 1e9, "GB/s"
+        out[name] = {"value": round(val, 4), "single_thread": round(val1, 4), "unit": unit, "cores": threads,
+                     "ms_per_call": round(per * 1e3, 3), "single_thread_ms_per_call": round(per1 * 1e3, 3),
+                     "sample": "whole workload" if rows is None else f"leading {rows} of {w.shape[0]} rows"}
+        log(f"oracle {name}: {val:.4g} {unit} on {threads} threads, {val1:.4g} on one")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -903,6 +973,7 @@ def main():
     study = None if a.no_rows else launch_study(torch, api, synth)
     selection = None if a.no_rows else selection_study(torch, api, synth)
     cpu = None if a.no_cpu else cpu_baseline(synth, roofline)
+    oracle_rows = None if (a.no_cpu or a.no_rows) else cpu_rows(synth, roofline)
 
     traffic = read_counters()
     trace = read_trace(h["bytes"])
@@ -941,6 +1012,7 @@ def main():
                                    "alone, from the committed rocprofv3 trace of this command",
                      "kernel_trace": trace},
         "cpu_baseline": cpu,
+        "cpu_rows": oracle_rows,
         "headline_hot_cache": h["hot"],
         "rows": rows,
         "launch_study": study,
