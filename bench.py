@@ -846,13 +846,23 @@ def cpu_baseline(synth, roofline, budget_s=8.0, single_budget_s=4.0):
     finally:
         oracle.set_threads(threads)
     per1 = el1 / reps1
+    # the product path's result on the same inputs against the oracle's
+    import torch
+    from oracle.tolerance import RULE_TEXT, compare
+
+    from memory_bound_amd import api
+    y = api.fuse_add_layernorm(d["x"].cuda(), d["residual"].cuda(), d["gamma"].cuda(), d["beta"].cuda(), d["eps"])
+    c = compare(y, oracle.add_layernorm(x, r, g, b, eps), w.dtype)
+    par = {"rule": RULE_TEXT[w.dtype], "n": c["n"], "max_abs_err": c["max_abs"],
+           "max_err_over_allowed": round(c["max_excess"], 4), "n_bad": c["n_bad"], "ok": c["ok"]}
+    torch.cuda.synchronize()
     return {"value": round(work["bytes"] / per / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"full {w.shape[0]}x{w.shape[1]} workload, {reps} oracle calls in {el:.1f} s "
                       f"({per * 1e3:.2f} ms per call, fp64, inputs pre-widened)",
             "single_thread": {"value": round(work["bytes"] / per1 / 1e9, 3), "unit": "GB/s",
                               "sample": f"{reps1} calls in {el1:.1f} s ({per1 * 1e3:.2f} ms per call)"},
-            "host_cpu": host_cpu_model(), "host_cpus": os.cpu_count()}
+            "host_cpu": host_cpu_model(), "host_cpus": os.cpu_count(), "parity": par}
 
 
 # (workload, rows of it in the timed sample) for the oracle timings of the other rows: whole
@@ -880,6 +890,18 @@ def cpu_rows(synth, roofline, budget_s=1.0):
             if el >= budget:
                 return el / reps
 
+    import torch
+    from oracle.tolerance import RULE_TEXT, compare
+
+    from memory_bound_amd import api
+
+    def parity(y_gpu, ref, kind, rows):
+        # the product path's result on the same inputs, its leading rows against the oracle's
+        y = y_gpu if rows is None else y_gpu[:rows]
+        r = compare(y, ref, kind)
+        return {"rule": RULE_TEXT[kind], "n": r["n"], "max_abs_err": r["max_abs"],
+                "max_err_over_allowed": round(r["max_excess"], 4), "n_bad": r["n_bad"], "ok": r["ok"]}
+
     out = {}
     threads = oracle.threads()
     for name, rows in CPU_ROWS:
@@ -887,26 +909,33 @@ def cpu_rows(synth, roofline, budget_s=1.0):
         d = w.inputs()
         shape = w.shape if rows is None else (rows,) + tuple(w.shape[1:])
         cut = (lambda t: t) if rows is None else (lambda t: t[:rows])
+        g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in d.items()}
         if w.op == "add_layernorm":
-            x, r, g, b = oracle.f64(cut(d["x"])), oracle.f64(cut(d["residual"])), oracle.f64(d["gamma"]), \
+            x, r, gm, b = oracle.f64(cut(d["x"])), oracle.f64(cut(d["residual"])), oracle.f64(d["gamma"]), \
                 oracle.f64(d["beta"])
             eps = float(np.float32(d["eps"]))
-            fn = lambda: oracle.add_layernorm(x, r, g, b, eps)
+            fn = lambda: oracle.add_layernorm(x, r, gm, b, eps)
+            gpu = lambda: api.fuse_add_layernorm(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"])
         elif w.op == "bias_gelu_residual":
             x, bias, r = oracle.f64(cut(d["x"])), oracle.f64(d["bias"]), oracle.f64(cut(d["residual"]))
             fn = lambda: oracle.bias_gelu_residual(x, bias, r)
+            gpu = lambda: api.fuse_bias_gelu_residual(g["x"], g["bias"], g["residual"])
         elif w.op == "softmax_rows":
             x, sc = oracle.f64(cut(d["x"])), float(np.float32(d["scale"]))
             fn = lambda: oracle.softmax_rows(x, sc)
+            gpu = lambda: api.fuse_softmax_rows(g["x"], d["scale"])
         elif w.op == "cumsum_scale_rows":
             x, sc = oracle.f64(cut(d["x"])), float(np.float32(d["scale"]))
             fn = lambda: oracle.cumsum_scale_rows(x, sc)
+            gpu = lambda: api.fuse_cumsum_scale_rows(g["x"], d["scale"])
         elif w.op == "swiglu":
             a, b1, b2 = oracle.f64(cut(d["a"])), oracle.f64(d["b1"]), oracle.f64(d["b2"])
             fn = lambda: oracle.swiglu(a, b1, b2)
+            gpu = lambda: api.fuse_swiglu_dualgemm(g["a"], g["b1"], g["b2"])
         else:
             x, wt, bias = oracle.f64(cut(d["x"])), oracle.f64(d["w"]), oracle.f64(d["bias"])
             fn = lambda: oracle.gemm_bias_act(x, wt, bias, "relu")
+            gpu = lambda: api.fuse_gemm_bias_act(g["x"], g["w"], g["bias"], "relu")
         work = roofline.workload_work(w.op, shape, w.dtype)
         per = timed(fn, budget_s)
         oracle.set_threads(1)
@@ -920,7 +949,8 @@ def cpu_rows(synth, roofline, budget_s=1.0):
             val, val1, unit = work["bytes"] / per / 1e9, work["bytes"] / per1 / 1e9, "GB/s"
         out[name] = {"value": round(val, 4), "single_thread": round(val1, 4), "unit": unit, "cores": threads,
                      "ms_per_call": round(per * 1e3, 3), "single_thread_ms_per_call": round(per1 * 1e3, 3),
-                     "sample": "whole workload" if rows is None else f"leading {rows} of {w.shape[0]} rows"}
+                     "sample": "whole workload" if rows is None else f"leading {rows} of {w.shape[0]} rows",
+                     "parity": parity(gpu(), fn(), w.dtype, rows)}
         log(f"oracle {name}: {val:.4g} {unit} on {threads} threads, {val1:.4g} on one")
     return out
 

@@ -24,6 +24,13 @@ BF16_REL = 1e-2
 BF16_FLOOR = 1e-2
 FP32_ABS = 1e-5
 
+# The rules above as text, for reports.
+RULE_TEXT = {
+    "f16": "|y - ref| <= max(2e-3, ulp16(ref))",
+    "bf16": "|y - ref| / max(|ref|, 1e-2) <= 1e-2",
+    "f32": "|y - ref| <= 1e-5",
+}
+
 
 def ulp16(v) -> np.ndarray:
     """Spacing of the binary16 grid in the binade of |v| (2^-24 in the subnormal range)."""
