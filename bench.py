@@ -40,14 +40,17 @@ def log(msg):
 
 
 def read_counters():
-    """HBM bytes per dispatch from the committed counter summary, or None when the kernel
-    source changed since the counters were taken."""
+    """HBM bytes per dispatch of the headline kernel and the unfused chain's bytes over them,
+    from the committed counter summary; (None, None) when the kernel source changed since the
+    counters were taken."""
     from memory_bound_amd import profsum
     kv = profsum.read_profile(PROFILE_COUNTERS)
     try:
-        return float(kv["hbm_bytes_per_dispatch"]) if kv else None
+        if not kv:
+            return None, None
+        return float(kv["hbm_bytes_per_dispatch"]), float(kv["unfused_over_fused_traffic"])
     except (KeyError, ValueError):
-        return None
+        return None, None
 
 
 def read_trace(nbytes):
@@ -1005,7 +1008,7 @@ def main():
     cpu = None if a.no_cpu else cpu_baseline(synth, roofline)
     oracle_rows = None if (a.no_cpu or a.no_rows) else cpu_rows(synth, roofline)
 
-    traffic = read_counters()
+    traffic, unfused_ratio = read_counters()
     trace = read_trace(h["bytes"])
     w = h["workload"]
     host_us, ev_us = h["host_s"] * 1e6, h["avg_launch_us"] * a.steps
@@ -1035,6 +1038,7 @@ def main():
                      "peak": roofline.HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(h["achieved_gbps"] / roofline.HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes": h["bytes"],
+                     "unfused_over_fused_traffic": unfused_ratio,
                      "avg_launch_us": round(h["avg_launch_us"], 3),
                      "definition": "achieved = algorithmic bytes / avg_launch_us, the HIP-event time of the "
                                    "timed graph replay on the launch stream over the steps: the kernel plus the "
