@@ -503,35 +503,33 @@ cumsum_scale_kernel(const typename Elem<D>::T* x, typename Elem<D>::T* y, int64_
             btot[j] = lane_read(inc, 63);
         }
 
-        // offsets of the blocks before this wave's (j, wpos) blocks
-        float pre[NV];
-        if constexpr (WPR == 1) {
-            float off = 0.0f;
-#pragma unroll
-            for (int j = 0; j < NV; j++) {
-                pre[j] = off;
-                off += btot[j];
-            }
-        } else {
-            float (&tot)[NV][WPR] = lds_tot[KS > 1 ? (k & 1) : 0][rib];
+        // offsets of the blocks before this wave's (j, wpos) blocks: the running sum `off` of the
+        // block totals in (j, wave) order, taken for each j as it is stored, so that only one
+        // chunk group's totals are live at a time
+        float (&tot)[NV][WPR] = lds_tot[KS > 1 ? (k & 1) : 0][rib];
+        if constexpr (WPR > 1) {
             if ((threadIdx.x & 63) == 0) {
 #pragma unroll
                 for (int j = 0; j < NV; j++) tot[j][wpos] = btot[j];
             }
             __syncthreads();
-            float off = 0.0f;
-#pragma unroll
-            for (int j = 0; j < NV; j++)
-#pragma unroll
-                for (int w = 0; w < WPR; w++) {
-                    if (w == wpos) pre[j] = off;
-                    off += tot[j][w];
-                }
         }
+        float off = 0.0f;
 
 #pragma unroll
         for (int j = 0; j < NV; j++) {
-            const float base = pre[j] + excl[j];
+            float pre = 0.0f;
+            if constexpr (WPR == 1) {
+                pre = off;
+                off += btot[j];
+            } else {
+#pragma unroll
+                for (int w = 0; w < WPR; w++) {
+                    if (w == wpos) pre = off;
+                    off += tot[j][w];
+                }
+            }
+            const float base = pre + excl[j];
             float o[V];
 #pragma unroll
             for (int e = 0; e < V; e++) o[e] = scale * (base + v[j][e]);
