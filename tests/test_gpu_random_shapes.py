@@ -1,6 +1,7 @@
 """Seeded random shapes for every fused operation (GPU required): row lengths across the whole
-supported range, odd row counts, every storage type, with and without the residual or bias, and
-tensors that start one element past a 16-byte boundary (the per-element paths).  Each result is
+supported range, odd row counts, every storage type, with and without the residual, every
+activation and LayerNorm-variant output combination, and tensors that start one element past a
+16-byte boundary (the per-element paths).  Each result is
 compared with the CPU oracle element by element under the operation's rule.  The shapes are
 drawn once from a fixed seed, so a failure names a case that can be rerun alone.
 """
@@ -15,7 +16,6 @@ from oracle.tolerance import assert_close
 pytestmark = pytest.mark.gpu
 
 DTYPES = ["f32", "f16", "bf16"]
-TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
 def _cases(seed, n, draw):
@@ -126,3 +126,19 @@ def test_gemm_bias_act_random(M, N, K, offset, act):
     api.fuse_gemm_bias_act(_place(d["x"], offset), _place(d["w"], offset), d["bias"].cuda(), act, y=y)
     assert_close(y, oracle.gemm_bias_act(d["x"], d["w"], d["bias"], act), "bf16",
                  f"gemm {M}x{N}x{K} off={offset} {act}")
+
+
+LN_EX_CASES = _cases(20261209, 12, lambda r: (int(r.integers(1, 40)), int(r.integers(2, 16385)),
+                                              DTYPES[int(r.integers(0, 3))], bool(r.integers(0, 2)),
+                                              bool(r.integers(0, 2)), bool(r.integers(0, 2))))
+
+
+@pytest.mark.parametrize("rows,hidden,dtype,relu,want_sum,want_stats", LN_EX_CASES)
+def test_add_layernorm_ex_random(rows, hidden, dtype, relu, want_sum, want_stats):
+    from test_gpu_parity import _check_ln_ex
+    announce(f"add_layernorm_ex random {rows}x{hidden} {dtype} relu={relu} sum={want_sum} stats={want_stats}")
+    d = synth.add_layernorm_inputs(rows, hidden, dtype, seed=rows * 47 + hidden)
+    outs = api.fuse_add_layernorm_ex(d["x"].cuda(), d["residual"].cuda(), d["gamma"].cuda(), d["beta"].cuda(),
+                                     d["eps"], relu=relu, want_sum=want_sum, want_stats=want_stats)
+    assert (outs[1] is not None) == want_sum and (outs[2] is not None) == want_stats
+    _check_ln_ex(outs, d, relu, dtype, f"ln_ex {rows}x{hidden} {dtype} relu={relu} sum={want_sum} stats={want_stats}")
