@@ -1,9 +1,9 @@
 """Seeded random shapes for every fused operation (GPU required): row lengths across the whole
-supported range, odd row counts, every storage type, with and without the residual, every
-activation and LayerNorm-variant output combination, and tensors that start one element past a
-16-byte boundary (the per-element paths).  Each result is
-compared with the CPU oracle element by element under the operation's rule.  The shapes are
-drawn once from a fixed seed, so a failure names a case that can be rerun alone.
+supported range, odd row counts, every storage type, with and without the residual, random
+activations and LayerNorm-variant outputs, and tensors that start one element past a 16-byte
+boundary (the per-element paths).  Each result is compared with the CPU oracle element by
+element under the operation's rule.  The shapes are drawn once from a fixed seed, so a failure
+names a case that can be rerun alone.
 """
 import numpy as np
 import pytest
