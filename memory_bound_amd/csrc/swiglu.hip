@@ -89,13 +89,21 @@ struct Tile {
     int m0, n0;
 };
 
-// Bijective remap of the dispatch index so that XCD x (= bid % 8) gets a contiguous tile range.
+// Bijective remap of the dispatch index so that XCD x (= bid % 8) gets a contiguous tile range,
+// and tiles in that range ordered in groups of up to 8 row tiles by every column tile (row tile
+// fastest): the 32 tiles an XCD's CUs run at once then share 8 a row panels and about 4 b column
+// panels in its L2, whatever the row count.  With 8 row tiles or fewer this is plain column
+// order.
 __device__ __forceinline__ Tile tile_of(int bid, int tiles_m, int tiles_n, int bn_step) {
     const int nt = tiles_m * tiles_n;
     const int xcd = bid % NUM_XCD, slot = bid / NUM_XCD;
     const int q = nt / NUM_XCD, rem = nt % NUM_XCD;
     const int t = xcd * q + min(xcd, rem) + slot;
-    return {(t % tiles_m) * BM, (t / tiles_m) * bn_step};
+    constexpr int GM = 8;
+    const int gm = min(GM, tiles_m);
+    const int g = t / (gm * tiles_n), r = t - g * gm * tiles_n;
+    const int rows = min(gm, tiles_m - g * gm);  // the last group may hold fewer row tiles
+    return {(g * gm + r % rows) * BM, (r / rows) * bn_step};
 }
 
 // Global -> registers for one K step.  The a resource spans the tile's valid rows and the b
