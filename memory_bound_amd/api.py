@@ -174,6 +174,17 @@ def _workspace(op, d0, d1, d2, dtype_code, device, stream=None):
     return _scratch(load().fuse_unfused_workspace_bytes(op, d0, d1, d2, dtype_code), device, stream)
 
 
+def _caller_workspace(workspace):
+    """The `workspace` argument of the entry points that take one: None (allocate one for this
+    call), a contiguous GPU tensor whose bytes are the workspace (at least what the matching
+    fuse_*_workspace_bytes call returns, 256-byte aligned; the library checks both), or what
+    _workspace / _auto_workspace return."""
+    if workspace is None or isinstance(workspace, tuple):
+        return workspace
+    _check(workspace, "workspace")
+    return workspace, ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+
+
 # ------------------------------------------------------------------------------------------------
 # fused entry points
 # ------------------------------------------------------------------------------------------------
@@ -312,7 +323,7 @@ def fuse_swiglu_auto(a, b1, b2, out=None, workspace=None, stream=None):
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
     _check(out, "out", a.dtype, (M, N))
-    ws = workspace or _auto_workspace(FUSE_OP_SWIGLU, M, N, K, a.device, stream)
+    ws = _caller_workspace(workspace) or _auto_workspace(FUSE_OP_SWIGLU, M, N, K, a.device, stream)
     _ok(load().fuse_swiglu_auto(_ptr(a), _ptr(b1), _ptr(b2), _ptr(out), M, N, K, _dt(a), ws[1], ws[2],
                                 _stream(stream)), "fuse_swiglu_auto")
     return out
@@ -344,7 +355,7 @@ def fuse_gemm_bias_act_auto(x, w, bias=None, act="relu", y=None, workspace=None,
     if y is None:
         y = torch.empty((M, N), dtype=x.dtype, device=x.device)
     _check(y, "y", x.dtype, (M, N))
-    ws = workspace or _auto_workspace(FUSE_OP_GEMM_BIAS_ACT, M, N, K, x.device, stream)
+    ws = _caller_workspace(workspace) or _auto_workspace(FUSE_OP_GEMM_BIAS_ACT, M, N, K, x.device, stream)
     _ok(load().fuse_gemm_bias_act_auto(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), M, N, K, FUSE_ACT[act], _dt(x),
                                        ws[1], ws[2], _stream(stream)), "fuse_gemm_bias_act_auto")
     return y
@@ -363,7 +374,7 @@ def fuse_unfused_add_layernorm(x, residual, gamma, beta, eps=1e-5, y=None, works
     if y is None:
         y = torch.empty_like(x)
     _check(y, "y", x.dtype, x.shape)
-    ws = workspace or _workspace(FUSE_OP_ADD_LAYERNORM, rows, hidden, 0, _dt(x), x.device, stream)
+    ws = _caller_workspace(workspace) or _workspace(FUSE_OP_ADD_LAYERNORM, rows, hidden, 0, _dt(x), x.device, stream)
     _ok(load().fuse_unfused_add_layernorm(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y), rows,
                                           hidden, float(eps), _dt(x), ws[1], ws[2], _stream(stream)),
         "fuse_unfused_add_layernorm")
@@ -378,7 +389,7 @@ def fuse_unfused_bias_gelu_residual(x, bias, residual, y=None, workspace=None, s
     if y is None:
         y = torch.empty_like(x)
     _check(y, "y", x.dtype, x.shape)
-    ws = workspace or _workspace(FUSE_OP_BIAS_GELU_RESIDUAL, rows, hidden, 0, _dt(x), x.device, stream)
+    ws = _caller_workspace(workspace) or _workspace(FUSE_OP_BIAS_GELU_RESIDUAL, rows, hidden, 0, _dt(x), x.device, stream)
     _ok(load().fuse_unfused_bias_gelu_residual(_ptr(x), _ptr(bias), _ptr(residual), _ptr(y), rows, hidden,
                                                _dt(x), ws[1], ws[2], _stream(stream)),
         "fuse_unfused_bias_gelu_residual")
@@ -391,7 +402,7 @@ def fuse_unfused_softmax_rows(x, scale=1.0, y=None, workspace=None, stream=None)
     if y is None:
         y = torch.empty_like(x)
     _check(y, "y", x.dtype, x.shape)
-    ws = workspace or _workspace(FUSE_OP_SOFTMAX_ROWS, rows, cols, 0, _dt(x), x.device, stream)
+    ws = _caller_workspace(workspace) or _workspace(FUSE_OP_SOFTMAX_ROWS, rows, cols, 0, _dt(x), x.device, stream)
     _ok(load().fuse_unfused_softmax_rows(_ptr(x), _ptr(y), rows, cols, float(scale), _dt(x), ws[1], ws[2],
                                          _stream(stream)), "fuse_unfused_softmax_rows")
     return y
@@ -403,7 +414,7 @@ def fuse_unfused_cumsum_scale_rows(x, scale=1.0, y=None, workspace=None, stream=
     if y is None:
         y = torch.empty_like(x)
     _check(y, "y", x.dtype, x.shape)
-    ws = workspace or _workspace(FUSE_OP_CUMSUM_SCALE, rows, cols, 0, _dt(x), x.device, stream)
+    ws = _caller_workspace(workspace) or _workspace(FUSE_OP_CUMSUM_SCALE, rows, cols, 0, _dt(x), x.device, stream)
     _ok(load().fuse_unfused_cumsum_scale_rows(_ptr(x), _ptr(y), rows, cols, float(scale), _dt(x), ws[1], ws[2],
                                               _stream(stream)), "fuse_unfused_cumsum_scale_rows")
     return y
@@ -418,7 +429,7 @@ def fuse_unfused_swiglu(a, b1, b2, out=None, workspace=None, stream=None):
     if out is None:
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
     _check(out, "out", a.dtype, (M, N))
-    ws = workspace or _workspace(FUSE_OP_SWIGLU, M, N, K, _dt(a), a.device, stream)
+    ws = _caller_workspace(workspace) or _workspace(FUSE_OP_SWIGLU, M, N, K, _dt(a), a.device, stream)
     _ok(load().fuse_unfused_swiglu(_ptr(a), _ptr(b1), _ptr(b2), _ptr(out), M, N, K, _dt(a), ws[1], ws[2],
                                    _stream(stream)), "fuse_unfused_swiglu")
     return out
@@ -438,7 +449,7 @@ def fuse_unfused_gemm_bias_act(x, w, bias=None, act="relu", y=None, workspace=No
     if y is None:
         y = torch.empty((M, N), dtype=x.dtype, device=x.device)
     _check(y, "y", x.dtype, (M, N))
-    ws = workspace or _workspace(FUSE_OP_GEMM_BIAS_ACT, M, N, K, _dt(x), x.device, stream)
+    ws = _caller_workspace(workspace) or _workspace(FUSE_OP_GEMM_BIAS_ACT, M, N, K, _dt(x), x.device, stream)
     _ok(load().fuse_unfused_gemm_bias_act(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), M, N, K, FUSE_ACT[act], _dt(x),
                                           ws[1], ws[2], _stream(stream)), "fuse_unfused_gemm_bias_act")
     return y

@@ -828,6 +828,36 @@ def test_unfused_gemm_bias_act(act):
     _loose(y, oracle.gemm_bias_act_unfused(d["x"], d["w"], None, act, "bf16"), "bf16", f"unfused gemm {act} no bias")
 
 
+def test_caller_workspace_tensors():
+    # a plain device tensor as the workspace gives the same result as the one the binding
+    # allocates; a too small or misaligned one is refused with nothing launched
+    announce("caller-owned workspace tensors: split-K SwiGLU plan, unfused Add+LayerNorm")
+    lib = api.load()
+    M, N, K = 256, 512, 1536
+    d = synth.swiglu_inputs(M, N, K, "bf16", seed=17)
+    a, b1, b2 = d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda()
+    need = lib.fuse_auto_workspace_bytes(api.FUSE_OP_SWIGLU, M, N, K, api.FUSE_BF16)
+    assert need > 0
+    ref = api.fuse_swiglu_auto(a, b1, b2)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    assert torch.equal(api.fuse_swiglu_auto(a, b1, b2, workspace=ws), ref)
+    out = torch.full_like(ref, 7.0)
+    with pytest.raises(api.FuseError) as e:
+        api.fuse_swiglu_auto(a, b1, b2, out=out, workspace=ws[:need - 256])
+    assert e.value.status == 7 and torch.equal(out, torch.full_like(ref, 7.0))
+    big = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+    with pytest.raises(api.FuseError) as e:
+        api.fuse_swiglu_auto(a, b1, b2, out=out, workspace=big[16:16 + need])
+    assert e.value.status == 7
+    d = synth.add_layernorm_inputs(64, 4096, "f16", seed=18)
+    g = cuda(d)
+    y0 = api.fuse_unfused_add_layernorm(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"])
+    n = lib.fuse_unfused_workspace_bytes(api.FUSE_OP_ADD_LAYERNORM, 64, 4096, 0, api.FUSE_F16)
+    ws = torch.empty(n // 2, dtype=torch.float16, device="cuda")
+    y1 = api.fuse_unfused_add_layernorm(g["x"], g["residual"], g["gamma"], g["beta"], d["eps"], workspace=ws)
+    assert torch.equal(y0, y1)
+
+
 def test_internal_workspaces_on_a_side_stream():
     # The wrappers allocate the split-K partials and the unfused intermediates themselves when no
     # workspace is given, and enqueue the kernels on the caller's stream.  Run each on a stream
