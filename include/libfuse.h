@@ -274,10 +274,13 @@ fuse_status_t fuse_unfused_gemm_bias_act(const void *x, const void *w, const voi
  * 不同场景下的选型建议 and 迁移与使用注意事项 §4: whether fusing pays depends on whether the fused
  * kernel's blocks fill the GPU, so the choice is made per shape from the device's attributes).
  * The fused kernel's time has a floor: one workgroup walks all of K for its output tile.  When the
- * tiles cover less than a quarter of the device's CUs (the CU count is read from the device), K is
+ * tiles cover less than half of the device's CUs (the CU count is read from the device), K may be
  * split over several workgroups per tile, each storing fp32 partial products in the workspace,
- * and a second kernel sums them in a fixed order and applies the same epilogue.  Full-tile,
- * 16-byte aligned shapes only; anything else runs the single fused kernel.
+ * and a second kernel sums them in a fixed order and applies the same epilogue.  The split count
+ * minimises an estimated time: the rounds of tiles x splits workgroups over the CUs times the K
+ * steps of one split, plus, when split, a fixed cost for the second kernel and the partials'
+ * traffic.  Each split keeps at least 4 K steps of 32 and the partials stay within 64 MiB.
+ * Full-tile, 16-byte aligned shapes only; anything else runs the single fused kernel.
  *
  * fuse_auto_splits: the number of K splits the plan uses for (op, M, N, K) on the current device
  *   (1 = the single fused kernel; 0 for an invalid shape).  op is FUSE_OP_SWIGLU or

@@ -901,13 +901,23 @@ DualArgs dual_args(const void* a, const void* b1, const void* b2, int M, int N, 
     return p;
 }
 
-// Split of K for a shape (1 = the single fused kernel).  Full tiles only.  When the tiles cover
-// fewer than SPLIT_BELOW_CU_FRACTION of the CUs, K is divided so that tiles x splits is about one
-// workgroup per CU, each split keeping at least MIN_SPLIT_STEPS steps of 32.  Measured on 256
-// CUs at K = 1536: 2 to 32 tiles gain 1.1-2.2x from the split, 64 tiles split 4 ways gain
-// nothing.  FUSE_SPLITK forces a split count (1 = never split) for tuning sweeps.
-constexpr double SPLIT_BELOW_CU_FRACTION = 0.25;
+// Split of K for a shape (1 = the single fused kernel).  Full tiles only, and only when the tiles
+// cover fewer than SPLIT_BELOW_CU_FRACTION of the CUs (one partial round).  Each split count sp,
+// 2 .. K steps / MIN_SPLIT_STEPS, is priced against the single kernel by a cost model fitted to
+// measurements on MI355X (256 CUs; 13 shapes, M 256-2048, K 512-4096, every split count from 1 to
+// 16; the model's choice was within 5 % of the fastest split count measured for each):
+//   time(sp) = ceil(units / CUs) x ceil(K steps / sp) x STEP_US
+//            + (sp > 1) x (SPLIT_FIXED_US + 8 x planes x sp x M x N bytes / SPLIT_BYTES_PER_US)
+// with units = tiles x sp: the K steps each workgroup walks, plus the second kernel and the fp32
+// partial products written and read back (planes = 2 for the dual product, 1 for a GEMM).  The
+// cheapest wins; no plan's partials exceed SPLIT_MAX_BYTES.  FUSE_SPLITK forces a split count
+// (1 = never split) for tuning sweeps.
+constexpr double SPLIT_BELOW_CU_FRACTION = 0.5;
 constexpr int MIN_SPLIT_STEPS = 4;
+constexpr double STEP_US = 0.7;             // one 32-deep K step of a full tile
+constexpr double SPLIT_FIXED_US = 4.0;      // the reduction kernel's launch and tail
+constexpr double SPLIT_BYTES_PER_US = 5.0e6;
+constexpr double SPLIT_MAX_BYTES = 64.0 * 1024 * 1024;
 
 struct SplitPlan {
     int splits, ksteps;
@@ -924,7 +934,25 @@ SplitPlan split_plan(int M, int N, int K, int tile_cols, bool aligned) {
     } else {
         const int cus = cu_count();
         if (tiles >= SPLIT_BELOW_CU_FRACTION * cus) return {1, kt};
-        sp = min(cus / tiles, kt / MIN_SPLIT_STEPS);
+        const double planes = tile_cols == BN ? 2.0 : 1.0;
+        const double mn = (double)M * (double)N;
+        auto cost = [&](int s) {
+            const int steps = (kt + s - 1) / s;
+            const double rounds = (double)((tiles * s + cus - 1) / cus);
+            double t = rounds * steps * STEP_US;
+            if (s > 1) t += SPLIT_FIXED_US + 8.0 * planes * s * mn / SPLIT_BYTES_PER_US;
+            return t;
+        };
+        sp = 1;
+        double best = cost(1);
+        for (int s = 2; s <= kt / MIN_SPLIT_STEPS; s++) {
+            if ((double)s * planes * mn * 4.0 > SPLIT_MAX_BYTES) break;
+            const double c = cost(s);
+            if (c < best) {
+                best = c;
+                sp = s;
+            }
+        }
     }
     sp = max(1, min(sp, kt));
     if (sp < 2) return {1, kt};

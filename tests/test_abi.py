@@ -251,18 +251,23 @@ def test_gemm_bias_act_validation(lib):
 
 def test_auto_plan_and_validation(lib):
     # Plans depend only on the shape and the CU count (256 here when no device answers, as on the
-    # MI355X): the split form is taken while the tiles cover less than a quarter of the CUs.
+    # MI355X): below half the CUs in tiles, the split count the library's cost model prices
+    # cheapest (the values below are that model's choices for 256 CUs).
     SW, GM = 3, 5
-    cus = 256
     assert lib.fuse_auto_splits(SW, 2048, 8960, 1536) == 1               # 560 tiles: single kernel
+    assert lib.fuse_auto_splits(GM, 2048, 8960, 1536) == 1               # 280 tiles: single kernel
     assert lib.fuse_auto_splits(SW, 300, 512, 1536) == 1                 # ragged M: single kernel
-    assert lib.fuse_auto_splits(SW, 256, 512, 1536) == min(cus // 4, 48 // 4)  # 4 tiles
+    assert lib.fuse_auto_splits(SW, 256, 512, 1536) == 8                 # 4 tiles, 48 K steps
     assert lib.fuse_auto_splits(SW, 256, 512, 96) == 1                   # 3 K steps: too short to split
-    assert lib.fuse_auto_splits(SW, 512, 2048, 1536) == 8                # 32 tiles
-    assert lib.fuse_auto_splits(SW, 1024, 2048, 1536) == 1               # 64 tiles: single kernel
+    assert lib.fuse_auto_splits(SW, 512, 2048, 1536) == 3                # 32 tiles
+    assert lib.fuse_auto_splits(SW, 1024, 2048, 1536) == 1               # 64 tiles, 48 K steps: not worth it
+    assert lib.fuse_auto_splits(SW, 2048, 1024, 4096) == 4               # 64 tiles, 128 K steps
+    assert lib.fuse_auto_splits(GM, 2048, 2048, 2048) == 3               # 64 tiles of 256 x 256
+    assert lib.fuse_auto_splits(GM, 2048, 2048, 512) == 1                # 16 K steps: not worth it
+    assert lib.fuse_auto_splits(SW, 2048, 2048, 4096) == 1               # 128 tiles: half the CUs
     assert lib.fuse_auto_splits(GM, 256, 512, 1536) == 12                # 2 tiles of 256 x 256
     assert lib.fuse_auto_splits(SW, 0, 512, 1536) == 0
-    assert lib.fuse_auto_workspace_bytes(SW, 256, 512, 1536, BF16) == 12 * 2 * 256 * 512 * 4
+    assert lib.fuse_auto_workspace_bytes(SW, 256, 512, 1536, BF16) == 8 * 2 * 256 * 512 * 4
     assert lib.fuse_auto_workspace_bytes(GM, 256, 512, 1536, BF16) == 12 * 256 * 512 * 4
     assert lib.fuse_auto_workspace_bytes(SW, 2048, 8960, 1536, BF16) == 0
     assert lib.fuse_auto_workspace_bytes(SW, 256, 512, 1536, F16) == 0

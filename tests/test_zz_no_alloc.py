@@ -1,7 +1,7 @@
 """The allocation-free SwiGLU entry point (GPU): same result as the workspace entry point.
 
 fuse_swiglu_auto_noalloc keeps the split-K partials in the library's fixed per-device array.  It
-is called through the C ABI twice in a row -- a shape whose plan fills the whole 64 MiB array,
+is called through the C ABI twice in a row -- a shape whose plan takes 24 MiB of the 64 MiB array,
 then a smaller one that reuses it -- and each result is compared with fuse_swiglu_auto (caller
 workspace) on the same inputs, under the bf16 rule and bit for bit (same plan, same kernels,
 same summation order).  A shape that needs no split, a plan too large for the array (refused,
