@@ -306,8 +306,9 @@ fuse_status_t fuse_gemm_bias_act_auto(const void *x, const void *w, const void *
  * arguments without the workspace, same plan, same kernels and the same result bit for bit.
  * When the plan splits K, the fp32 partial products go to a fixed array inside the library of
  * FUSE_NOALLOC_SCRATCH_BYTES (64 MiB) per device, which each device the library runs on holds
- * from the first call there until the process ends; on a device of up to 256 CUs every plan
- * fits.  A plan that needs more returns FUSE_ERR_WORKSPACE with nothing launched.  The call
+ * from the first call there until the process ends; every plan the library chooses fits (it
+ * keeps split partials within this size).  A plan that needs more (a split count forced with
+ * FUSE_SPLITK) returns FUSE_ERR_WORKSPACE with nothing launched.  The call
  * allocates nothing (the array's device address is looked up once per device, on the first
  * call there).  Every call on one device shares that device's array: calls that overlap on a
  * device (on two streams, or from two threads) race on it and must be serialised by the

@@ -910,14 +910,15 @@ DualArgs dual_args(const void* a, const void* b1, const void* b2, int M, int N, 
 //            + (sp > 1) x (SPLIT_FIXED_US + 8 x planes x sp x M x N bytes / SPLIT_BYTES_PER_US)
 // with units = tiles x sp: the K steps each workgroup walks, plus the second kernel and the fp32
 // partial products written and read back (planes = 2 for the dual product, 1 for a GEMM).  The
-// cheapest wins; no plan's partials exceed SPLIT_MAX_BYTES.  FUSE_SPLITK forces a split count
-// (1 = never split) for tuning sweeps.
+// cheapest wins; no plan's partials exceed SPLIT_MAX_BYTES, the size of the allocation-free entry
+// point's array, so every chosen plan fits there.  FUSE_SPLITK forces a split count (1 = never
+// split) for tuning sweeps.
 constexpr double SPLIT_BELOW_CU_FRACTION = 0.5;
 constexpr int MIN_SPLIT_STEPS = 4;
 constexpr double STEP_US = 0.7;             // one 32-deep K step of a full tile
 constexpr double SPLIT_FIXED_US = 4.0;      // the reduction kernel's launch and tail
 constexpr double SPLIT_BYTES_PER_US = 5.0e6;
-constexpr double SPLIT_MAX_BYTES = 64.0 * 1024 * 1024;
+constexpr double SPLIT_MAX_BYTES = (double)SWIGLU_NOALLOC_SCRATCH_BYTES;
 
 struct SplitPlan {
     int splits, ksteps;
@@ -1019,9 +1020,8 @@ hipError_t launch_swiglu_auto(const void* a, const void* b1, const void* b2, voi
 // ------------------------------------------------------------------------------------------------
 // Allocation-free split-K SwiGLU, for callers that cannot allocate device memory.  The fp32 partial
 // products go to `scratch`, a fixed array of the library, instead of a caller workspace.  Its size
-// covers every split plan on a device of up to 256 CUs: the plan splits only when the tiles fill
-// less than a quarter of the CUs and keeps tiles x splits at most one workgroup per CU, each
-// holding two fp32 planes of a 256 x 128 tile (256 KiB), so 256 CUs need at most 64 MiB.  Each
+// covers every split plan the library chooses: the split planner keeps the partials within it
+// (SPLIT_MAX_BYTES); only a split count forced through FUSE_SPLITK can need more.  Each
 // device holds its own copy from the first call on it until the process ends.  Every call on a
 // device shares that copy, so calls that overlap on one device (two streams, two threads) race
 // on it.  Every partial a launch reads is written earlier in the same launch, so nothing needs
