@@ -733,6 +733,8 @@ def test_gemm_tail_slices_at_full_grid(monkeypatch, act):
     (512, 256, 320, None),    # short K: too few steps to pay for a reduction pass, not split
     (256, 512, 1536, "2"), (256, 512, 1536, "5"), (256, 512, 1536, "48"),  # uneven and one step per split
     (2048, 1024, 64, None),   # 64 tiles, two K steps: no split
+    (1024, 2048, 2048, None), # 64 tiles, 64 K steps: split by the cost model (3 on 256 CUs)
+    (2048, 1024, 4096, None), # 64 tiles, 128 K steps (4 on 256 CUs)
 ])
 def test_swiglu_auto_parity(monkeypatch, M, N, K, force):
     if force:
@@ -763,6 +765,23 @@ def test_gemm_auto_parity(monkeypatch, act):
             assert_close(y, oracle.gemm_bias_act(d["x"], d["w"], d["bias"], act), "bf16", f"gemm auto {M}x{N}x{K} {act}")
             y = api.fuse_gemm_bias_act_auto(d["x"].cuda(), d["w"].cuda(), None, act)
             assert_close(y, oracle.gemm_bias_act(d["x"], d["w"], None, act), "bf16", f"gemm auto no bias {act}")
+
+
+@pytest.mark.parametrize("M,N,K,act", [(2048, 2048, 2048, "gelu"), (256, 8960, 1536, "silu")])
+def test_gemm_auto_large_parity(M, N, K, act):
+    """Larger shapes the cost model splits (3 splits each on 256 CUs: 64 tiles over a deep K, 35
+    tiles of a wide N): sampled rows against the oracle, with and without bias, and the same bits
+    on a second call."""
+    splits = api.fuse_auto_splits(api.FUSE_OP_GEMM_BIAS_ACT, M, N, K)
+    announce(f"gemm auto {M}x{N}x{K} {act} splits={splits}")
+    d = synth.gemm_inputs(M, N, K, "bf16", seed=M + 7 * N + K)
+    x, w, bias = d["x"].cuda(), d["w"].cuda(), d["bias"].cuda()
+    rows = torch.arange(0, M, max(1, M // 48))
+    for b, bref in ((bias, d["bias"]), (None, None)):
+        y = api.fuse_gemm_bias_act_auto(x, w, b, act)
+        assert_close(y[rows.cuda()], oracle.gemm_bias_act(d["x"][rows], d["w"], bref, act), "bf16",
+                     f"gemm auto {M}x{N}x{K} {act} bias={b is not None} s={splits}")
+        assert torch.equal(y, api.fuse_gemm_bias_act_auto(x, w, b, act))
 
 
 # ------------------------------------------------------------------------------------------------
