@@ -348,7 +348,7 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
         record("softmax_unfused_f16_65536x2048", w.op, w.shape, w.dtype, False, ev, n_launch // 2)
         del sets, ws
 
-        ceiling = mfma_ceiling(torch, api, stream, roofline, n_launch // 2)
+        ceiling = mfma_ceiling(torch, api, stream, roofline, MFMA_LAUNCHES)
         out["mfma_ceiling"] = ceiling
 
         w = synth.WORKLOADS["swiglu_bf16_2048x8960x1536"]
@@ -365,12 +365,12 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
         for i in range(3):
             sw(i)
         one = single_dispatch_us(torch, stream, sw)
-        _, ev = time_launches(torch, stream, sw, n_launch // 2)
-        record("swiglu_bf16_2048x8960x1536", w.op, w.shape, w.dtype, True, ev, n_launch // 2,
+        _, ev = time_launches(torch, stream, sw, MFMA_LAUNCHES)
+        record("swiglu_bf16_2048x8960x1536", w.op, w.shape, w.dtype, True, ev, MFMA_LAUNCHES,
                single_dispatch(one, roofline.workload_work(w.op, w.shape, w.dtype, True)))
         of_ceiling("swiglu_bf16_2048x8960x1536", ceiling)
-        _, ev = time_launches(torch, stream, sw_unf, n_launch // 2)
-        record("swiglu_unfused_bf16_2048x8960x1536", w.op, w.shape, w.dtype, False, ev, n_launch // 2)
+        _, ev = time_launches(torch, stream, sw_unf, MFMA_LAUNCHES)
+        record("swiglu_unfused_bf16_2048x8960x1536", w.op, w.shape, w.dtype, False, ev, MFMA_LAUNCHES)
         del ws
 
         w = synth.WORKLOADS["gemm_relu_bf16_2048x8960x1536"]
@@ -390,15 +390,15 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
         for i in range(3):
             gm(i)
         one = single_dispatch_us(torch, stream, gm)
-        _, ev = time_launches(torch, stream, gm, n_launch // 2)
-        record("gemm_bias_relu_bf16_2048x8960x1536", w.op, w.shape, w.dtype, True, ev, n_launch // 2,
+        _, ev = time_launches(torch, stream, gm, MFMA_LAUNCHES)
+        record("gemm_bias_relu_bf16_2048x8960x1536", w.op, w.shape, w.dtype, True, ev, MFMA_LAUNCHES,
                single_dispatch(one, roofline.workload_work(w.op, w.shape, w.dtype, True)))
         of_ceiling("gemm_bias_relu_bf16_2048x8960x1536", ceiling)
-        _, ev = time_launches(torch, stream, gm_unf, n_launch // 2)
-        record("gemm_bias_relu_unfused_bf16_2048x8960x1536", w.op, w.shape, w.dtype, False, ev, n_launch // 2,
+        _, ev = time_launches(torch, stream, gm_unf, MFMA_LAUNCHES)
+        record("gemm_bias_relu_unfused_bf16_2048x8960x1536", w.op, w.shape, w.dtype, False, ev, MFMA_LAUNCHES,
                {"note": "GEMM kernel, bias kernel, ReLU kernel"})
-        _, ev = time_launches(torch, stream, gm_vendor, n_launch // 2)
-        record("reference_vendor_gemm_bf16_2048x8960x1536", w.op, w.shape, w.dtype, True, ev, n_launch // 2,
+        _, ev = time_launches(torch, stream, gm_vendor, MFMA_LAUNCHES)
+        record("reference_vendor_gemm_bf16_2048x8960x1536", w.op, w.shape, w.dtype, True, ev, MFMA_LAUNCHES,
                {"note": "torch.matmul (hipBLASLt) without bias or activation: context for the MFMA ceiling, "
                         "not part of the path"})
         del ws
@@ -442,6 +442,10 @@ def other_rows(torch, api, synth, roofline, n_launch=40):
 
 
 CEILING_ITERS = 448  # rounds of the matrix-core calibration kernel: about the SwiGLU workload's length
+# Launches per back-to-back replay of the matrix-core rows and their ceiling.  Under the board's
+# power limit the clock oscillates over a few milliseconds: consecutive replays of 20 SwiGLU
+# launches measured 110-142 us per launch on one box, one of 200 launches 118.8 us each time.
+MFMA_LAUNCHES = 200
 
 
 def mfma_ceiling(torch, api, stream, roofline, n_launch, iters=CEILING_ITERS):
