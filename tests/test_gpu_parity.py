@@ -705,7 +705,8 @@ def test_gemm_workload_sampled_rows():
 @pytest.mark.parametrize("act", ["relu", "gelu"])
 def test_gemm_tail_slices_at_full_grid(monkeypatch, act):
     # 2048x8960 in 256x256 tiles is 280 tiles: one round on 256 CUs and 24 tiles left, run as
-    # 64-row quarters, the 352 units walked by one resident workgroup per CU.  The k order per
+    # 64-row quarters ahead of the whole tiles, the 352 units walked by one resident workgroup per
+    # CU.  The k order per
     # element does not depend on how the tiles are cut or launched: bit-identical to whole tiles
     # and to one workgroup per unit, and checked against the oracle on sampled rows.
     M, N, K = 2048, 8960, 256
