@@ -707,13 +707,18 @@ __device__ __forceinline__ void direct_tile(const DualArgs& p, char* lds, int m0
 // steps [split * ksteps, split * ksteps + ksteps) of its tile.  Otherwise tiles - tail units are
 // a whole tile each, and parts * tail units the remaining tiles as 128-row halves or 64-row
 // quarters: when the tiles leave a last round that fills few CUs, that round is spread over more
-// of them.  The SwiGLU kernels run the slices last; the GEMM modes run them first, so that the
-// CUs that take a slice start their whole tile later and the whole tiles' output bursts do not
-// all fall at one moment (2048x8960x1536 GEMM + bias + ReLU, three alternating rounds: 67.4-67.6
-// against 69.1-69.4 us per synchronised dispatch and 63.4-64.0 against 64.7-64.8 us over 200
-// launches; for the SwiGLU slices first gained 2.5 us per dispatch but lost 1.5 us sustained).
-// Whole tile t then runs as unit t + parts * tail, on the XCD the tile map assigns it when
-// parts * tail is a multiple of 8 (96 at that shape), on a neighbouring one otherwise.  One workgroup per unit, or, with more units than CUs, a grid of one
+// of them.  Where the slices go in the unit order spreads the whole tiles' output bursts, which
+// otherwise all fall at the end of a round: the GEMM modes (about one round of whole tiles) run
+// the slices first, the SwiGLU kernels (two and more rounds) right after the first round of
+// whole tiles, one per workgroup of the grid.  Measured at 2048x8960x1536 (three alternating
+// rounds each), GEMM + bias + ReLU against slices last: 67.4-67.6 against 69.1-69.4 us per
+// synchronised dispatch, 63.4-64.0 against 64.7-64.8 us over 200 launches; SwiGLU against
+// slices last, on two machines: 106.5-106.7 against 109.0-109.2 and 112.1-112.8 against
+// 112.6-113.2 us per dispatch, 104.6-105.3 against 105.3-105.9 and 107.4-108.0 against
+// 108.6-109.1 us over 200 launches (slices first: 2.5 us faster per dispatch, 1.5 us slower
+// sustained).  Whole tiles after the slices run as unit t + parts * tail, on the XCD the tile
+// map assigns tile t when parts * tail is a multiple of 8 (96 and 192 at these shapes), on a
+// neighbouring one otherwise.  A grid of one workgroup per unit puts the SwiGLU slices last.  One workgroup per unit, or, with more units than CUs, a grid of one
 // workgroup per CU (rounded down to a multiple of 8) walking units b, b + grid, ..., so that unit u
 // still runs on XCD u % 8, the one the tile map assumes.
 // Last-round slice q (of tail tiles cut in P row slices each): its tile among the tail tiles and
@@ -746,8 +751,11 @@ __device__ __forceinline__ void direct_unit(const DualArgs& p, char* lds, int bi
         if (SLICES_FIRST) {
             if (bid < nsl) q = bid;
             else bid -= nsl;
-        } else if (bid >= head) {
-            q = bid - head;
+        } else {
+            // slices after the first round of whole tiles: one per workgroup of the grid
+            const int w1 = min(head, (int)gridDim.x);
+            if (bid >= w1 && bid < w1 + nsl) q = bid - w1;
+            else if (bid >= w1 + nsl) bid -= nsl;
         }
     }
     if (q < 0) {
