@@ -15,6 +15,8 @@ are timed the same way and reported under "rows".  cpu_baseline times the CPU or
 same workload.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-rows] [--no-cpu]
+Profiling and study modes (one JSON line each): --counters, --counters-rows, --dispatch WORKLOAD,
+--sweep (size sweep of Add+LN and the copy), --split-sweep (split-K plan against forced splits).
 """
 from __future__ import annotations
 
@@ -962,6 +964,62 @@ def cpu_rows(synth, roofline, budget_s=1.0):
     return out
 
 
+SPLIT_SWEEP_SHAPES = (
+    ("swiglu", 256, 512, 1536), ("swiglu", 256, 2048, 1536), ("swiglu", 512, 2048, 1536),
+    ("swiglu", 1024, 1024, 1024), ("swiglu", 256, 4096, 4096), ("swiglu", 1024, 2048, 2048),
+    ("swiglu", 2048, 1024, 4096), ("gemm", 1024, 1024, 1024), ("gemm", 256, 8960, 1536),
+    ("gemm", 512, 4096, 4096), ("gemm", 2048, 2048, 2048), ("gemm", 2048, 2560, 2048),
+    ("gemm", 2048, 2048, 512),
+)
+SPLIT_SWEEP_COUNTS = (1, 2, 3, 4, 5, 6, 8, 12)
+
+
+def split_sweep(torch, api):
+    """The split-K plan against every forced split count (FUSE_SPLITK) at the shapes its cost model
+    was fitted to: per synchronised single dispatch of the auto entry points (median of 10), the
+    time of each split count and of the plan's own choice."""
+    stream = torch.cuda.Stream()
+    out = []
+    with torch.cuda.stream(stream):
+        for op, M, N, K in SPLIT_SWEEP_SHAPES:
+            g = torch.Generator().manual_seed(M + N + K)
+            a = torch.randn(M, K, generator=g).to(torch.bfloat16).cuda()
+            b1 = (torch.randn(K, N, generator=g) / math.sqrt(K)).to(torch.bfloat16).cuda()
+            b2 = (torch.randn(K, N, generator=g) / math.sqrt(K)).to(torch.bfloat16).cuda()
+            bias = (torch.randn(N, generator=g) * 0.02).to(torch.bfloat16).cuda()
+            o = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+            code = api.FUSE_OP_SWIGLU if op == "swiglu" else api.FUSE_OP_GEMM_BIAS_ACT
+            kt = K // 32
+
+            def timed():
+                need = api.load().fuse_auto_workspace_bytes(code, M, N, K, api.FUSE_BF16)
+                ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+                if op == "swiglu":
+                    f = lambda i: api.fuse_swiglu_auto(a, b1, b2, out=o, workspace=ws)
+                else:
+                    f = lambda i: api.fuse_gemm_bias_act_auto(a, b1, bias, "relu", y=o, workspace=ws)
+                for i in range(3):
+                    f(i)
+                return round(single_dispatch_us(torch, stream, f), 2)
+            r = {"op": op, "shape": [M, N, K], "forced": {}}
+            for sp in SPLIT_SWEEP_COUNTS:
+                if sp > kt:
+                    continue
+                os.environ["FUSE_SPLITK"] = str(sp)
+                try:
+                    r["forced"][str(api.fuse_auto_splits(code, M, N, K))] = timed()
+                finally:
+                    del os.environ["FUSE_SPLITK"]
+            r["plan_splits"] = api.fuse_auto_splits(code, M, N, K)
+            r["plan_us"] = timed()
+            best = min(r["forced"], key=r["forced"].get)
+            r["best_forced"] = [int(best), r["forced"][best]]
+            log(f"split sweep {op} {M}x{N}x{K}: plan {r['plan_splits']} splits {r['plan_us']} us; "
+                f"best forced {best} splits {r['forced'][best]} us; all {r['forced']}")
+            out.append(r)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -979,6 +1037,8 @@ def main():
                     help="the same for the other rows of the path (their fused and unfused kernels)")
     ap.add_argument("--sweep", action="store_true",
                     help="only the size sweep of fused Add+LayerNorm and the copy (fixed cost and streaming rate)")
+    ap.add_argument("--split-sweep", action="store_true",
+                    help="only the split-K plan against every forced split count (its fitted shapes)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): the fused row kernels are "
@@ -1003,6 +1063,9 @@ def main():
         return
     if a.sweep:
         print(json.dumps({"size_sweep": size_sweep(torch, api, synth, roofline)}), flush=True)
+        return
+    if a.split_sweep:
+        print(json.dumps({"split_sweep": split_sweep(torch, api)}), flush=True)
         return
     h = headline(torch, api, synth, roofline, a.steps, a.warmup)
     log(f"headline: {h['avg_launch_us']:.2f} us/launch, value {h['value_gbps']:.0f} GB/s")

@@ -952,7 +952,8 @@ DualArgs dual_args(const void* a, const void* b1, const void* b2, int M, int N, 
 // cover fewer than SPLIT_BELOW_CU_FRACTION of the CUs (one partial round).  Each split count sp,
 // 2 .. K steps / MIN_SPLIT_STEPS, is priced against the single kernel by a cost model fitted to
 // measurements on MI355X (256 CUs; 13 shapes, M 256-2048, K 512-4096, every split count from 1 to
-// 16; the model's choice was within 5 % of the fastest split count measured for each):
+// 16; with the current kernels the model's choice is within 1 % of the fastest forced split count
+// at 10 of the 13 and 2-8 % off at the other three):
 //   time(sp) = ceil(units / CUs) x ceil(K steps / sp) x STEP_US
 //            + (sp > 1) x (SPLIT_FIXED_US + 8 x planes x sp x M x N bytes / SPLIT_BYTES_PER_US)
 // with units = tiles x sp: the K steps each workgroup walks, plus the second kernel and the fp32
