@@ -1,7 +1,8 @@
 """Seeded random shapes for every fused operation (GPU required): row lengths across the whole
 supported range, odd row counts, every storage type, with and without the residual, random
 activations and LayerNorm-variant outputs, and tensors that start one element past a 16-byte
-boundary (the per-element paths).  Each result is compared with the CPU oracle element by
+boundary (the per-element paths), and whole-tile dual-product shapes (the persistent kernel, its
+last-round slices, the split-K plans).  Each result is compared with the CPU oracle element by
 element under the operation's rule.  The shapes are drawn once from a fixed seed, so a failure
 names a case that can be rerun alone.
 """
@@ -142,3 +143,35 @@ def test_add_layernorm_ex_random(rows, hidden, dtype, relu, want_sum, want_stats
                                      d["eps"], relu=relu, want_sum=want_sum, want_stats=want_stats)
     assert (outs[1] is not None) == want_sum and (outs[2] is not None) == want_stats
     _check_ln_ex(outs, d, relu, dtype, f"ln_ex {rows}x{hidden} {dtype} relu={relu} sum={want_sum} stats={want_stats}")
+
+
+def _full_tile_case(rng):
+    gemm = bool(rng.integers(0, 2))
+    return (256 * int(rng.integers(1, 9)), (256 if gemm else 128) * int(rng.integers(1, 37 if gemm else 73)),
+            32 * int(rng.integers(1, 65)), gemm, bool(rng.integers(0, 2)), ["none", "relu", "gelu", "silu"][int(rng.integers(0, 4))])
+
+
+FULL_TILE_CASES = _cases(20261210, 12, _full_tile_case)
+
+
+@pytest.mark.parametrize("M,N,K,gemm,auto,act", FULL_TILE_CASES)
+def test_dual_product_full_tile_random(M, N, K, gemm, auto, act):
+    """Shapes made of whole 256-row tiles: the full-tile kernels (one workgroup per CU walking its
+    units when they outnumber the CUs, last-round slices) and, through the *_auto entry points,
+    the split-K plans; 12 sampled rows against the oracle."""
+    op = api.FUSE_OP_GEMM_BIAS_ACT if gemm else api.FUSE_OP_SWIGLU
+    splits = api.fuse_auto_splits(op, M, N, K) if auto else 1
+    announce(f"{'gemm ' + act if gemm else 'swiglu'} full tiles {M}x{N}x{K} auto={auto} splits={splits}")
+    rows = torch.from_numpy(np.sort(np.random.default_rng(M + N + K).choice(M, size=12, replace=False)))
+    if gemm:
+        d = synth.gemm_inputs(M, N, K, "bf16", seed=M + 3 * N + 5 * K)
+        x, w, bias = d["x"].cuda(), d["w"].cuda(), d["bias"].cuda()
+        y = api.fuse_gemm_bias_act_auto(x, w, bias, act) if auto else api.fuse_gemm_bias_act(x, w, bias, act)
+        assert_close(y[rows.cuda()], oracle.gemm_bias_act(d["x"][rows], d["w"], d["bias"], act), "bf16",
+                     f"gemm {M}x{N}x{K} {act} auto={auto}")
+    else:
+        d = synth.swiglu_inputs(M, N, K, "bf16", seed=M + 3 * N + 5 * K)
+        a, b1, b2 = d["a"].cuda(), d["b1"].cuda(), d["b2"].cuda()
+        out = api.fuse_swiglu_auto(a, b1, b2) if auto else api.fuse_swiglu_dualgemm(a, b1, b2)
+        assert_close(out[rows.cuda()], oracle.swiglu(d["a"][rows], d["b1"], d["b2"]), "bf16",
+                     f"swiglu {M}x{N}x{K} auto={auto}")
