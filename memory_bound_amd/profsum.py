@@ -20,6 +20,10 @@
     python -m memory_bound_amd.profsum split  <results.db> <kernel> <grid> <n>
         # one kernel at one grid size: its first n dispatches and the rest, apart (a benchmark
         # that times the same kernel first on rotating cold buffers, then on one hot buffer set)
+    python -m memory_bound_amd.profsum splits <bench.json>
+        # the JSON line of `bench.py --split-sweep` as a table: per shape, the split-K plan's
+        # choice and time, the fastest forced split count, how far off the plan is, and every
+        # forced split count's time (this mode reads the benchmark's output, not a database)
 
 rocprofv3's own --stats table groups dispatches by kernel name only; the same kernel
 instantiation runs at several shapes here (the [2048,4096] and [16384,4096] Add+LayerNorm share
@@ -27,6 +31,8 @@ one), so the tables below also split by grid size.  Durations are in microsecond
 are what rocprofv3 reports per dispatch (FETCH_SIZE and WRITE_SIZE in KiB).
 """
 from __future__ import annotations
+
+import json
 
 import sqlite3
 import statistics
@@ -210,8 +216,27 @@ def sweep(db_path: str, skip: int = 3) -> dict:
     return {"sizes": sizes, "fits": fits}
 
 
+def split_table(path: str) -> str:
+    """The `bench.py --split-sweep` JSON line (the last line of `path` starting with '{') as text."""
+    line = [l for l in open(path).read().splitlines() if l.startswith("{")][-1]
+    rows = json.loads(line)["split_sweep"]
+    counts = sorted({int(k) for r in rows for k in r["forced"]})
+    out = [f"{'op':6s} {'M x N x K':>16s} {'plan':>5s} {'plan_us':>8s} {'best':>5s} {'best_us':>8s} {'off':>6s}  "
+           + " ".join(f"{'s=' + str(c):>7s}" for c in counts)]
+    for r in rows:
+        m, n, k = r["shape"]
+        best, best_us = r["best_forced"]
+        cells = " ".join(f"{r['forced'][str(c)]:7.2f}" if str(c) in r["forced"] else f"{'-':>7s}" for c in counts)
+        out.append(f"{r['op']:6s} {f'{m}x{n}x{k}':>16s} {r['plan_splits']:5d} {r['plan_us']:8.2f} {best:5d} "
+                   f"{best_us:8.2f} {(r['plan_us'] / best_us - 1) * 100:5.1f}%  {cells}")
+    return "\n".join(out)
+
+
 def main(argv):
     mode, path = argv[1], argv[2]
+    if mode == "splits":
+        print(split_table(path))
+        return
     if mode == "trace":
         print(f"{'kernel':64s} {'grid':>9s} {'wg':>4s} {'calls':>5s} {'mean_us':>9s} {'median_us':>9s} "
               f"{'p10_us':>8s} {'p90_us':>8s} {'min_us':>8s} {'max_us':>8s}")
