@@ -33,7 +33,6 @@ are what rocprofv3 reports per dispatch (FETCH_SIZE and WRITE_SIZE in KiB).
 from __future__ import annotations
 
 import json
-
 import sqlite3
 import statistics
 import sys
