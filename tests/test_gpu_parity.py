@@ -425,6 +425,23 @@ def test_softmax_constant_rows_and_inplace():
     assert_close(x, ref, "f16", "softmax in place")
 
 
+@pytest.mark.parametrize("dtype,cols", [("f16", 2048), ("f32", 1000), ("bf16", 4096), ("f16", 333)])
+def test_softmax_masked_rows(dtype, cols):
+    # causal-style masks: row r keeps its first r * cols / rows + 1 entries and the rest are -inf;
+    # masked entries come out exactly 0 and the kept ones match the oracle
+    rows = 48
+    announce(f"softmax masked rows {rows}x{cols} {dtype}")
+    d = synth.softmax_inputs(rows, cols, dtype, seed=cols + 5)
+    x = d["x"].clone()
+    mask = torch.zeros(rows, cols, dtype=torch.bool)
+    for r in range(rows):
+        mask[r, (r * cols) // rows + 1:] = True
+    x[mask] = float("-inf")
+    y = api.fuse_softmax_rows(x.cuda(), d["scale"])
+    assert_close(y, oracle.softmax_rows(x, np.float32(d["scale"])), KIND[dtype], f"masked softmax {dtype}")
+    assert bool((y.cpu()[mask] == 0).all())
+
+
 def test_softmax_nan_propagates():
     x = torch.randn(2, 2048).half()
     x[1, 100] = float("nan")

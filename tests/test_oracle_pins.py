@@ -237,6 +237,15 @@ def test_softmax_scale_applied_before_max_including_negative():
     np.testing.assert_allclose(y2[0], [1 / 3, 2 / 3], rtol=0, atol=1e-15)
 
 
+def test_softmax_masked_entries():
+    # -inf entries (an attention mask) get exactly 0 and the rest renormalise:
+    # [0, -inf, ln 2] -> [1/3, 0, 2/3]; a row with one finite entry puts all its mass there
+    y = oracle.softmax_rows(np.array([[0.0, -math.inf, math.log(2.0)], [-math.inf, 5.0, -math.inf]]), 1.0)
+    np.testing.assert_allclose(y[0], [1 / 3, 0.0, 2 / 3], rtol=0, atol=1e-15)
+    assert y[0, 1] == 0.0
+    assert list(y[1]) == [0.0, 1.0, 0.0]
+
+
 def test_softmax_constant_row_and_single_column():
     y = oracle.softmax_rows(np.full((2, 2048), 3.7), 0.5)
     assert np.all(y == 2.0 ** -11)
