@@ -20,6 +20,10 @@
     python -m memory_bound_amd.profsum split  <results.db> <kernel> <grid> <n>
         # one kernel at one grid size: its first n dispatches and the rest, apart (a benchmark
         # that times the same kernel first on rotating cold buffers, then on one hot buffer set)
+    python -m memory_bound_amd.profsum rows   <fetch.db> <write.db>
+        # a `bench.py --counters-rows` FETCH_SIZE run and WRITE_SIZE run: per row of the path
+        # other than the headline, the bytes its kernels moved (as `hbm` scales them) against the
+        # row's algorithmic bytes, fused and unfused
     python -m memory_bound_amd.profsum splits <bench.json>
         # the JSON line of `bench.py --split-sweep` as a table: per shape, the split-K plan's
         # choice and time, the fastest forced split count, how far off the plan is, and every
@@ -215,6 +219,48 @@ def sweep(db_path: str, skip: int = 3) -> dict:
     return {"sizes": sizes, "fits": fits}
 
 
+# The rows of `bench.py --counters-rows`: label, workload (its algorithmic bytes come from
+# roofline.workload_work), fused or not, and the (kernel, grid) dispatches that make it up.
+ROW_TRAFFIC = (
+    ("LN+ReLU, sum, mean/var fp16 [2048,4096]", ("add_layernorm_ex", (2048, 4096), "f16"), True,
+     (("add_layernorm_ex_kernel<1, true, 1, 8, true, 4>", 262144),)),
+    ("cumsum+scale fp16 [2048,4096]", "cumsum_f16_2048x4096", True, (("cumsum_scale_kernel<1, true, 2, 4, 2>", 262144),)),
+    ("  unfused: scan + scale", "cumsum_f16_2048x4096", False,
+     (("cumsum_scale_kernel<1, true, 2, 4, 2>", 262144), ("ew_kernel<1, true, 2, OpScale>", 524288))),
+    ("softmax fp16 [65536,2048]", "softmax_f16_65536x2048", True, (("softmax_rows_kernel<1, true, 2, 2, true>", 8388608),)),
+    ("  unfused: max, exp+sum, divide", "softmax_f16_65536x2048", False,
+     (("softmax_rowmax_kernel<1, true>", 4194304), ("softmax_expsum_kernel<1, true>", 4194304),
+      ("softmax_divide_kernel<1, true>", 4194304))),
+    ("SwiGLU bf16 2048x8960x1536", "swiglu_bf16_2048x8960x1536", True, (("swiglu_persist_kernel<4, 0>", 65536),)),
+    ("  unfused: products + SiLU*", "swiglu_bf16_2048x8960x1536", False,
+     (("swiglu_persist_kernel<4, 1>", 65536), ("ew_kernel<2, true, 4, OpSiluMul>", 573440))),
+    ("GEMM+bias+ReLU bf16 2048x8960x1536", "gemm_relu_bf16_2048x8960x1536", True, (("swiglu_persist_kernel<4, 3>", 65536),)),
+    ("  unfused: GEMM, bias, ReLU", "gemm_relu_bf16_2048x8960x1536", False,
+     (("swiglu_persist_kernel<4, 2>", 65536), ("ew_kernel<2, true, 4, OpBiasAdd>", 573440),
+      ("ew_kernel<2, true, 4, OpRelu>", 573440))),
+)
+
+
+def row_traffic(fetch_db: str, write_db: str) -> str:
+    """The ROW_TRAFFIC table from a FETCH_SIZE run and a WRITE_SIZE run, as text."""
+    from memory_bound_amd import roofline, synth
+    fs, ws, rows = hbm(fetch_db, write_db)
+    by = {(r["kernel"], r["grid"]): r for r in rows}
+    c = by[(COPY_KERNEL, COPY_BYTES // 64)]
+    out = [f"# Calibration in the same runs: a copy of exactly 24 MiB reads FETCH_SIZE {c['fetch_kib']:.2f} KiB "
+           f"and WRITE_SIZE", f"# {c['write_kib']:.2f} KiB, so counter KiB x {fs:.5f} (fetch) and x {ws:.5f} "
+           f"(write) are bytes moved.",
+           f"{'row':41s} {'measured_bytes':>14s} {'algorithmic':>13s} {'ratio':>7s}   kernels (fetch KiB / write KiB)"]
+    for label, work, fused, kernels in ROW_TRAFFIC:
+        op, shape, dtype = work if isinstance(work, tuple) else (synth.WORKLOADS[work].op, synth.WORKLOADS[work].shape,
+                                                                 synth.WORKLOADS[work].dtype)
+        alg = roofline.workload_work(op, shape, dtype, fused)["bytes"]
+        m = round(sum(by[k]["bytes"] for k in kernels))
+        out.append(f"{label:41s} {m:14d} {alg:13d} {m / alg:7.3f}   "
+                   + "; ".join(f"{k[0]} {by[k]['fetch_kib']:.0f}/{by[k]['write_kib']:.0f}" for k in kernels))
+    return "\n".join(out)
+
+
 def split_table(path: str) -> str:
     """The `bench.py --split-sweep` JSON line (the last line of `path` starting with '{') as text."""
     line = [l for l in open(path).read().splitlines() if l.startswith("{")][-1]
@@ -235,6 +281,9 @@ def main(argv):
     mode, path = argv[1], argv[2]
     if mode == "splits":
         print(split_table(path))
+        return
+    if mode == "rows":
+        print(row_traffic(path, argv[3]))
         return
     if mode == "trace":
         print(f"{'kernel':64s} {'grid':>9s} {'wg':>4s} {'calls':>5s} {'mean_us':>9s} {'median_us':>9s} "

@@ -172,6 +172,32 @@ def test_profile_summary_scales_counters_by_the_calibration_copy(tmp_path):
     assert c["bytes"] == 2 * (24 << 20)
 
 
+def test_profile_row_traffic_table(tmp_path):
+    # every kernel of the rows table reads 1000 KiB on FETCH_SIZE and 500 on WRITE_SIZE, with the
+    # copy calibrating both counters at 1:1 bytes; a row's measured bytes are then 1500 KiB per
+    # kernel, set against the row's algorithmic bytes
+    import sqlite3
+    from memory_bound_amd import profsum, roofline, synth
+    kernels = sorted({k for _, _, _, ks in profsum.ROW_TRAFFIC for k in ks})
+    dbs = []
+    for cname, copy_kib, k_kib in (("FETCH_SIZE", 24576.0, 1000.0), ("WRITE_SIZE", 24576.0, 500.0)):
+        path = str(tmp_path / f"{cname}.db")
+        db = sqlite3.connect(path)
+        db.execute("create table counters_collection (dispatch_id, kernel_name, grid_size, workgroup_size, "
+                   "counter_name, value)")
+        rows = [(1, "void fuse::copy16_kernel<4>(uint4 const*, uint4*, unsigned long)", 393216, 256, cname, copy_kib)]
+        rows += [(i + 2, f"void fuse::{k}(int)", g, 256, cname, k_kib) for i, (k, g) in enumerate(kernels)]
+        db.executemany("insert into counters_collection values (?, ?, ?, ?, ?, ?)", rows)
+        db.commit()
+        dbs.append(path)
+    lines = profsum.row_traffic(*dbs).splitlines()
+    body = {l[:41].strip(): l for l in lines[3:]}
+    assert len(body) == len(profsum.ROW_TRAFFIC)
+    softmax_unfused = body["unfused: max, exp+sum, divide"].split()
+    alg = roofline.workload_work("softmax_rows", synth.WORKLOADS["softmax_f16_65536x2048"].shape, "f16", False)["bytes"]
+    assert int(softmax_unfused[4]) == 3 * 1500 * 1024 and int(softmax_unfused[5]) == alg
+
+
 def test_profile_summary_clock_and_matrix_core_busy(tmp_path):
     # one dispatch of 1 us with 2000 cycles per shader engine runs at 2000 MHz; busy cycles of
     # half the SIMD-cycles give a busy fraction of 0.5; 1 GFLOP in 1 us is 1000 TFLOP/s
