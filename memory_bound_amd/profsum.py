@@ -20,6 +20,10 @@
     python -m memory_bound_amd.profsum split  <results.db> <kernel> <grid> <n>
         # one kernel at one grid size: its first n dispatches and the rest, apart (a benchmark
         # that times the same kernel first on rotating cold buffers, then on one hot buffer set)
+    python -m memory_bound_amd.profsum headline-counters <fetch.db> <write.db>
+        # a `bench.py --counters` FETCH_SIZE run and WRITE_SIZE run: the raw counter means of the
+        # calibration copy, the headline kernel and the unfused chains, the scale factors, and the
+        # `key: value` lines bench.py reads back (HBM bytes per dispatch, unfused over fused)
     python -m memory_bound_amd.profsum rows   <fetch.db> <write.db>
         # a `bench.py --counters-rows` FETCH_SIZE run and WRITE_SIZE run: per row of the path
         # other than the headline, the bytes its kernels moved (as `hbm` scales them) against the
@@ -261,6 +265,49 @@ def row_traffic(fetch_db: str, write_db: str) -> str:
     return "\n".join(out)
 
 
+# The kernels of `bench.py --counters`: label and (kernel, grid).
+COUNTER_KERNELS = (
+    ("copy 24 MiB", (COPY_KERNEL, COPY_BYTES // 64)),
+    ("fused Add+LayerNorm", (HEADLINE_KERNEL, HEADLINE_GRID)),
+    ("unfused: add kernel", ("ew_kernel<1, true, 2, OpAdd>", 524288)),
+    ("unfused: LayerNorm kernel", ("add_layernorm_kernel<1, true, 2, 4, false, 4>", 131072)),
+    ("fused BiasAdd+GELU+Residual", ("ew_kernel<1, true, 2, OpBiasGeluRes>", 524288)),
+    ("unfused: bias kernel", ("ew_kernel<1, true, 2, OpBiasAdd>", 524288)),
+    ("unfused: GELU kernel", ("ew_kernel<1, true, 2, OpGelu>", 524288)),
+)
+
+
+def headline_counters(fetch_db: str, write_db: str) -> str:
+    """The headline counter summary (raw means, scales, the key lines bench.py reads) as text."""
+    from memory_bound_amd import roofline
+    fs, ws, rows = hbm(fetch_db, write_db)
+    by = {(r["kernel"], r["grid"]): r for r in rows}
+    b = {label: by[kg]["bytes"] for label, kg in COUNTER_KERNELS}
+    ln_alg = roofline.workload_work("add_layernorm", (2048, 4096), "f16", True)["bytes"]
+    ln_unf_alg = roofline.workload_work("add_layernorm", (2048, 4096), "f16", False)["bytes"]
+    ge_alg = roofline.workload_work("bias_gelu_residual", (2048, 4096), "f16", True)["bytes"]
+    ge_unf_alg = roofline.workload_work("bias_gelu_residual", (2048, 4096), "f16", False)["bytes"]
+    fused, unf = b["fused Add+LayerNorm"], b["unfused: add kernel"] + b["unfused: LayerNorm kernel"]
+    ge, ge_unf = (b["fused BiasAdd+GELU+Residual"],
+                  b["unfused: bias kernel"] + b["unfused: GELU kernel"] + b["unfused: add kernel"])
+    out = ["# Raw counter means per dispatch (KiB):"]
+    for label, kg in COUNTER_KERNELS:
+        r = by[kg]
+        out.append(f"#   {label:30s} {kg[0]:44s} FETCH_SIZE {r['fetch_kib']:10.2f}  WRITE_SIZE {r['write_kib']:10.2f}")
+    out += ["#   (the unfused GELU chain ends with the same add kernel as the unfused Add+LayerNorm)", "#",
+            f"fetch_scale: {fs:.5f}", f"write_scale: {ws:.5f}", "#",
+            "# Scaled HBM bytes per dispatch (fetch * fetch_scale + write * write_scale, in bytes):",
+            f"kernel: {HEADLINE_KERNEL} grid {HEADLINE_GRID}",
+            f"kernel_source_sha256: {source_hash()}",
+            f"hbm_bytes_per_dispatch: {round(fused)}", f"algorithmic_bytes_per_dispatch: {ln_alg}",
+            f"traffic_over_algorithmic: {fused / ln_alg:.4f}",
+            f"unfused_chain_hbm_bytes: {round(unf)}", f"unfused_chain_algorithmic_bytes: {ln_unf_alg}",
+            f"unfused_over_fused_traffic: {unf / fused:.4f}",
+            f"gelu_fused_hbm_bytes: {round(ge)}   (algorithmic {ge_alg})",
+            f"gelu_unfused_chain_hbm_bytes: {round(ge_unf)}   (algorithmic {ge_unf_alg}; ratio {ge_unf / ge:.3f})"]
+    return "\n".join(out)
+
+
 def split_table(path: str) -> str:
     """The `bench.py --split-sweep` JSON line (the last line of `path` starting with '{') as text."""
     line = [l for l in open(path).read().splitlines() if l.startswith("{")][-1]
@@ -284,6 +331,9 @@ def main(argv):
         return
     if mode == "rows":
         print(row_traffic(path, argv[3]))
+        return
+    if mode == "headline-counters":
+        print(headline_counters(path, argv[3]))
         return
     if mode == "trace":
         print(f"{'kernel':64s} {'grid':>9s} {'wg':>4s} {'calls':>5s} {'mean_us':>9s} {'median_us':>9s} "

@@ -198,6 +198,30 @@ def test_profile_row_traffic_table(tmp_path):
     assert int(softmax_unfused[4]) == 3 * 1500 * 1024 and int(softmax_unfused[5]) == alg
 
 
+def test_profile_headline_counter_lines(tmp_path):
+    # the key lines bench.py reads back: with every kernel at 1000 KiB fetched and 500 written and
+    # the copy calibrating both counters 1:1, the fused kernel moves 1500 KiB and the unfused
+    # add -> LayerNorm pair twice that
+    import sqlite3
+    from memory_bound_amd import profsum
+    dbs = []
+    for cname, k_kib in (("FETCH_SIZE", 1000.0), ("WRITE_SIZE", 500.0)):
+        path = str(tmp_path / f"h{cname}.db")
+        db = sqlite3.connect(path)
+        db.execute("create table counters_collection (dispatch_id, kernel_name, grid_size, workgroup_size, "
+                   "counter_name, value)")
+        rows = [(i, f"void fuse::{kg[0]}(int)", kg[1], 256, cname, 24576.0 if kg[0] == profsum.COPY_KERNEL else k_kib)
+                for i, (_, kg) in enumerate(profsum.COUNTER_KERNELS)]
+        db.executemany("insert into counters_collection values (?, ?, ?, ?, ?, ?)", rows)
+        db.commit()
+        dbs.append(path)
+    text = profsum.headline_counters(*dbs)
+    kv = dict(l.split(": ", 1) for l in text.splitlines() if ": " in l and not l.startswith("#"))
+    assert int(kv["hbm_bytes_per_dispatch"]) == 1500 * 1024
+    assert kv["unfused_over_fused_traffic"] == "2.0000"
+    assert kv["kernel_source_sha256"] == profsum.source_hash()
+
+
 def test_profile_summary_clock_and_matrix_core_busy(tmp_path):
     # one dispatch of 1 us with 2000 cycles per shader engine runs at 2000 MHz; busy cycles of
     # half the SIMD-cycles give a busy fraction of 0.5; 1 GFLOP in 1 us is 1000 TFLOP/s
